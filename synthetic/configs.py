@@ -1,0 +1,312 @@
+"""The five synthetic paged-attention workloads, as seeded random draws.
+
+Every array is drawn from ``numpy.random.default_rng`` keyed by
+``[seed, stream, ...]``.  Large arrays are drawn in fixed chunks of the
+flattened array, chunk ``c`` from the key ``[..., c]``, so a result never
+depends on how many threads drew it.  Queries and K/V values are N(0,1) in
+float32 rounded to fp16 (round to nearest even).
+
+Shapes follow the five workloads:
+
+1. tiny MHA decode: 12/12 heads, d64, 8-block pool, lengths 40/20/16/30;
+2. GPT-2-small-shaped batch: 12/12 heads, d64, 32 prompts of 32..512 tokens
+   prefilled, then 64 decode steps;
+3. GQA decode: 32/8 heads, d128, 256 sequences of 1..4096 tokens;
+4. shared 1024-token prefix with 4-beam copy-on-write, GQA 32/8, d128;
+5. packed chunked prefill + decode over an int8 pool, GQA 32/8, d128.
+
+Every constructor takes overrides so tests can build the same structure at a
+size the CPU oracle finishes in seconds.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Callable, Optional
+
+import numpy as np
+
+BLOCK_SIZE = 16
+CHUNK = 1 << 20  # elements per independently seeded draw chunk
+
+# stream ids inside one workload's seed
+S_META, S_POOL_K, S_POOL_V, S_NEW_K, S_NEW_V, S_Q, S_KSCALE, S_VSCALE, S_CTX_K, S_CTX_V = range(10)
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _chunked(key, shape, dtype, fill_chunk):
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype)
+    nchunks = max(1, -(-n // CHUNK))
+
+    def one(c):
+        lo = c * CHUNK
+        hi = min(n, lo + CHUNK)
+        if hi > lo:
+            fill_chunk(np.random.default_rng([*key, c]), out[lo:hi])
+
+    if nchunks == 1:
+        one(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one, range(nchunks)))
+    return out.reshape(shape)
+
+
+def normal_f16(key, shape) -> np.ndarray:
+    """N(0,1) float32 draws rounded to fp16 (RNE)."""
+    def fill(rng, dst):
+        dst[:] = rng.standard_normal(dst.shape[0], dtype=np.float32)
+    return _chunked(tuple(key), tuple(shape), np.float16, fill)
+
+
+def uniform_i8(key, shape) -> np.ndarray:
+    """Uniform integers in [-127, 127] (filler for unused int8 pool slots)."""
+    def fill(rng, dst):
+        dst[:] = rng.integers(-127, 128, dst.shape[0], dtype=np.int8)
+    return _chunked(tuple(key), tuple(shape), np.int8, fill)
+
+
+def uniform_scale_f16(key, shape) -> np.ndarray:
+    """Uniform (0.005, 0.05) rounded to fp16 (filler scales for unused blocks)."""
+    def fill(rng, dst):
+        dst[:] = rng.uniform(0.005, 0.05, dst.shape[0]).astype(np.float32)
+    return _chunked(tuple(key), tuple(shape), np.float16, fill)
+
+
+@dataclass
+class StepDraw:
+    """One step: every sequence (in canonical order) appends ``q_lens[i]`` new
+    tokens, which are written and then queried (packed, sequence-major)."""
+    q_lens: np.ndarray            # int64 [S]
+    new_k: np.ndarray             # fp16 [T, Hkv, D]
+    new_v: np.ndarray             # fp16 [T, Hkv, D]
+    q: np.ndarray                 # fp16 [T, Hq, D]
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    kv_dtype: str                 # "f16" or "i8"
+    scale: float
+    num_blocks: int
+    first_pops: Optional[np.ndarray]   # free-list order: successive pops return these ids
+    ctx_lens: np.ndarray          # tokens cached per sequence before the first step
+    # initial pool contents, drawn on first access: fp16 [NB, Hkv, bs, D]
+    # (int8 codes for int8 pools) and fp16 [NB, Hkv] scales for int8 pools
+    pool_draws: dict = field(default_factory=dict, repr=False)
+    steps: list = field(default_factory=list)   # list[StepDraw] or a callable(step)->StepDraw
+    num_steps: int = 1
+    # sharing (workload 4): request r holds ctx_lens[r] tokens whose first
+    # ``shared_prefix`` tokens are one chain of blocks common to all requests;
+    # request r is forked into ``beams[r]`` sequences before the step.
+    shared_prefix: int = 0
+    beams: Optional[np.ndarray] = None
+    # int8 pools: the fp16 K/V of the cached context of sequence i, written
+    # token by token into the pool before the first step.
+    context: Optional[Callable[[int], tuple]] = None
+
+    _cache: dict = field(default_factory=dict, repr=False)
+
+    def _pool(self, name):
+        if name not in self.pool_draws:
+            return None
+        if name not in self._cache:
+            self._cache[name] = self.pool_draws[name]()
+        return self._cache[name]
+
+    @property
+    def pool_k(self) -> np.ndarray:
+        return self._pool("k")
+
+    @property
+    def pool_v(self) -> np.ndarray:
+        return self._pool("v")
+
+    @property
+    def pool_k_scale(self) -> Optional[np.ndarray]:
+        return self._pool("k_scale")
+
+    @property
+    def pool_v_scale(self) -> Optional[np.ndarray]:
+        return self._pool("v_scale")
+
+    def drop_pools(self) -> None:
+        """Forget the drawn pool arrays (they are redrawn identically on access)."""
+        self._cache.clear()
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def step(self, s: int) -> StepDraw:
+        if callable(self.steps):
+            return self.steps(s)
+        return self.steps[s]
+
+    @property
+    def num_seqs(self) -> int:
+        if self.beams is not None:
+            return int(np.sum(self.beams))
+        return len(self.ctx_lens)
+
+
+def _ceil_div(a, b):
+    return -(-a // b)
+
+
+def _f16_pool(seed, nb, hkv, d):
+    return {
+        "k": lambda: normal_f16((seed, S_POOL_K), (nb, hkv, BLOCK_SIZE, d)),
+        "v": lambda: normal_f16((seed, S_POOL_V), (nb, hkv, BLOCK_SIZE, d)),
+    }
+
+
+def _step(seed, tag, q_lens, hq, hkv, d):
+    t = int(np.sum(q_lens))
+    return StepDraw(
+        q_lens=np.asarray(q_lens, np.int64),
+        new_k=normal_f16((seed, S_NEW_K, *tag), (t, hkv, d)),
+        new_v=normal_f16((seed, S_NEW_V, *tag), (t, hkv, d)),
+        q=normal_f16((seed, S_Q, *tag), (t, hq, d)),
+    )
+
+
+def config1(seed: int = 47001) -> Workload:
+    """Tiny MHA decode: 12/12 heads, d64, bs 16, an 8-block pool; post-write
+    lengths 40/20/16/30; the free list is a seeded permutation of 0..7."""
+    hq = hkv = 12
+    d = 64
+    nb = 8
+    rng = np.random.default_rng([seed, S_META])
+    perm = rng.permutation(nb)
+    post = np.array([40, 20, 16, 30], np.int64)
+    return Workload(
+        name="tiny-mha-decode", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
+        first_pops=perm, ctx_lens=post - 1,
+        pool_draws=_f16_pool(seed, nb, hkv, d),
+        steps=[_step(seed, (0,), np.ones(4, np.int64), hq, hkv, d)],
+    )
+
+
+def config2(seed: int = 47002, num_seqs: int = 32, min_prompt: int = 32, max_prompt: int = 512,
+            decode_steps: int = 64) -> Workload:
+    """GPT-2-small-shaped batch: 12/12 heads, d64; prompts U[32,512] prefilled
+    (step 0, causal), then ``decode_steps`` steps of one token per sequence.
+    Plain free list (first pops 0, 1, 2, ...); blocks grow on demand."""
+    hq = hkv = 12
+    d = 64
+    rng = np.random.default_rng([seed, S_META])
+    prompts = rng.integers(min_prompt, max_prompt + 1, num_seqs).astype(np.int64)
+    nb = num_seqs * _ceil_div(max_prompt + decode_steps, BLOCK_SIZE)
+
+    def steps(s):
+        if s == 0:
+            return _step(seed, (0,), prompts, hq, hkv, d)
+        return _step(seed, (s,), np.ones(num_seqs, np.int64), hq, hkv, d)
+
+    return Workload(
+        name="gpt2-continuous-batch", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
+        first_pops=None, ctx_lens=np.zeros(num_seqs, np.int64),
+        pool_draws=_f16_pool(seed, nb, hkv, d),
+        steps=steps, num_steps=1 + decode_steps,
+    )
+
+
+def config3(seed: int = 47003, num_seqs: int = 256, max_len: int = 4096, min_len: int = 1,
+            num_q_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128) -> Workload:
+    """GQA decode: 32/8 heads, d128; post-write lengths U[1,4096]; pool = the
+    blocks needed plus 10%, free list a seeded permutation of the pool."""
+    hq, hkv, d = num_q_heads, num_kv_heads, head_dim
+    rng = np.random.default_rng([seed, S_META])
+    post = rng.integers(min_len, max_len + 1, num_seqs).astype(np.int64)
+    nb = int(math.ceil(1.1 * int(np.sum(_ceil_div(post, BLOCK_SIZE)))))
+    perm = rng.permutation(nb)
+    return Workload(
+        name="gqa-decode", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
+        first_pops=perm, ctx_lens=post - 1,
+        pool_draws=_f16_pool(seed, nb, hkv, d),
+        steps=[_step(seed, (0,), np.ones(num_seqs, np.int64), hq, hkv, d)],
+    )
+
+
+def config4(seed: int = 47004, num_requests: int = 64, prefix: int = 1024, min_suffix: int = 16,
+            max_suffix: int = 256, beam_requests: int = 16, beam_width: int = 4) -> Workload:
+    """Shared prefix + beam copy-on-write: every request's table starts with
+    the same ``prefix``-token chain; suffixes U[16,256]; requests
+    0..beam_requests-1 are forked into ``beam_width`` sequences; one decode
+    token per sequence.  Free list is a seeded permutation."""
+    hq, hkv, d = 32, 8, 128
+    rng = np.random.default_rng([seed, S_META])
+    suffix = rng.integers(min_suffix, max_suffix + 1, num_requests).astype(np.int64)
+    beams = np.ones(num_requests, np.int64)
+    beams[:beam_requests] = beam_width
+    need = _ceil_div(prefix, BLOCK_SIZE) + int(np.sum(beams * _ceil_div(suffix + 1, BLOCK_SIZE)))
+    nb = int(math.ceil(1.1 * need))
+    perm = rng.permutation(nb)
+    nseq = int(np.sum(beams))
+    return Workload(
+        name="prefix-share-beam-cow", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
+        first_pops=perm, ctx_lens=prefix + suffix,
+        pool_draws=_f16_pool(seed, nb, hkv, d),
+        steps=[_step(seed, (0,), np.ones(nseq, np.int64), hq, hkv, d)],
+        shared_prefix=prefix, beams=beams,
+    )
+
+
+def config5(seed: int = 47005, num_chunks: int = 8, chunk_q: int = 512, max_chunk_ctx: int = 8192,
+            num_decode: int = 192, max_decode_len: int = 32768) -> Workload:
+    """Packed chunked prefill + decode over an int8 pool: ``num_chunks``
+    segments of ``chunk_q`` query tokens with cached context U[0,8192], then
+    ``num_decode`` decode sequences with post-write length U[1,32768].  The
+    cached context is N(0,1) fp16 K/V, written into the int8 pool token by
+    token before the step.  Unused pool slots hold uniform int8 filler."""
+    hq, hkv, d = 32, 8, 128
+    rng = np.random.default_rng([seed, S_META])
+    cctx = rng.integers(0, max_chunk_ctx + 1, num_chunks).astype(np.int64)
+    dpost = rng.integers(1, max_decode_len + 1, num_decode).astype(np.int64)
+    ctx = np.concatenate([cctx, dpost - 1])
+    q_lens = np.concatenate([np.full(num_chunks, chunk_q, np.int64), np.ones(num_decode, np.int64)])
+    post = ctx + q_lens
+    nb = int(math.ceil(1.1 * int(np.sum(_ceil_div(post, BLOCK_SIZE)))))
+    perm = rng.permutation(nb)
+
+    def context(i):
+        n = int(ctx[i])
+        return (normal_f16((seed, S_CTX_K, i), (n, hkv, d)),
+                normal_f16((seed, S_CTX_V, i), (n, hkv, d)))
+
+    return Workload(
+        name="packed-int8-prefill-decode", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        block_size=BLOCK_SIZE, kv_dtype="i8", scale=1.0 / math.sqrt(d), num_blocks=nb,
+        first_pops=perm, ctx_lens=ctx,
+        pool_draws={
+            "k": lambda: uniform_i8((seed, S_POOL_K), (nb, hkv, BLOCK_SIZE, d)),
+            "v": lambda: uniform_i8((seed, S_POOL_V), (nb, hkv, BLOCK_SIZE, d)),
+            "k_scale": lambda: uniform_scale_f16((seed, S_KSCALE), (nb, hkv)),
+            "v_scale": lambda: uniform_scale_f16((seed, S_VSCALE), (nb, hkv)),
+        },
+        steps=[_step(seed, (0,), q_lens, hq, hkv, d)],
+        context=context,
+    )
+
+
+CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
