@@ -1,0 +1,193 @@
+/*
+ * pa.h - C ABI of libpa.so: paged KV writes and paged attention on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The pages this library follows (cited by title and section):
+ *   [pytorch]   "How to Implement Paged Attention in PyTorch and vLLM"
+ *   [engine]    "Building a paged inference engine from scratch, and measuring
+ *               it honestly"
+ *   [manager]   "Build a paged KV cache manager from scratch"
+ *   [nanoserve] "Day 14: the block allocator, paging for attention starts as
+ *               pure bookkeeping"
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Every buffer argument is a DEVICE pointer unless its name starts with
+ *   h_ (host memory).  The caller owns every buffer, including the attention
+ *   workspace; the library allocates no device memory and keeps no global
+ *   mutable state.
+ * - Work is enqueued on `stream` and returns without synchronising.  The
+ *   status only covers what the host can check: argument validation and kernel
+ *   launch errors.  Arguments are checked before anything is enqueued.
+ * - KV pool layout (a reading: the pages store K and V either in one per-block
+ *   slab, [manager] "Step 1: The Block", or as two tensors, [pytorch]
+ *   "Allocate, append, and free KV-cache blocks"): two pools, K and V, each
+ *       fp16  [num_blocks][num_kv_heads][block_size][head_dim]   (PA_KV_F16)
+ *       int8  [num_blocks][num_kv_heads][block_size][head_dim]   (PA_KV_I8)
+ *   so one (block, KV head) tile is one contiguous run of
+ *   block_size * head_dim elements.  int8 pools carry per-block-per-head fp16
+ *   scales k_scale, v_scale [num_blocks][num_kv_heads] ([engine] "INT8 KV
+ *   cache design": symmetric, no zero point, one scale per block per head).
+ * - Supported shapes: block_size 16, head_dim 64 or 128, num_q_heads a
+ *   multiple of num_kv_heads with a group size of 1, 2, 4 or 8,
+ *   num_blocks * block_size < 2^31.  Anything else returns
+ *   PA_ERR_UNSUPPORTED (or PA_ERR_SHAPE for inconsistent sizes).
+ * - Device-side integer data (slots, block ids, lengths) are preconditions.
+ *   Kernels never read or write outside the pools for out-of-range values:
+ *   an out-of-range slot is skipped and an out-of-range block id reads block
+ *   0, so bad metadata gives wrong numbers, never a memory fault.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,         /* a required pointer is NULL                       */
+  PA_ERR_SHAPE = 2,        /* sizes inconsistent with each other               */
+  PA_ERR_DTYPE = 3,        /* unknown kv_dtype                                 */
+  PA_ERR_UNSUPPORTED = 4,  /* valid but not built: block size, head dim, group */
+  PA_ERR_WORKSPACE = 5,    /* workspace smaller than pa_attend_workspace_bytes */
+  PA_ERR_HIP = 6           /* a HIP launch failed                              */
+} pa_status;
+
+typedef enum { PA_KV_F16 = 0, PA_KV_I8 = 1 } pa_kv_dtype;
+
+/* Shape of one KV pool pair (see the layout above). */
+typedef struct {
+  int32_t num_blocks;    /* physical blocks in each pool                  */
+  int32_t block_size;    /* tokens per block (16)                         */
+  int32_t num_kv_heads;
+  int32_t head_dim;      /* 64 or 128                                     */
+  int32_t kv_dtype;      /* pa_kv_dtype                                   */
+} pa_cache_desc;
+
+/*
+ * pa_write_kv - write this step's new K/V rows into the pools through a slot
+ * mapping ([pytorch] "How to implement paged attention: the minimal data
+ * flow", steps 2-3; "Map the PyTorch design to vLLM PagedAttention": slot
+ * mappings are integer tensors handed over each step).
+ *
+ *   k, v          fp16 [num_tokens][num_kv_heads][head_dim], row-major.
+ *   slot_mapping  int32 [num_tokens]; slot = block_id * block_size + offset.
+ *                 A negative slot skips that token (padding).  Slots of one
+ *                 call must be distinct.
+ *   k_cache, v_cache  the pools (fp16 or int8 codes, per desc->kv_dtype).
+ *   k_scale, v_scale  fp16 [num_blocks][num_kv_heads] for PA_KV_I8, else
+ *                 ignored (may be NULL).
+ *
+ * fp16: token t's K/V of every head are copied bit-for-bit to offset
+ * slot % block_size of block slot / block_size.
+ *
+ * int8 ([engine] "INT8 KV cache design": on every token write the block's
+ * entries are dequantised, the new token appended, a new max-abs scale taken
+ * and everything requantised).  For each token in increasing t, separately
+ * for K and V and for each KV head, with o = slot % block_size and entries
+ * 0..o-1 of the block taken as valid:
+ *     x_j = float(code_j) * float(scale)  (j < o),  x_o = float(new)
+ *     scale' = fp16_rne(max_j |x_j| / 127.0f)        (IEEE fp32 division)
+ *     code_j = clamp(rint_half_even(x_j / float(scale')), -127, 127)
+ *              (all zero if scale' == 0), for j = 0..o.
+ * Entries past o are not touched.  Tokens that write the same block in one
+ * call must be consecutive in t with consecutive offsets (a sequence's new
+ * tokens packed in position order), which is how the replay order is found.
+ */
+pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v,
+                      const int32_t* slot_mapping, int32_t num_tokens,
+                      void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                      hipStream_t stream);
+
+/*
+ * Dispatch options of pa_attend (NULL = defaults).
+ *   partition_tokens  keys per split-K partition of the vector path:
+ *                     0 = chosen from the batch, > 0 = this many (a multiple
+ *                     of 16), < 0 = never split.
+ *   mfma_min_rows     a sequence whose q_len * group rows reach this count
+ *                     runs on the MFMA path, otherwise on the vector path:
+ *                     0 = default (16), 1 = every sequence on MFMA,
+ *                     INT32_MAX = every sequence on the vector path.
+ */
+typedef struct {
+  int32_t partition_tokens;
+  int32_t mfma_min_rows;
+} pa_attend_opts;
+
+/*
+ * pa_attend_workspace_bytes - device workspace pa_attend needs for this batch
+ * (same arguments as pa_attend's host side).  Returns 0 when the arguments
+ * are invalid (pa_attend then reports why).  The size depends only on the
+ * host lengths, the head counts and the options.
+ */
+size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
+                                 int32_t num_seqs, const int32_t* h_seq_lens,
+                                 const int32_t* h_q_lens, const pa_attend_opts* opts);
+
+/*
+ * pa_attend - scaled dot-product attention of a packed batch over paged K/V,
+ * walking each sequence's block table ([pytorch] "Compute reference attention
+ * without hiding the layout" for what is computed; "Map the PyTorch design to
+ * vLLM PagedAttention": fused kernels read the block table directly, so no
+ * contiguous copy is made; [engine] "02 The engine": kernel parameters
+ * block_table, q_len_per_seq, kv_len_per_seq, block_size, and one packed
+ * batch of prefill and decode rows).
+ *
+ *   q             fp16 [total_q][num_q_heads][head_dim], sequence-major:
+ *                 sequence i's q_lens[i] rows follow sequence i-1's.
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entry b of row i is
+ *                 the physical block of logical block b of sequence i.
+ *   seq_lens      int32 [num_seqs]: keys of sequence i after this step's
+ *                 writes (its new tokens included: write, then attend).
+ *   q_lens        int32 [num_seqs]: query rows of sequence i (0 allowed).
+ *   h_seq_lens, h_q_lens  host copies of the same values; the launch shape is
+ *                 chosen from them, so they must equal the device arrays.
+ *   scale         multiplier of q.k (normally head_dim ** -0.5).
+ *   out           fp16 [total_q][num_q_heads][head_dim].
+ *   workspace     device scratch of at least pa_attend_workspace_bytes.
+ *
+ * Query row t (0-based) of sequence i sits at position
+ * seq_lens[i] - q_lens[i] + t and attends to keys 0 .. that position
+ * ([engine] "03 Correctness, and the bugs a real model found": the mask uses
+ * the query's real position).  Query head h reads KV head h / group
+ * ([pytorch] reference attention: each KV head repeated group times along a
+ * new axis).  Softmax runs in fp32 with a running max; long key ranges are
+ * split into partitions whose (max, sum, output) are merged in log-sum-exp
+ * form.  Requires q_lens[i] <= seq_lens[i] and
+ * ceil(seq_lens[i] / block_size) <= max_blocks_per_seq.
+ */
+pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_heads,
+                    const void* k_cache, const void* v_cache,
+                    const void* k_scale, const void* v_scale,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
+                    const int32_t* h_seq_lens, const int32_t* h_q_lens,
+                    float scale, void* out, void* workspace, size_t workspace_bytes,
+                    const pa_attend_opts* opts, hipStream_t stream);
+
+/*
+ * pa_copy_blocks - copy whole blocks (every KV head, every slot, and the
+ * scales of int8 pools) from src to dst, for copy-on-write of a shared block
+ * before its first divergent write ([pytorch] "Map the PyTorch design to vLLM
+ * PagedAttention": shared blocks are copied only on the first divergent write;
+ * [manager] "Architecture Overview": the diverging block is duplicated).
+ *
+ *   src_dst  int32 [num_pairs][2] = (src, dst) pairs.  No dst may also be a
+ *            src or another pair's dst in the same call.
+ */
+pa_status pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache,
+                         void* k_scale, void* v_scale, const int32_t* src_dst,
+                         int32_t num_pairs, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* pa_status_str(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

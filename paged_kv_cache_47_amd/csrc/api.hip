@@ -1,0 +1,336 @@
+// C ABI of libpa.so: argument validation, workspace layout, dispatch.
+#include <algorithm>
+#include <climits>
+#include <cstring>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+// ------------------------------------------------------------------ plan ----
+// One workgroup turns the device lengths into the work lists the attention
+// kernels consume: per-sequence (kv_len, q_len, q_start) after clamping, the
+// vector-path rows and their split-K units, and the MFMA row tiles.  The
+// host computes the same counts from its copies of the lengths to size the
+// launches (caps); every list is filled up to its cap, unused entries marked
+// with seq = -1, so kernels never read an unwritten entry even if the host and
+// device lengths disagree.
+constexpr int kPlanThreads = 1024;
+
+__device__ int block_exclusive_scan(int v, int* lds, int& total) {
+  const int tid = threadIdx.x;
+  lds[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    int add = tid >= off ? lds[tid - off] : 0;
+    __syncthreads();
+    lds[tid] += add;
+    __syncthreads();
+  }
+  const int incl = lds[tid];
+  total = lds[kPlanThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__device__ __forceinline__ int parts_for(int nvis, int part) { return part <= 0 ? 1 : (nvis + part - 1) / part; }
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int lds[kPlanThreads];
+  int base_q = 0, base_vt = 0, base_vu = 0, base_mu = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
+    const int i = c0 + threadIdx.x;
+    int L = 0, Q = 0, nvt = 0, nvu = 0, nmu = 0;
+    if (i < a.num_seqs) {
+      L = min(max(a.seq_lens[i], 0), a.max_kv);
+      Q = min(max(a.q_lens[i], 0), L);
+    }
+    int tot;
+    int qs = base_q + block_exclusive_scan(Q, lds, tot);
+    const int qsum = tot;
+    if (i < a.num_seqs) {
+      // rows beyond the packed batch the host sized are dropped
+      Q = max(0, min(Q, a.total_q - qs));
+      if (Q > 0 && Q * a.group >= a.min_rows) {
+        nmu = (Q * a.group + kMfmaRows - 1) / kMfmaRows;
+      } else {
+        nvt = Q;
+        for (int t = 0; t < Q; ++t) nvu += parts_for(L - Q + t + 1, a.part);
+      }
+    }
+    const int vt0 = base_vt + block_exclusive_scan(nvt, lds, tot);
+    const int vtsum = tot;
+    const int vu0 = base_vu + block_exclusive_scan(nvu, lds, tot);
+    const int vusum = tot;
+    const int mu0 = base_mu + block_exclusive_scan(nmu, lds, tot);
+    const int musum = tot;
+    if (i < a.num_seqs) {
+      SeqInfo si;
+      si.kv_len = L;
+      si.q_len = Q;
+      si.q_start = qs;
+      si.pad = 0;
+      a.seqs[i] = si;
+      for (int r = 0; r < nmu; ++r)
+        if (mu0 + r < a.cap_munit) a.munit[mu0 + r] = make_int2(i, r);
+      int u = vu0;
+      for (int t = 0; t < nvt; ++t) {
+        const int parts = parts_for(L - Q + t + 1, a.part);
+        const int k = vt0 + t;
+        const bool fits = k < a.cap_vtok && u + parts <= a.cap_vunit;
+        if (k < a.cap_vtok) {
+          VTok vt;
+          vt.seq = fits ? i : -1;
+          vt.t = t;
+          vt.u0 = u;
+          vt.parts = parts;
+          a.vtok[k] = vt;
+        }
+        for (int p = 0; p < parts; ++p)
+          if (u + p < a.cap_vunit) a.vunit[u + p] = make_int2(fits ? k : -1, p);
+        u += parts;
+      }
+    }
+    base_q += qsum;
+    base_vt += vtsum;
+    base_vu += vusum;
+    base_mu += musum;
+  }
+  __syncthreads();
+  for (int k = base_vt + threadIdx.x; k < a.cap_vtok; k += kPlanThreads) {
+    VTok vt;
+    vt.seq = -1;
+    vt.t = vt.u0 = vt.parts = 0;
+    a.vtok[k] = vt;
+  }
+  for (int u = base_vu + threadIdx.x; u < a.cap_vunit; u += kPlanThreads) a.vunit[u] = make_int2(-1, 0);
+  for (int u = base_mu + threadIdx.x; u < a.cap_munit; u += kPlanThreads) a.munit[u] = make_int2(-1, 0);
+}
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+  plan_kernel<<<1, kPlanThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ host plan ----
+struct HostPlan {
+  int32_t part = 0, min_rows = 16, total_q = 0;
+  int64_t n_vtok = 0, n_vunit = 0, n_munit = 0;
+  int32_t max_parts = 0;
+  size_t off_seqs = 0, off_vtok = 0, off_vunit = 0, off_munit = 0, off_lse = 0, off_po = 0, bytes = 0;
+};
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static pa_status check_desc(const pa_cache_desc* d) {
+  if (d == nullptr) return PA_ERR_NULL;
+  if (d->kv_dtype != PA_KV_F16 && d->kv_dtype != PA_KV_I8) return PA_ERR_DTYPE;
+  if (d->num_blocks <= 0 || d->num_kv_heads <= 0 || d->block_size <= 0 || d->head_dim <= 0) return PA_ERR_SHAPE;
+  if (d->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)d->num_blocks * d->block_size >= ((int64_t)1 << 31)) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+static pa_status check_heads(const pa_cache_desc* d, int32_t hq) {
+  if (hq <= 0 || hq % d->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int g = hq / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+// Keys per split-K partition when the caller leaves it to the library: aim
+// for about 16 workgroups per compute unit over the whole vector path, with
+// partitions of 256 .. 4096 keys.
+static int32_t auto_part(int64_t total_keys, int32_t hkv) {
+  const int64_t target_units = 256 * 16;
+  int64_t p = total_keys * hkv / target_units;
+  p = (p + 255) / 256 * 256;
+  return (int32_t)std::min<int64_t>(4096, std::max<int64_t>(256, p));
+}
+
+static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs, const int32_t* hL,
+                           const int32_t* hQ, int32_t max_blocks, const pa_attend_opts* opts, HostPlan& P) {
+  pa_status st = check_desc(d);
+  if (st != PA_OK) return st;
+  if ((st = check_heads(d, hq)) != PA_OK) return st;
+  if (num_seqs < 0) return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (hL == nullptr || hQ == nullptr)) return PA_ERR_NULL;
+  const int g = hq / d->num_kv_heads;
+  int32_t req_part = opts ? opts->partition_tokens : 0;
+  P.min_rows = (opts && opts->mfma_min_rows > 0) ? opts->mfma_min_rows : 16;
+  if (req_part > 0 && req_part % kBlockSize != 0) return PA_ERR_SHAPE;
+  const int64_t max_kv = (int64_t)max_blocks * kBlockSize;
+  int64_t total_q = 0, vec_keys = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    if (hL[i] < 0 || hQ[i] < 0 || hQ[i] > hL[i] || hL[i] > max_kv) return PA_ERR_SHAPE;
+    total_q += hQ[i];
+    if (!(hQ[i] > 0 && (int64_t)hQ[i] * g >= P.min_rows))
+      for (int t = 0; t < hQ[i]; ++t) vec_keys += hL[i] - hQ[i] + t + 1;
+  }
+  if (total_q >= INT32_MAX / 2) return PA_ERR_SHAPE;
+  P.total_q = (int32_t)total_q;
+  P.part = req_part > 0 ? req_part : (req_part < 0 ? 0 : auto_part(vec_keys, d->num_kv_heads));
+  for (int i = 0; i < num_seqs; ++i) {
+    const int L = hL[i], Q = hQ[i];
+    if (Q > 0 && (int64_t)Q * g >= P.min_rows) {
+      P.n_munit += ((int64_t)Q * g + kMfmaRows - 1) / kMfmaRows;
+    } else {
+      P.n_vtok += Q;
+      for (int t = 0; t < Q; ++t) {
+        const int nvis = L - Q + t + 1;
+        const int parts = P.part <= 0 ? 1 : (nvis + P.part - 1) / P.part;
+        P.n_vunit += parts;
+        P.max_parts = std::max(P.max_parts, parts);
+      }
+    }
+  }
+  if (P.n_vunit >= INT32_MAX / 2 || P.n_munit >= INT32_MAX / 2) return PA_ERR_SHAPE;
+  size_t off = 0;
+  P.off_seqs = off;
+  off = align_up(off + sizeof(SeqInfo) * (size_t)std::max(num_seqs, 1), 256);
+  P.off_vtok = off;
+  off = align_up(off + sizeof(VTok) * (size_t)std::max<int64_t>(P.n_vtok, 1), 256);
+  P.off_vunit = off;
+  off = align_up(off + sizeof(int2) * (size_t)std::max<int64_t>(P.n_vunit, 1), 256);
+  P.off_munit = off;
+  off = align_up(off + sizeof(int2) * (size_t)std::max<int64_t>(P.n_munit, 1), 256);
+  const bool split = P.max_parts > 1;
+  P.off_lse = off;
+  if (split) off = align_up(off + sizeof(float) * (size_t)P.n_vunit * hq, 256);
+  P.off_po = off;
+  if (split) off = align_up(off + sizeof(float) * (size_t)P.n_vunit * hq * d->head_dim, 256);
+  P.bytes = off;
+  return PA_OK;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "sizes are inconsistent";
+    case PA_ERR_DTYPE: return "unknown kv dtype";
+    case PA_ERR_UNSUPPORTED: return "unsupported block size, head dim or group size";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v, const int32_t* slot_mapping,
+                      int32_t num_tokens, void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                      hipStream_t stream) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  hipError_t e;
+  if (desc->kv_dtype == PA_KV_I8) {
+    if (!k_scale || !v_scale) return PA_ERR_NULL;
+    if (num_tokens > 2147483647 / 1) return PA_ERR_SHAPE;
+    e = launch_write_i8(*desc, k, v, slot_mapping, num_tokens, k_cache, v_cache, k_scale, v_scale, stream);
+  } else {
+    e = launch_write_f16(*desc, k, v, slot_mapping, num_tokens, k_cache, v_cache, stream);
+  }
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                         const int32_t* src_dst, int32_t num_pairs, hipStream_t stream) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !src_dst) return PA_ERR_NULL;
+  if (desc->kv_dtype == PA_KV_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  hipError_t e = launch_copy(*desc, k_cache, v_cache, k_scale, v_scale, src_dst, num_pairs, stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads, int32_t num_seqs,
+                                 const int32_t* h_seq_lens, const int32_t* h_q_lens, const pa_attend_opts* opts) {
+  HostPlan P;
+  // the table width only bounds lengths; size the workspace for any width that fits them
+  if (make_plan(desc, num_q_heads, num_seqs, h_seq_lens, h_q_lens, INT32_MAX / kBlockSize, opts, P) != PA_OK)
+    return 0;
+  return P.bytes;
+}
+
+pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_heads, const void* k_cache,
+                    const void* v_cache, const void* k_scale, const void* v_scale, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
+                    const int32_t* h_seq_lens, const int32_t* h_q_lens, float scale, void* out, void* workspace,
+                    size_t workspace_bytes, const pa_attend_opts* opts, hipStream_t stream) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (max_blocks_per_seq < 0) return PA_ERR_SHAPE;
+  HostPlan P;
+  if ((st = make_plan(desc, num_q_heads, num_seqs, h_seq_lens, h_q_lens, max_blocks_per_seq, opts, P)) != PA_OK)
+    return st;
+  if (P.total_q == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !q_lens || !out || !workspace) return PA_ERR_NULL;
+  if (desc->kv_dtype == PA_KV_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (max_blocks_per_seq == 0) return PA_ERR_SHAPE;
+  if (workspace_bytes < P.bytes) return PA_ERR_WORKSPACE;
+
+  char* ws = (char*)workspace;
+  const int g = num_q_heads / desc->num_kv_heads;
+  const bool i8 = desc->kv_dtype == PA_KV_I8;
+
+  PlanArgs pl;
+  pl.seq_lens = seq_lens;
+  pl.q_lens = q_lens;
+  pl.seqs = (SeqInfo*)(ws + P.off_seqs);
+  pl.vtok = (VTok*)(ws + P.off_vtok);
+  pl.vunit = (int2*)(ws + P.off_vunit);
+  pl.munit = (int2*)(ws + P.off_munit);
+  pl.num_seqs = num_seqs;
+  pl.group = g;
+  pl.part = P.part;
+  pl.min_rows = P.min_rows;
+  pl.max_kv = (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * kBlockSize, INT32_MAX);
+  pl.total_q = P.total_q;
+  pl.cap_vtok = (int32_t)P.n_vtok;
+  pl.cap_vunit = (int32_t)P.n_vunit;
+  pl.cap_munit = (int32_t)P.n_munit;
+  if (launch_plan(pl, stream) != hipSuccess) return PA_ERR_HIP;
+
+  AttnArgs a;
+  a.q = (const half_t*)q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.ks = (const half_t*)k_scale;
+  a.vs = (const half_t*)v_scale;
+  a.block_tables = block_tables;
+  a.seqs = pl.seqs;
+  a.vtok = pl.vtok;
+  a.vunit = pl.vunit;
+  a.munit = pl.munit;
+  a.plse = P.max_parts > 1 ? (float*)(ws + P.off_lse) : nullptr;
+  a.po = P.max_parts > 1 ? (float*)(ws + P.off_po) : nullptr;
+  a.out = (half_t*)out;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = desc->num_blocks;
+  a.hq = num_q_heads;
+  a.hkv = desc->num_kv_heads;
+  a.part = P.part > 0 ? P.part : INT32_MAX / 2;
+  a.scale_log2 = scale * kLog2e;
+
+  if (P.n_vunit > 0) {
+    if (launch_decode(a, desc->head_dim, g, i8, (int)P.n_vunit, stream) != hipSuccess) return PA_ERR_HIP;
+    if (P.max_parts > 1 && launch_reduce(a, desc->head_dim, (int)P.n_vtok, stream) != hipSuccess) return PA_ERR_HIP;
+  }
+  if (P.n_munit > 0) {
+    if (launch_prefill(a, desc->head_dim, g, i8, (int)P.n_munit, stream) != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

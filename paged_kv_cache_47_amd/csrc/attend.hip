@@ -1,0 +1,481 @@
+// Paged attention kernels for gfx950.
+//
+// What is computed ([pytorch] "Compute reference attention without hiding
+// the layout"): for each query row, scores q.k * scale over the keys it may
+// see, softmax, weighted sum of V; KV head = query head / group.  The block
+// table is walked inside the kernels, so no contiguous K/V copy is made
+// ([pytorch] "Map the PyTorch design to vLLM PagedAttention").  Query row t of
+// a sequence with q_len rows and kv_len keys sits at position
+// kv_len - q_len + t and sees keys 0 .. that position ([engine] "03
+// Correctness, and the bugs a real model found").  int8 blocks are
+// dequantised in registers before each of the two products ([engine] "INT8
+// KV cache design").
+//
+// Two paths:
+//  * vector path (decode and other short query groups): one workgroup per
+//    (query row, KV head, split-K partition); the G query heads of the KV head
+//    are processed together so every K/V element loaded from HBM serves all G
+//    rows.  K/V tiles arrive as 16-byte loads (one (block, head) tile is a
+//    contiguous 2-4 KB run); fp32 online softmax with a running max; partials
+//    of split rows are merged by `reduce_kernel` in log-sum-exp form.
+//  * MFMA path (prefill / chunked prefill, q_len * G >= 16 rows): 64 query
+//    rows per workgroup (4 waves x 16), 32 keys per step, S^T = K Q^T and
+//    O^T = V^T P^T on v_mfma_f32_16x16x32_f16.  Computing the transposes makes
+//    each lane own one query row in both accumulators, and the P accumulator
+//    already sits in the B-operand layout of the second product.  V is staged
+//    in LDS and read with the gfx950 transposing LDS read.
+#include "pa_internal.h"
+
+namespace pa {
+
+// bytes b0 b1 of a dword of int8 codes -> exact fp16 pair, via 0x64XX = 1024 + XX
+__device__ __forceinline__ void i8x4_to_h2(uint32_t w, half2_t& lo, half2_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;  // biased: XX = code + 128
+  const uint32_t l = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t h = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const half2_t bias = {(half_t)1152.0f, (half_t)1152.0f};
+  lo = __builtin_bit_cast(half2_t, l) - bias;
+  hi = __builtin_bit_cast(half2_t, h) - bias;
+}
+
+// ============================================================ vector path ===
+template <int D, int G, bool I8, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
+  constexpr int EB = I8 ? 1 : 2;       // bytes per element
+  constexpr int E = 16 / EB;           // elements per lane per 16-byte load
+  constexpr int LPT = D / E;           // lanes per token row
+  constexpr int TPL = 64 / LPT;        // token rows per wave-wide load
+  constexpr int NL = kBlockSize / TPL; // loads per (block, head) tile
+  constexpr int E2 = E / 2;            // fp16 pairs per lane per row
+  constexpr int64_t TILE = (int64_t)kBlockSize * D * EB;
+
+  __shared__ float sm[NW][G], sl[NW][G];
+  __shared__ float so[NW][G][D];
+
+  const int u = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int2 un = a.vunit[u];
+  if (un.x < 0) return;
+  const VTok vt = a.vtok[un.x];
+  if (vt.seq < 0) return;
+  const SeqInfo si = a.seqs[vt.seq];
+  const int nvis = si.kv_len - si.q_len + vt.t + 1;
+  const int kbeg = un.y * a.part;
+  const int kend = min(nvis, kbeg + a.part);
+  const int grp = lane / LPT, sub = lane % LPT;
+  const int64_t row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
+  const int32_t* tbl = a.block_tables + (int64_t)vt.seq * a.max_blocks;
+
+  half2_t qh[G][E2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint4* qp = (const uint4*)(a.q + (row0 + g) * D + sub * E);
+#pragma unroll
+    for (int c = 0; c < E / 8; ++c) {
+      const uint4 w = qp[c];
+      qh[g][4 * c + 0] = __builtin_bit_cast(half2_t, w.x);
+      qh[g][4 * c + 1] = __builtin_bit_cast(half2_t, w.y);
+      qh[g][4 * c + 2] = __builtin_bit_cast(half2_t, w.z);
+      qh[g][4 * c + 3] = __builtin_bit_cast(half2_t, w.w);
+    }
+  }
+
+  float m[G], l[G], acc[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegBig;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+  }
+
+  const int bend = (kend + kBlockSize - 1) / kBlockSize;
+  int b = kbeg / kBlockSize + wave;
+  uint4 kr[NL], vr[NL];
+  int phys = 0;
+  auto load_tile = [&](int blk, uint4* kd, uint4* vd, int& ph) {
+    ph = clamp_block(tbl[blk], a.num_blocks);
+    const int64_t off = ((int64_t)ph * a.hkv + h) * TILE;
+    const uint4* kt = (const uint4*)((const char*)a.kc + off);
+    const uint4* vt2 = (const uint4*)((const char*)a.vc + off);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) kd[i] = kt[i * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) vd[i] = vt2[i * 64 + lane];
+  };
+  if (b < bend) load_tile(b, kr, vr, phys);
+
+  while (b < bend) {
+    const int bn = b + NW;
+    uint4 kn[NL], vn[NL];
+    int physn = 0;
+    if (bn < bend) load_tile(bn, kn, vn, physn);
+
+    float ksc = a.scale_log2, vsc = 1.f;
+    if constexpr (I8) {
+      ksc *= (float)a.ks[(int64_t)phys * a.hkv + h];
+      vsc = (float)a.vs[(int64_t)phys * a.hkv + h];
+    }
+    const int tok0 = b * kBlockSize + grp;
+    if (b * kBlockSize + kBlockSize > kend) {  // last block of the range: drop V of keys past it
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if (tok0 + i * TPL >= kend) vr[i] = make_uint4(0, 0, 0, 0);
+    }
+
+    float s[NL][G];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      half2_t kh[E2];
+      const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+      if constexpr (I8) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) i8x4_to_h2(w4[c], kh[2 * c], kh[2 * c + 1]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kh[c] = __builtin_bit_cast(half2_t, w4[c]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < E2; ++c) d = __builtin_amdgcn_fdot2(qh[g][c], kh[c], d, false);
+        d = group_sum<LPT>(d);
+        s[i][g] = (tok0 + i * TPL < kend) ? d * ksc : -__builtin_inff();
+      }
+    }
+
+    float vf[NL][E];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+      if constexpr (I8) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          half2_t lo, hi;
+          i8x4_to_h2(w4[c], lo, hi);
+          vf[i][4 * c + 0] = (float)lo.x * vsc;
+          vf[i][4 * c + 1] = (float)lo.y * vsc;
+          vf[i][4 * c + 2] = (float)hi.x * vsc;
+          vf[i][4 * c + 3] = (float)hi.y * vsc;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const half2_t p2 = __builtin_bit_cast(half2_t, w4[c]);
+          vf[i][2 * c + 0] = (float)p2.x;
+          vf[i][2 * c + 1] = (float)p2.y;
+        }
+      }
+    }
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mb = s[0][g];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) mb = fmaxf(mb, s[i][g]);
+      const float mn = fmaxf(m[g], mb);
+      const float alpha = fast_exp2(m[g] - mn);
+      m[g] = mn;
+      float p[NL];
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        p[i] = fast_exp2(s[i][g] - mn);
+        ps += p[i];
+      }
+      l[g] = l[g] * alpha + ps;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float x = acc[g][e] * alpha;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) x = fmaf(p[i], vf[i][e], x);
+        acc[g][e] = x;
+      }
+    }
+
+    b = bn;
+    phys = physn;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      kr[i] = kn[i];
+      vr[i] = vn[i];
+    }
+  }
+
+  // merge the TPL token-row streams of this wave (lane groups), then the waves
+#pragma unroll
+  for (int msk = LPT; msk < 64; msk <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mo = __shfl_xor(m[g], msk, 64);
+      const float lo = __shfl_xor(l[g], msk, 64);
+      const float mn = fmaxf(m[g], mo);
+      const float fa = fast_exp2(m[g] - mn), fb = fast_exp2(mo - mn);
+      l[g] = l[g] * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] = acc[g][e] * fa + __shfl_xor(acc[g][e], msk, 64) * fb;
+      m[g] = mn;
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) so[wave][g][sub * E + e] = acc[g][e];
+      if (sub == 0) {
+        sm[wave][g] = m[g];
+        sl[wave][g] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  const bool split = vt.parts > 1;
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int g = idx / D, d = idx % D;
+    float M = sm[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm[w][g]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(sm[w][g] - M);
+      Ls += sl[w][g] * f;
+      O += so[w][g][d] * f;
+    }
+    if (!split) {
+      a.out[(row0 + g) * D + d] = (half_t)(O / Ls);
+    } else {
+      const int64_t pr = (int64_t)u * a.hq + (int64_t)h * G + g;
+      a.po[pr * D + d] = O / Ls;
+      if (d == 0) a.plse[pr] = M + __builtin_log2f(Ls);
+    }
+  }
+}
+
+// Merge the split-K partials of one query row (all heads): base-2 log-sum-exp.
+template <int D>
+__global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
+  const VTok vt = a.vtok[blockIdx.x];
+  if (vt.seq < 0 || vt.parts <= 1) return;
+  const SeqInfo si = a.seqs[vt.seq];
+  const int64_t row = (int64_t)si.q_start + vt.t;
+  for (int idx = threadIdx.x; idx < a.hq * D; idx += 256) {
+    const int hq = idx / D, d = idx % D;
+    float M = -__builtin_inff();
+    for (int p = 0; p < vt.parts; ++p) M = fmaxf(M, a.plse[(int64_t)(vt.u0 + p) * a.hq + hq]);
+    float S = 0.f, O = 0.f;
+    for (int p = 0; p < vt.parts; ++p) {
+      const int64_t pr = (int64_t)(vt.u0 + p) * a.hq + hq;
+      const float w = fast_exp2(a.plse[pr] - M);
+      S += w;
+      O = fmaf(w, a.po[pr * D + d], O);
+    }
+    a.out[(row * a.hq + hq) * D + d] = (half_t)(O / S);
+  }
+}
+
+// ============================================================== MFMA path ===
+template <int D, int G, bool I8>
+__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;   // k-steps of 32 over the head dim
+  constexpr int NT = D / 16;   // 16-wide output column tiles
+  constexpr int BN = 32;       // keys per step (two blocks)
+  constexpr int LDV = D + 8;   // LDS row stride of the V tile, in halves
+  __shared__ __attribute__((aligned(16))) half_t vlds[BN * LDV];
+
+  const int u = blockIdx.x, h = blockIdx.y;
+  const int2 mu = a.munit[u];
+  if (mu.x < 0) return;
+  const SeqInfo si = a.seqs[mu.x];
+  const int L = si.kv_len, Q = si.q_len, rows = Q * G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int r0 = mu.y * kMfmaRows;
+  const int myrow = r0 + wave * 16 + l16;
+  const bool rvalid = myrow < rows;
+  const int tq = rvalid ? myrow / G : 0;
+  const int gq = myrow % G;
+  const int qpos = rvalid ? L - Q + tq : -1;
+  const int last_row = min(rows, r0 + kMfmaRows) - 1;
+  const int kmax = min(L, L - Q + last_row / G + 1);
+  const int32_t* tbl = a.block_tables + (int64_t)mu.x * a.max_blocks;
+  const int64_t orow = ((int64_t)(si.q_start + tq) * a.hq + (int64_t)h * G + gq) * D;
+
+  half8_t qop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (rvalid) qop[ks] = *(const half8_t*)(a.q + orow + ks * 32 + 8 * grp);
+    else qop[ks] = (half8_t)(half_t)0.f;
+  }
+
+  float4_t o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = (float4_t)0.f;
+  float m = kNegBig, lsum = 0.f;
+
+  for (int kt = 0; kt < kmax; kt += BN) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < BN * D / 8; c += 256) {
+      const int key = c / (D / 8), dc = c % (D / 8);
+      const int kg = kt + key;
+      half8_t val = (half8_t)(half_t)0.f;
+      if (kg < L) {
+        const int ph = clamp_block(tbl[kg / kBlockSize], a.num_blocks);
+        const int64_t base = (((int64_t)ph * a.hkv + h) * kBlockSize + (kg % kBlockSize)) * D + dc * 8;
+        if constexpr (I8) {
+          const uint2 w = *(const uint2*)((const int8_t*)a.vc + base);
+          half2_t h0, h1, h2, h3;
+          i8x4_to_h2(w.x, h0, h1);
+          i8x4_to_h2(w.y, h2, h3);
+          val = (half8_t){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+        } else {
+          val = *(const half8_t*)((const half_t*)a.vc + base);
+        }
+      }
+      *(half8_t*)(vlds + key * LDV + dc * 8) = val;
+    }
+    __syncthreads();
+
+    // Both 16-key blocks of the step always run their MFMAs: when the second
+    // block lies past the last key it re-reads the first block (always a valid
+    // table entry) and its scores are masked below.  Keeping MFMAs out of
+    // conditional code also keeps every MFMA-result read in straight-line code.
+    float4_t sacc[2];
+    float kscl[2] = {1.f, 1.f}, vscl[2] = {1.f, 1.f};
+    const int kb0 = kt / kBlockSize;
+    const int kb1 = (kb0 + 1) * kBlockSize < kmax ? kb0 + 1 : kb0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = (float4_t)0.f;
+      const int ph = clamp_block(tbl[kb == 0 ? kb0 : kb1], a.num_blocks);
+      const int64_t base = (((int64_t)ph * a.hkv + h) * kBlockSize + l16) * D + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        half8_t kop;
+        if constexpr (I8) {
+          const uint2 w = *(const uint2*)((const int8_t*)a.kc + base + ks * 32);
+          half2_t h0, h1, h2, h3;
+          i8x4_to_h2(w.x, h0, h1);
+          i8x4_to_h2(w.y, h2, h3);
+          kop = (half8_t){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+        } else {
+          kop = *(const half8_t*)((const half_t*)a.kc + base + ks * 32);
+        }
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[ks], sacc[kb], 0, 0, 0);
+      }
+      if constexpr (I8) {
+        kscl[kb] = (float)a.ks[(int64_t)ph * a.hkv + h];
+        vscl[kb] = (float)a.vs[(int64_t)ph * a.hkv + h];
+      }
+    }
+
+    // this lane: query row l16 of the wave; keys kt + 16 kb + 4 grp + e
+    float sv[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kt + kb * 16 + 4 * grp + e;
+        const float x = sacc[kb][e] * (a.scale_log2 * kscl[kb]);
+        sv[kb * 4 + e] = key <= qpos ? x : -__builtin_inff();
+      }
+    float mloc = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sv[j]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mn = fmaxf(m, mloc);
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    half8_t pop;
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = fast_exp2(sv[j] - mn);
+      if constexpr (I8) {
+        ps += p;
+        pop[j] = (half_t)(p * vscl[j / 4]);
+      } else {
+        const half_t ph = (half_t)p;  // the weight the product uses is also the one summed
+        ps += (float)ph;
+        pop[j] = ph;
+      }
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+
+    typedef __attribute__((address_space(3))) short4_t lds_short4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const half_t* p1 = vlds + (4 * grp + (l16 >> 2)) * LDV + nt * 16 + 4 * (l16 & 3);
+      const half_t* p2 = p1 + 16 * LDV;
+      const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
+      const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p2);
+      const half4_t h1 = __builtin_bit_cast(half4_t, v1), h2 = __builtin_bit_cast(half4_t, v2);
+      const half8_t vop = (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w};
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, o[nt], 0, 0, 0);
+    }
+  }
+
+  if (rvalid) {
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      half4_t r;
+      r.x = (half_t)(o[nt][0] * inv);
+      r.y = (half_t)(o[nt][1] * inv);
+      r.z = (half_t)(o[nt][2] * inv);
+      r.w = (half_t)(o[nt][3] * inv);
+      *(half4_t*)(a.out + orow + nt * 16 + 4 * grp) = r;
+    }
+  }
+}
+
+// =============================================================== dispatch ===
+template <int D, bool I8>
+static hipError_t decode_g(const AttnArgs& a, int g, int n, hipStream_t s) {
+  dim3 grid(n, a.hkv);
+  switch (g) {
+    case 1: decode_kernel<D, 1, I8, 4><<<grid, 256, 0, s>>>(a); break;
+    case 2: decode_kernel<D, 2, I8, 4><<<grid, 256, 0, s>>>(a); break;
+    case 4: decode_kernel<D, 4, I8, 4><<<grid, 256, 0, s>>>(a); break;
+    case 8: decode_kernel<D, 8, I8, 4><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, bool i8, int n, hipStream_t s) {
+  if (head_dim == 128) return i8 ? decode_g<128, true>(a, group, n, s) : decode_g<128, false>(a, group, n, s);
+  return i8 ? decode_g<64, true>(a, group, n, s) : decode_g<64, false>(a, group, n, s);
+}
+
+hipError_t launch_reduce(const AttnArgs& a, int head_dim, int n_vtok, hipStream_t s) {
+  if (head_dim == 128) reduce_kernel<128><<<n_vtok, 256, 0, s>>>(a);
+  else reduce_kernel<64><<<n_vtok, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int D, bool I8>
+static hipError_t prefill_g(const AttnArgs& a, int g, int n, hipStream_t s) {
+  dim3 grid(n, a.hkv);
+  switch (g) {
+    case 1: prefill_kernel<D, 1, I8><<<grid, 256, 0, s>>>(a); break;
+    case 2: prefill_kernel<D, 2, I8><<<grid, 256, 0, s>>>(a); break;
+    case 4: prefill_kernel<D, 4, I8><<<grid, 256, 0, s>>>(a); break;
+    case 8: prefill_kernel<D, 8, I8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, int group, bool i8, int n, hipStream_t s) {
+  if (head_dim == 128) return i8 ? prefill_g<128, true>(a, group, n, s) : prefill_g<128, false>(a, group, n, s);
+  return i8 ? prefill_g<64, true>(a, group, n, s) : prefill_g<64, false>(a, group, n, s);
+}
+
+}  // namespace pa

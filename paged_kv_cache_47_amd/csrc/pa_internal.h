@@ -1,0 +1,116 @@
+// Internal declarations shared by the libpa.so translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBlockSize = 16;     // tokens per block (the only size built)
+constexpr int kWave = 64;
+constexpr int kMfmaRows = 64;      // query rows per MFMA workgroup (4 waves x 16)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+
+// Per-sequence values after host/device agreement checks (written by the plan kernel).
+struct SeqInfo {
+  int32_t kv_len;   // keys after this step's writes, clamped to the table width
+  int32_t q_len;    // query rows, clamped to kv_len and to the packed batch
+  int32_t q_start;  // first packed row of the sequence
+  int32_t pad;
+};
+
+// One query row of the vector path: sequence, row within sequence, first unit, units.
+struct VTok {
+  int32_t seq, t, u0, parts;
+};
+
+struct AttnArgs {
+  const half_t* q;
+  const void* kc;
+  const void* vc;
+  const half_t* ks;
+  const half_t* vs;
+  const int32_t* block_tables;
+  const SeqInfo* seqs;
+  const VTok* vtok;
+  const int2* vunit;   // {vtok index, partition}
+  const int2* munit;   // {sequence, row tile}
+  float* po;           // [n_vunit][Hq][D] normalised partial outputs
+  float* plse;         // [n_vunit][Hq] base-2 log-sum-exp of each partial
+  half_t* out;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t hq, hkv;
+  int32_t part;        // keys per partition (a multiple of 16)
+  float scale_log2;    // scale * log2(e)
+};
+
+struct PlanArgs {
+  const int32_t* seq_lens;
+  const int32_t* q_lens;
+  SeqInfo* seqs;
+  VTok* vtok;
+  int2* vunit;
+  int2* munit;
+  int32_t num_seqs;
+  int32_t group;
+  int32_t part;        // <= 0: one partition per row
+  int32_t min_rows;
+  int32_t max_kv;      // max_blocks_per_seq * block_size
+  int32_t total_q;
+  int32_t cap_vtok, cap_vunit, cap_munit;
+};
+
+// Launchers (one translation unit each); all return hipGetLastError() after launch.
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, bool i8, int n_vunit, hipStream_t s);
+hipError_t launch_reduce(const AttnArgs& a, int head_dim, int n_vtok, hipStream_t s);
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, int group, bool i8, int n_munit, hipStream_t s);
+hipError_t launch_write_f16(const pa_cache_desc& d, const void* k, const void* v, const int32_t* slots,
+                            int32_t T, void* kc, void* vc, hipStream_t s);
+hipError_t launch_write_i8(const pa_cache_desc& d, const void* k, const void* v, const int32_t* slots,
+                           int32_t T, void* kc, void* vc, void* ks, void* vs, hipStream_t s);
+hipError_t launch_copy(const pa_cache_desc& d, void* kc, void* vc, void* ks, void* vs,
+                       const int32_t* pairs, int32_t n, hipStream_t s);
+
+// ----------------------------------------------------------------------------
+// Device helpers
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N in {1,2,4,8,16}); every lane of the group ends with the sum.
+// After the quad steps all lanes of a quad agree, so the row half-mirror (lane i <-> 7-i) acts
+// as an exchange with the other quad and the row mirror (lane i <-> 15-i) as one with the other
+// half-row.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);   // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+__device__ __forceinline__ int clamp_block(int b, int nb) { return (unsigned)b < (unsigned)nb ? b : 0; }
+
+}  // namespace pa
