@@ -105,7 +105,7 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v,
                       hipStream_t stream);
 
 /*
- * Dispatch options of pa_attend (NULL = defaults).
+ * Dispatch options of pa_attend (NULL = defaults; zero-initialise unused fields).
  *   partition_tokens  keys per split-K partition of the vector path:
  *                     0 = chosen from the batch, > 0 = this many (a multiple
  *                     of 16), < 0 = never split.
@@ -113,10 +113,18 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v,
  *                     runs on the MFMA path, otherwise on the vector path:
  *                     0 = default (16), 1 = every sequence on MFMA,
  *                     INT32_MAX = every sequence on the vector path.
+ *   vector_begin/end  optional caller-created HIP events, recorded on
+ *   mfma_begin/end    `stream` immediately before and after the vector-path
+ *                     (resp. MFMA-path) attention kernel when that kernel is
+ *                     launched; NULL = not recorded.  For per-kernel timing.
  */
 typedef struct {
   int32_t partition_tokens;
   int32_t mfma_min_rows;
+  hipEvent_t vector_begin;
+  hipEvent_t vector_end;
+  hipEvent_t mfma_begin;
+  hipEvent_t mfma_end;
 } pa_attend_opts;
 
 /*

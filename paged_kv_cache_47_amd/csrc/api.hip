@@ -16,41 +16,67 @@ namespace pa {
 // with seq = -1, so kernels never read an unwritten entry even if the host and
 // device lengths disagree.
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
 
-__device__ int block_exclusive_scan(int v, int* lds, int& total) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    int add = tid >= off ? lds[tid - off] : 0;
-    __syncthreads();
-    lds[tid] += add;
-    __syncthreads();
+// Exclusive scan of four counters over the workgroup (one sequence per
+// thread): wave-level shuffles, then the 16 wave totals through LDS.
+__device__ int4 block_exclusive_scan4(int4 v, int4* lds, int4& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int4 inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int4 t;
+    t.x = __shfl_up(inc.x, off, 64);
+    t.y = __shfl_up(inc.y, off, 64);
+    t.z = __shfl_up(inc.z, off, 64);
+    t.w = __shfl_up(inc.w, off, 64);
+    if (lane >= off) {
+      inc.x += t.x;
+      inc.y += t.y;
+      inc.z += t.z;
+      inc.w += t.w;
+    }
   }
-  const int incl = lds[tid];
-  total = lds[kPlanThreads - 1];
+  if (lane == 63) lds[wave] = inc;
   __syncthreads();
-  return incl - v;
+  int4 base = make_int4(0, 0, 0, 0);
+  total = make_int4(0, 0, 0, 0);
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const int4 t = lds[w];
+    if (w < wave) {
+      base.x += t.x;
+      base.y += t.y;
+      base.z += t.z;
+      base.w += t.w;
+    }
+    total.x += t.x;
+    total.y += t.y;
+    total.z += t.z;
+    total.w += t.w;
+  }
+  __syncthreads();
+  return make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
 }
 
 __device__ __forceinline__ int parts_for(int nvis, int part) { return part <= 0 ? 1 : (nvis + part - 1) / part; }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int lds[kPlanThreads];
+  __shared__ int4 lds[kPlanWaves];
   int base_q = 0, base_vt = 0, base_vu = 0, base_mu = 0;
   for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
     const int i = c0 + threadIdx.x;
-    int L = 0, Q = 0, nvt = 0, nvu = 0, nmu = 0;
+    int L = 0, Q = 0;
     if (i < a.num_seqs) {
       L = min(max(a.seq_lens[i], 0), a.max_kv);
       Q = min(max(a.q_lens[i], 0), L);
     }
-    int tot;
-    int qs = base_q + block_exclusive_scan(Q, lds, tot);
-    const int qsum = tot;
+    // the packed row offsets come from the unclamped-by-batch row counts
+    int4 tot;
+    const int qs = base_q + block_exclusive_scan4(make_int4(Q, 0, 0, 0), lds, tot).x;
+    const int qsum = tot.x;
+    int nvt = 0, nvu = 0, nmu = 0;
     if (i < a.num_seqs) {
-      // rows beyond the packed batch the host sized are dropped
-      Q = max(0, min(Q, a.total_q - qs));
+      Q = max(0, min(Q, a.total_q - qs));   // rows beyond the batch the host sized are dropped
       if (Q > 0 && Q * a.group >= a.min_rows) {
         nmu = (Q * a.group + kMfmaRows - 1) / kMfmaRows;
       } else {
@@ -58,12 +84,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         for (int t = 0; t < Q; ++t) nvu += parts_for(L - Q + t + 1, a.part);
       }
     }
-    const int vt0 = base_vt + block_exclusive_scan(nvt, lds, tot);
-    const int vtsum = tot;
-    const int vu0 = base_vu + block_exclusive_scan(nvu, lds, tot);
-    const int vusum = tot;
-    const int mu0 = base_mu + block_exclusive_scan(nmu, lds, tot);
-    const int musum = tot;
+    const int4 ex = block_exclusive_scan4(make_int4(nvt, nvu, nmu, 0), lds, tot);
+    const int vt0 = base_vt + ex.x, vu0 = base_vu + ex.y, mu0 = base_mu + ex.z;
     if (i < a.num_seqs) {
       SeqInfo si;
       si.kv_len = L;
@@ -92,11 +114,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
     }
     base_q += qsum;
-    base_vt += vtsum;
-    base_vu += vusum;
-    base_mu += musum;
+    base_vt += tot.x;
+    base_vu += tot.y;
+    base_mu += tot.z;
   }
-  __syncthreads();
   for (int k = base_vt + threadIdx.x; k < a.cap_vtok; k += kPlanThreads) {
     VTok vt;
     vt.seq = -1;
@@ -323,12 +344,18 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.part = P.part > 0 ? P.part : INT32_MAX / 2;
   a.scale_log2 = scale * kLog2e;
 
+  auto mark = [&](hipEvent_t ev) { return ev == nullptr || hipEventRecord(ev, stream) == hipSuccess; };
   if (P.n_vunit > 0) {
+    if (!mark(opts ? opts->vector_begin : nullptr)) return PA_ERR_HIP;
     if (launch_decode(a, desc->head_dim, g, i8, (int)P.n_vunit, stream) != hipSuccess) return PA_ERR_HIP;
-    if (P.max_parts > 1 && launch_reduce(a, desc->head_dim, (int)P.n_vtok, stream) != hipSuccess) return PA_ERR_HIP;
+    if (!mark(opts ? opts->vector_end : nullptr)) return PA_ERR_HIP;
+    if (P.max_parts > 1 && launch_reduce(a, desc->head_dim, g, (int)P.n_vtok, stream) != hipSuccess)
+      return PA_ERR_HIP;
   }
   if (P.n_munit > 0) {
+    if (!mark(opts ? opts->mfma_begin : nullptr)) return PA_ERR_HIP;
     if (launch_prefill(a, desc->head_dim, g, i8, (int)P.n_munit, stream) != hipSuccess) return PA_ERR_HIP;
+    if (!mark(opts ? opts->mfma_end : nullptr)) return PA_ERR_HIP;
   }
   return PA_OK;
 }

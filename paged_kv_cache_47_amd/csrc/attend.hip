@@ -16,8 +16,11 @@
 //    (query row, KV head, split-K partition); the G query heads of the KV head
 //    are processed together so every K/V element loaded from HBM serves all G
 //    rows.  K/V tiles arrive as 16-byte loads (one (block, head) tile is a
-//    contiguous 2-4 KB run); fp32 online softmax with a running max; partials
-//    of split rows are merged by `reduce_kernel` in log-sum-exp form.
+//    contiguous 2-4 KB run); fp32 online softmax with a running max.  Rows
+//    split over several partitions are merged in log-sum-exp form by
+//    `reduce_kernel` (a kernel boundary, not a device-scope fence: each XCD
+//    has its own L2, so a device-wide release/acquire inside the kernel would
+//    write back and invalidate whole caches).
 //  * MFMA path (prefill / chunked prefill, q_len * G >= 16 rows): 64 query
 //    rows per workgroup (4 waves x 16), 32 keys per step, S^T = K Q^T and
 //    O^T = V^T P^T on v_mfma_f32_16x16x32_f16.  Computing the transposes makes
@@ -39,6 +42,27 @@ __device__ __forceinline__ void i8x4_to_h2(uint32_t w, half2_t& lo, half2_t& hi)
 }
 
 // ============================================================ vector path ===
+#ifndef PA_DECODE_NW
+#define PA_DECODE_NW 4   // waves per workgroup
+#endif
+#ifndef PA_DECODE_PF
+#define PA_DECODE_PF 1   // tiles in flight ahead of the one being processed
+#endif
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1   // 1: K/V tile loads carry the nontemporal hint (each tile is read once)
+#endif
+constexpr int PF = PA_DECODE_PF;
+
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+#if PA_DECODE_NT
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+
 template <int D, int G, bool I8, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   constexpr int EB = I8 ? 1 : 2;       // bytes per element
@@ -91,116 +115,124 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 
   const int bend = (kend + kBlockSize - 1) / kBlockSize;
   int b = kbeg / kBlockSize + wave;
-  uint4 kr[NL], vr[NL];
-  int phys = 0;
   auto load_tile = [&](int blk, uint4* kd, uint4* vd, int& ph) {
     ph = clamp_block(tbl[blk], a.num_blocks);
     const int64_t off = ((int64_t)ph * a.hkv + h) * TILE;
     const uint4* kt = (const uint4*)((const char*)a.kc + off);
     const uint4* vt2 = (const uint4*)((const char*)a.vc + off);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) kd[i] = kt[i * 64 + lane];
+    for (int i = 0; i < NL; ++i) kd[i] = load16(kt + i * 64 + lane);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vd[i] = vt2[i * 64 + lane];
+    for (int i = 0; i < NL; ++i) vd[i] = load16(vt2 + i * 64 + lane);
   };
-  if (b < bend) load_tile(b, kr, vr, phys);
+  // Software pipeline: tiles for the next PF blocks of this wave are in flight
+  // while the current one is processed.
+  uint4 kbuf[PF + 1][NL], vbuf[PF + 1][NL];
+  int pbuf[PF + 1];
+#pragma unroll
+  for (int j = 0; j < PF; ++j)
+    if (b + j * NW < bend) load_tile(b + j * NW, kbuf[j], vbuf[j], pbuf[j]);
 
   while (b < bend) {
-    const int bn = b + NW;
-    uint4 kn[NL], vn[NL];
-    int physn = 0;
-    if (bn < bend) load_tile(bn, kn, vn, physn);
-
-    float ksc = a.scale_log2, vsc = 1.f;
-    if constexpr (I8) {
-      ksc *= (float)a.ks[(int64_t)phys * a.hkv + h];
-      vsc = (float)a.vs[(int64_t)phys * a.hkv + h];
-    }
-    const int tok0 = b * kBlockSize + grp;
-    if (b * kBlockSize + kBlockSize > kend) {  // last block of the range: drop V of keys past it
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-        if (tok0 + i * TPL >= kend) vr[i] = make_uint4(0, 0, 0, 0);
-    }
-
-    float s[NL][G];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      half2_t kh[E2];
-      const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+    if (b + PF * NW < bend) load_tile(b + PF * NW, kbuf[PF], vbuf[PF], pbuf[PF]);
+    {
+      uint4* kr = kbuf[0];
+      uint4* vr = vbuf[0];
+      const int phys = pbuf[0];
+      float ksc = a.scale_log2, vsc = 1.f;
       if constexpr (I8) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) i8x4_to_h2(w4[c], kh[2 * c], kh[2 * c + 1]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kh[c] = __builtin_bit_cast(half2_t, w4[c]);
+        ksc *= (float)a.ks[(int64_t)phys * a.hkv + h];
+        vsc = (float)a.vs[(int64_t)phys * a.hkv + h];
       }
+      const int tok0 = b * kBlockSize + grp;
+      if (b * kBlockSize + kBlockSize > kend) {  // last block of the range: drop V of keys past it
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float d = 0.f;
-#pragma unroll
-        for (int c = 0; c < E2; ++c) d = __builtin_amdgcn_fdot2(qh[g][c], kh[c], d, false);
-        d = group_sum<LPT>(d);
-        s[i][g] = (tok0 + i * TPL < kend) ? d * ksc : -__builtin_inff();
+        for (int i = 0; i < NL; ++i)
+          if (tok0 + i * TPL >= kend) vr[i] = make_uint4(0, 0, 0, 0);
       }
-    }
 
-    float vf[NL][E];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-      if constexpr (I8) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          half2_t lo, hi;
-          i8x4_to_h2(w4[c], lo, hi);
-          vf[i][4 * c + 0] = (float)lo.x * vsc;
-          vf[i][4 * c + 1] = (float)lo.y * vsc;
-          vf[i][4 * c + 2] = (float)hi.x * vsc;
-          vf[i][4 * c + 3] = (float)hi.y * vsc;
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const half2_t p2 = __builtin_bit_cast(half2_t, w4[c]);
-          vf[i][2 * c + 0] = (float)p2.x;
-          vf[i][2 * c + 1] = (float)p2.y;
-        }
-      }
-    }
-
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mb = s[0][g];
-#pragma unroll
-      for (int i = 1; i < NL; ++i) mb = fmaxf(mb, s[i][g]);
-      const float mn = fmaxf(m[g], mb);
-      const float alpha = fast_exp2(m[g] - mn);
-      m[g] = mn;
-      float p[NL];
-      float ps = 0.f;
+      float s[NL][G];
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        p[i] = fast_exp2(s[i][g] - mn);
-        ps += p[i];
-      }
-      l[g] = l[g] * alpha + ps;
+        half2_t kh[E2];
+        const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+        if constexpr (I8) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float x = acc[g][e] * alpha;
+          for (int c = 0; c < 4; ++c) i8x4_to_h2(w4[c], kh[2 * c], kh[2 * c + 1]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < NL; ++i) x = fmaf(p[i], vf[i][e], x);
-        acc[g][e] = x;
+          for (int c = 0; c < 4; ++c) kh[c] = __builtin_bit_cast(half2_t, w4[c]);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d = 0.f;
+#pragma unroll
+          for (int c = 0; c < E2; ++c) d = __builtin_amdgcn_fdot2(qh[g][c], kh[c], d, false);
+          d = group_sum<LPT>(d);
+          s[i][g] = (tok0 + i * TPL < kend) ? d * ksc : -__builtin_inff();
+        }
       }
-    }
 
-    b = bn;
-    phys = physn;
+      float vf[NL][E];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      kr[i] = kn[i];
-      vr[i] = vn[i];
+      for (int i = 0; i < NL; ++i) {
+        const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+        if constexpr (I8) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            half2_t lo, hi;
+            i8x4_to_h2(w4[c], lo, hi);
+            vf[i][4 * c + 0] = (float)lo.x * vsc;
+            vf[i][4 * c + 1] = (float)lo.y * vsc;
+            vf[i][4 * c + 2] = (float)hi.x * vsc;
+            vf[i][4 * c + 3] = (float)hi.y * vsc;
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const half2_t p2 = __builtin_bit_cast(half2_t, w4[c]);
+            vf[i][2 * c + 0] = (float)p2.x;
+            vf[i][2 * c + 1] = (float)p2.y;
+          }
+        }
+      }
+
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mb = s[0][g];
+#pragma unroll
+        for (int i = 1; i < NL; ++i) mb = fmaxf(mb, s[i][g]);
+        const float mn = fmaxf(m[g], mb);
+        const float alpha = fast_exp2(m[g] - mn);
+        m[g] = mn;
+        float p[NL];
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          p[i] = fast_exp2(s[i][g] - mn);
+          ps += p[i];
+        }
+        l[g] = l[g] * alpha + ps;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float x = acc[g][e] * alpha;
+#pragma unroll
+          for (int i = 0; i < NL; ++i) x = fmaf(p[i], vf[i][e], x);
+          acc[g][e] = x;
+        }
+      }
+
     }
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      pbuf[j] = pbuf[j + 1];
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        kbuf[j][i] = kbuf[j + 1][i];
+        vbuf[j][i] = vbuf[j + 1][i];
+      }
+    }
+    b += NW;
   }
 
   // merge the TPL token-row streams of this wave (lane groups), then the waves
@@ -253,25 +285,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split-K partials of one query row (all heads): base-2 log-sum-exp.
-template <int D>
+// Merge the split-K partials of one (query row, KV head): its G query heads,
+// base-2 log-sum-exp: out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M).
+template <int D, int G>
 __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const VTok vt = a.vtok[blockIdx.x];
   if (vt.seq < 0 || vt.parts <= 1) return;
+  const int h = blockIdx.y;
   const SeqInfo si = a.seqs[vt.seq];
-  const int64_t row = (int64_t)si.q_start + vt.t;
-  for (int idx = threadIdx.x; idx < a.hq * D; idx += 256) {
-    const int hq = idx / D, d = idx % D;
+  const int64_t row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int g = idx / D, d = idx % D;
+    const int64_t col = (int64_t)h * G + g;
     float M = -__builtin_inff();
-    for (int p = 0; p < vt.parts; ++p) M = fmaxf(M, a.plse[(int64_t)(vt.u0 + p) * a.hq + hq]);
+    for (int p = 0; p < vt.parts; ++p) M = fmaxf(M, a.plse[(int64_t)(vt.u0 + p) * a.hq + col]);
     float S = 0.f, O = 0.f;
     for (int p = 0; p < vt.parts; ++p) {
-      const int64_t pr = (int64_t)(vt.u0 + p) * a.hq + hq;
-      const float w = fast_exp2(a.plse[pr] - M);
-      S += w;
-      O = fmaf(w, a.po[pr * D + d], O);
+      const int64_t pr = (int64_t)(vt.u0 + p) * a.hq + col;
+      const float wgt = fast_exp2(a.plse[pr] - M);
+      S += wgt;
+      O = fmaf(wgt, a.po[pr * D + d], O);
     }
-    a.out[(row * a.hq + hq) * D + d] = (half_t)(O / S);
+    a.out[(row0 + g) * D + d] = (half_t)(O / S);
   }
 }
 
@@ -440,10 +475,10 @@ template <int D, bool I8>
 static hipError_t decode_g(const AttnArgs& a, int g, int n, hipStream_t s) {
   dim3 grid(n, a.hkv);
   switch (g) {
-    case 1: decode_kernel<D, 1, I8, 4><<<grid, 256, 0, s>>>(a); break;
-    case 2: decode_kernel<D, 2, I8, 4><<<grid, 256, 0, s>>>(a); break;
-    case 4: decode_kernel<D, 4, I8, 4><<<grid, 256, 0, s>>>(a); break;
-    case 8: decode_kernel<D, 8, I8, 4><<<grid, 256, 0, s>>>(a); break;
+    case 1: decode_kernel<D, 1, I8, PA_DECODE_NW><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 2: decode_kernel<D, 2, I8, PA_DECODE_NW><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 4: decode_kernel<D, 4, I8, PA_DECODE_NW><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 8: decode_kernel<D, 8, I8, PA_DECODE_NW><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -454,10 +489,21 @@ hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, bool i8, in
   return i8 ? decode_g<64, true>(a, group, n, s) : decode_g<64, false>(a, group, n, s);
 }
 
-hipError_t launch_reduce(const AttnArgs& a, int head_dim, int n_vtok, hipStream_t s) {
-  if (head_dim == 128) reduce_kernel<128><<<n_vtok, 256, 0, s>>>(a);
-  else reduce_kernel<64><<<n_vtok, 256, 0, s>>>(a);
+template <int D>
+static hipError_t reduce_g(const AttnArgs& a, int g, int n, hipStream_t s) {
+  dim3 grid(n, a.hkv);
+  switch (g) {
+    case 1: reduce_kernel<D, 1><<<grid, 256, 0, s>>>(a); break;
+    case 2: reduce_kernel<D, 2><<<grid, 256, 0, s>>>(a); break;
+    case 4: reduce_kernel<D, 4><<<grid, 256, 0, s>>>(a); break;
+    case 8: reduce_kernel<D, 8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_reduce(const AttnArgs& a, int head_dim, int group, int n_vtok, hipStream_t s) {
+  return head_dim == 128 ? reduce_g<128>(a, group, n_vtok, s) : reduce_g<64>(a, group, n_vtok, s);
 }
 
 template <int D, bool I8>
