@@ -8,5 +8,5 @@ inputs from here and each builds everything else on its own.
 """
 from .configs import (  # noqa: F401
     Workload, StepDraw, normal_f16, config1, config2, config3, config4, config5,
-    CONFIGS,
+    CONFIGS, custom,
 )

@@ -310,3 +310,37 @@ def config5(seed: int = 47005, num_chunks: int = 8, chunk_q: int = 512, max_chun
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def custom(seed: int, kv_lens, q_lens, num_q_heads: int = 8, num_kv_heads: int = 2, head_dim: int = 128,
+           kv_dtype: str = "f16", extra_blocks: int = 3, permute: bool = True) -> Workload:
+    """A one-step workload with explicit post-write lengths ``kv_lens`` and
+    query rows ``q_lens`` (the cached context is kv_len - q_len tokens).  For
+    int8 pools the cached context is drawn as N(0,1) fp16 and written token
+    by token before the step; fp16 pools hold N(0,1) everywhere."""
+    hq, hkv, d = num_q_heads, num_kv_heads, head_dim
+    post = np.asarray(kv_lens, np.int64)
+    ql = np.asarray(q_lens, np.int64)
+    ctx = post - ql
+    nb = int(np.sum(_ceil_div(post, BLOCK_SIZE))) + extra_blocks
+    rng = np.random.default_rng([seed, S_META])
+    perm = rng.permutation(nb) if permute else None
+    if kv_dtype == "i8":
+        draws = {
+            "k": lambda: uniform_i8((seed, S_POOL_K), (nb, hkv, BLOCK_SIZE, d)),
+            "v": lambda: uniform_i8((seed, S_POOL_V), (nb, hkv, BLOCK_SIZE, d)),
+            "k_scale": lambda: uniform_scale_f16((seed, S_KSCALE), (nb, hkv)),
+            "v_scale": lambda: uniform_scale_f16((seed, S_VSCALE), (nb, hkv)),
+        }
+
+        def context(i):
+            n = int(ctx[i])
+            return (normal_f16((seed, S_CTX_K, i), (n, hkv, d)), normal_f16((seed, S_CTX_V, i), (n, hkv, d)))
+    else:
+        draws = _f16_pool(seed, nb, hkv, d)
+        context = None
+    return Workload(
+        name=f"custom-{seed}", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=BLOCK_SIZE,
+        kv_dtype=kv_dtype, scale=1.0 / math.sqrt(d), num_blocks=nb, first_pops=perm, ctx_lens=ctx,
+        pool_draws=draws, steps=[_step(seed, (0,), ql, hq, hkv, d)], context=context,
+    )
