@@ -1,20 +1,26 @@
-"""Benchmark: paged GQA decode on one MI355X.
+"""Benchmark: paged attention steps on one MI355X.
 
-Workload (the one the headline metric is quoted on): 256 sequences, 32 query
-/ 8 KV heads, head_dim 128, 16-token blocks, fp16 KV pool sized to the
-blocks needed plus 10% with a seeded permutation of block ids, KV lengths
-U[1, 4096] (seed 47003), one new token per sequence.
+Default workload (the one the headline metric is quoted on): GQA decode,
+256 sequences, 32 query / 8 KV heads, head_dim 128, 16-token blocks, fp16
+KV pool sized to the blocks needed plus 10% with a seeded permutation of
+block ids, KV lengths U[1, 4096] (seed 47003), one new token per sequence.
+``--workload N`` times one of the other synthetic workloads instead (1 tiny
+MHA decode, 2 GPT-2-shaped batch: a decode step after the prefill, 4 shared
+prefix + beam copy-on-write, 5 packed int8 chunked prefill + decode).
 
-One step = the whole hot path over that batch with its metadata already in
-HBM: ``pa_write_kv`` of the 256 new K/V rows through the slot mapping, then
-``pa_attend`` (plan kernel, split-K vector attention kernel, log-sum-exp
-reduce).  W warmup steps, then K timed steps between two synchronisations.
+One step = the whole hot path over one batch with its inputs already in HBM:
+``pa_copy_blocks`` (copy-on-write pairs, if any), ``pa_write_kv`` of the
+step's new K/V rows through the slot mapping, then ``pa_attend`` (plan
+kernel, split-K vector attention kernel and its log-sum-exp reduce, MFMA
+attention kernel).  W warmup steps, then K timed steps between two
+synchronisations; each timed step also records fence-free HIP events around
+the attention kernels (the roofline); K more steps without those events
+follow, reported separately.
 
-Printed (one JSON line): KV-read throughput of the step in GB/s (algorithmic
-bytes: sum over sequences of kv_len * kv_heads * head_dim * 2 (K and V) * 2
-bytes), seq-steps/s, the roofline of the dominant kernel (the split-K
-attention kernel, timed with HIP events the library records around it on
-the same stream) and the CPU oracle timed on a bounded sample.
+Printed: one JSON line.  ``value`` is the KV-read throughput of the step in
+GB/s: algorithmic bytes = sum over sequences of kv_len * kv_heads *
+head_dim * 2 (K and V) * element bytes (+ one fp16 scale per (block, head)
+per pool for int8) over the step time.
 """
 from __future__ import annotations
 
@@ -31,8 +37,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-DOMINANT = "decode_kernel"
+PEAK_MFMA_F16_TFLOPS = 2500.0
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_gqa-decode-256_pmc.json")
+
+WORKLOADS = {
+    1: "tiny-mha-decode: 4 seqs (kv_len 40/20/16/30), 12/12 heads, head_dim 64, 8-block fp16 pool",
+    2: "gpt2-batch decode step: 32 seqs after prefill of U[32,512] prompts, 12/12 heads, head_dim 64, fp16",
+    3: "gqa-decode: 256 seqs, kv_len U[1,4096] (seed 47003), 32 q / 8 kv heads, head_dim 128, block 16, "
+       "fp16 KV, 1 new token per seq (write + attend)",
+    4: "prefix-share-beam-cow: 112 seqs over a shared 1024-token prefix, 16 requests x 4 beams, "
+       "copy-on-write + write + attend, 32/8 heads, head_dim 128, fp16",
+    5: "packed-int8: 8 chunks x 512 rows (context U[0,8192]) + 192 decode seqs (kv_len U[1,32768]), "
+       "32/8 heads, head_dim 128, int8 KV with per-block-per-head fp16 scales",
+}
 
 
 class TimingEvents:
@@ -55,6 +72,11 @@ class TimingEvents:
     def handle(self, i: int) -> int:
         return self.ev[i].value
 
+    def record_all(self, stream: int) -> None:
+        for e in self.ev:
+            if self.hip.hipEventRecord(e, self._ct.c_void_p(stream)) != 0:
+                raise RuntimeError("hipEventRecord failed")
+
     def elapsed_ms(self, i: int, j: int) -> float:
         ms = self._ct.c_float()
         if self.hip.hipEventElapsedTime(self._ct.byref(ms), self.ev[i], self.ev[j]) != 0:
@@ -71,9 +93,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(n_launch_units: float):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
-    when it is missing or was taken on other kernel sources."""
+def traffic_from_profile():
+    """HBM bytes per launch of the default workload's attention kernel from
+    the committed rocprofv3 PMC summary, or None when it is missing or was
+    taken on other kernel sources."""
     try:
         with open(PMC_FILE) as f:
             p = json.load(f)
@@ -84,34 +107,60 @@ def traffic_from_profile(n_launch_units: float):
     return p.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float):
+def work_split(w, L, Q):
+    """Algorithmic work of one step: (vector-path KV bytes, MFMA-path flops,
+    total KV bytes).  Rows with q_len * group >= 16 go to the MFMA path."""
+    eb = 1 if w.kv_dtype == "i8" else 2
+    per_tok = w.num_kv_heads * w.head_dim * 2 * eb
+    vec_bytes, mfma_flops, total = 0, 0, 0
+    for l, q in zip(L.tolist(), Q.tolist()):
+        kv = l * per_tok
+        if w.kv_dtype == "i8":
+            kv += -(-l // w.block_size) * w.num_kv_heads * 2 * 2
+        total += kv
+        if q == 0:
+            continue
+        if q * w.group >= 16:
+            vis = sum(l - q + t + 1 for t in range(q))
+            mfma_flops += 4 * w.head_dim * w.num_q_heads * vis
+        else:
+            vec_bytes += kv * q
+    return vec_bytes, mfma_flops, total
+
+
+def cpu_baseline(w, step: int, budget_s: float):
     """The oracle (gather through the block table + fp64 attention) on the
-    first sequences of the same workload, until ``budget_s`` of CPU time."""
+    first sequences of the same step, until ``budget_s`` of CPU time."""
     import oracle.attention as oatt
     import oracle.paging as opg
     st = opg.build_state(w)
-    slots, _ = opg.apply_step(st, w.step(0).q_lens)
-    q = w.step(0).q
+    for s in range(step + 1):
+        opg.apply_step(st, w.step(s).q_lens)
+    sd = w.step(step)
     K, V = w.pool_k, w.pool_v
     bs = w.block_size
+    eb = 1 if w.kv_dtype == "i8" else 2
+    starts = np.concatenate([[0], np.cumsum(sd.q_lens)[:-1]])
     t0 = time.perf_counter()
     done, kv_bytes = 0, 0
     for i in range(len(st.tables)):
-        L = st.lens[i]
-        Kc = oatt.gather(K, st.tables[i], L, bs)
-        Vc = oatt.gather(V, st.tables[i], L, bs)
-        oatt.attend(q[i:i + 1], oatt.query_positions(L, 1), Kc, Vc, w.scale)
+        L, Q = st.lens[i], int(sd.q_lens[i])
+        Kc = oatt.gather(K, st.tables[i], L, bs, w.pool_k_scale)
+        Vc = oatt.gather(V, st.tables[i], L, bs, w.pool_v_scale)
+        if Q:
+            oatt.attend(sd.q[starts[i]:starts[i] + Q], oatt.query_positions(L, Q), Kc, Vc, w.scale)
         done += 1
-        kv_bytes += L * w.num_kv_heads * w.head_dim * 2 * 2
+        kv_bytes += L * w.num_kv_heads * w.head_dim * 2 * eb
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    cores = len(os.sched_getaffinity(0))
     return {
-        "value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-        "sample": f"first {done} of {len(st.tables)} sequences ({kv_bytes / 1e6:.1f} MB of KV), "
-                  f"attention only (numpy fp64, BLAS threads={os.environ.get('OMP_NUM_THREADS', 'default')}), "
-                  f"{dt:.1f} s",
+        "value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"first {done} of {len(st.tables)} sequences ({kv_bytes / 1e6:.1f} MB of KV), attention only "
+                  f"(numpy fp64, BLAS threads={os.environ.get('OMP_NUM_THREADS', 'default')}), {dt:.1f} s"
+                  + (" (on the pool as drawn: the int8 context replay is not part of the timed oracle work)"
+                     if w.kv_dtype == "i8" else ""),
         "seq_steps_per_s": round(done / dt, 3),
     }
 
@@ -121,6 +170,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition-tokens", type=int, default=0)
@@ -138,26 +188,33 @@ def main(argv=None) -> int:
     from paged_kv_cache_47_amd.workload import DeviceRun
 
     torch.cuda.set_device(0)
-    w = synthetic.config3()
+    w = synthetic.CONFIGS[args.workload]()
     run = DeviceRun(w)
-    x = run.prepare(0)
+    step_index = 0
+    if args.workload == 2:            # prefill (step 0) first; the timed step is the first decode step
+        x0 = run.prepare(0)
+        run.run(x0)
+        step_index = 1
+    x = run.prepare(step_index)
     S = len(run.ids)
     L = x.batch.seq_lens.astype(np.int64)
-    kv_bytes = int(L.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    Q = x.batch.q_lens.astype(np.int64)
+    vec_bytes, mfma_flops, kv_bytes = work_split(w, L, Q)
     out = torch.empty_like(x.q)
     need = pa.pa_attend_workspace_bytes(run.k_cache, w.num_q_heads, x.batch.seq_lens, x.batch.q_lens,
                                         partition_tokens=args.partition_tokens)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     n = args.warmup + args.steps
-    evs = TimingEvents(2 * n)
+    evs = TimingEvents(4 * n)
+    evs.record_all(torch.cuda.current_stream().cuda_stream)   # first records are slow: do them untimed
     torch.cuda.synchronize()
 
     def step(i, timed_kernel=True):
         run.write(x)
-        ev = (evs.handle(2 * i), evs.handle(2 * i + 1), None, None) if timed_kernel else None
+        ev = tuple(evs.handle(4 * i + j) for j in range(4)) if timed_kernel else None
         pa.pa_attend(x.q, run.k_cache, run.v_cache, x.block_tables, x.seq_lens, x.q_lens, x.batch.seq_lens,
-                     x.batch.q_lens, w.scale, out=out, workspace=ws, partition_tokens=args.partition_tokens,
-                     events=ev)
+                     x.batch.q_lens, w.scale, out=out, workspace=ws, k_scale=run.k_scale, v_scale=run.v_scale,
+                     partition_tokens=args.partition_tokens, events=ev)
 
     def timed(steps, timed_kernel):
         torch.cuda.synchronize()
@@ -172,22 +229,33 @@ def main(argv=None) -> int:
 
     for i in range(args.warmup):
         step(i)
-    # the timed region: every step also records events around the attention kernel
-    ms = timed(range(args.warmup, n), True)
-    # the same steps without those events
-    ms_plain = timed(range(args.warmup, n), False)
+    ms = timed(range(args.warmup, n), True)          # the timed region
+    ms_plain = timed(range(args.warmup, n), False)   # the same steps without the kernel events
     if args.copy_calibration_mib:
-        # a plain device copy of known size, for scaling rocprofv3 byte counters
         nbytes = args.copy_calibration_mib << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    k_ms = [evs.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.warmup, n)]
-    k_avg = float(np.mean(k_ms))
-    achieved = kv_bytes / (k_avg * 1e-3) / 1e9
-    traffic = traffic_from_profile(1)
+
+    roof = []
+    if vec_bytes:
+        k_ms = float(np.mean([evs.elapsed_ms(4 * i, 4 * i + 1) for i in range(args.warmup, n)]))
+        ach = vec_bytes / (k_ms * 1e-3) / 1e9
+        roof.append({"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profile() if args.workload == 3 and not args.partition_tokens else None,
+                     "kernel": "decode_kernel (split-K vector path)", "kernel_ms": round(k_ms, 5),
+                     "algorithmic_bytes_per_launch": vec_bytes})
+    if mfma_flops:
+        k_ms = float(np.mean([evs.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(args.warmup, n)]))
+        ach = mfma_flops / (k_ms * 1e-3) / 1e12
+        roof.append({"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel (MFMA path, fp16 16x16x32)", "kernel_ms": round(k_ms, 5),
+                     "algorithmic_flops_per_launch": mfma_flops})
+    roof.sort(key=lambda r: -r["kernel_ms"])       # the dominant kernel first
     res = {
         "metric": "paged decode attn: achieved KV-read HBM GB/s (% of peak); seq-steps/s",
         "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
@@ -199,24 +267,22 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "i8" if w.kv_dtype == "i8" else "f16",
         "data": "synthetic",
-        "config": {"workload": "gqa-decode: 256 seqs, kv_len U[1,4096] (seed 47003), 32 q / 8 kv heads, "
-                               "head_dim 128, block 16, fp16 KV, 1 new token per seq (write + attend)",
-                   "num_seqs": S, "kv_tokens": int(L.sum()), "num_blocks": w.num_blocks,
+        "config": {"workload": WORKLOADS[args.workload], "num_seqs": S, "kv_tokens": int(L.sum()),
+                   "query_rows": int(Q.sum()), "num_blocks": w.num_blocks,
                    "partition_tokens": args.partition_tokens},
         "pct_of_peak": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "seq_steps_per_s": round(S / (ms * 1e-3), 1),
         "ms_per_step_without_kernel_events": round(ms_plain, 5),
         "value_without_kernel_events": round(kv_bytes / (ms_plain * 1e-3) / 1e9, 2),
         "kv_bytes_per_step": kv_bytes,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": DOMINANT, "kernel_ms": round(k_avg, 5),
-                     "algorithmic_bytes_per_launch": kv_bytes},
+        "roofline": roof[0] if roof else None,
     }
+    if len(roof) > 1:
+        res["roofline_other"] = roof[1:]
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(w, step_index, args.cpu_budget)
     print(json.dumps(res), flush=True)
     return 0
 
