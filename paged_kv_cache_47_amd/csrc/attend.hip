@@ -21,8 +21,8 @@
 //    `reduce_kernel` (a kernel boundary, not a device-scope fence: each XCD
 //    has its own L2, so a device-wide release/acquire inside the kernel would
 //    write back and invalidate whole caches).
-//  * MFMA path (prefill / chunked prefill, q_len * G >= 16 rows): 64 query
-//    rows per workgroup (4 waves x 16), 32 keys per step, S^T = K Q^T and
+//  * MFMA path (prefill / chunked prefill, q_len * G >= 16 rows): 128 query
+//    rows per workgroup (4 waves x 32), 64 keys per step, S^T = K Q^T and
 //    O^T = V^T P^T on v_mfma_f32_16x16x32_f16.  Computing the transposes makes
 //    each lane own one query row in both accumulators, and the P accumulator
 //    already sits in the B-operand layout of the second product.  V is staged
@@ -40,6 +40,36 @@ __device__ __forceinline__ void i8x4_to_h2(uint32_t w, half2_t& lo, half2_t& hi)
   lo = __builtin_bit_cast(half2_t, l) - bias;
   hi = __builtin_bit_cast(half2_t, h) - bias;
 }
+
+// V of two token rows (same dims) -> (row0, row1) fp16 pairs per dim, the
+// operand layout of v_dot2 over tokens.  fp16: one byte permute per pair.
+// int8: interleave the two rows' codes, then the 0x64XX fp16 trick.
+template <bool I8>
+__device__ __forceinline__ void v_token_pairs(const uint4& r0, const uint4& r1, half2_t* vp) {
+  const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w};
+  const uint32_t b[4] = {r1.x, r1.y, r1.z, r1.w};
+  if constexpr (I8) {
+    const half2_t bias = {(half_t)1152.0f, (half_t)1152.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t x = a[c] ^ 0x80808080u, y = b[c] ^ 0x80808080u;
+      const uint32_t t01 = __builtin_amdgcn_perm(y, x, 0x05010400u);  // x.b0 y.b0 x.b1 y.b1
+      const uint32_t t23 = __builtin_amdgcn_perm(y, x, 0x07030602u);  // x.b2 y.b2 x.b3 y.b3
+      vp[4 * c + 0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, t01, 0x04010400u)) - bias;
+      vp[4 * c + 1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, t01, 0x04030402u)) - bias;
+      vp[4 * c + 2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, t23, 0x04010400u)) - bias;
+      vp[4 * c + 3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, t23, 0x04030402u)) - bias;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      vp[2 * c + 0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b[c], a[c], 0x05040100u));
+      vp[2 * c + 1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b[c], a[c], 0x07060302u));
+    }
+  }
+}
+
+constexpr float kRescale = 8.0f;
 
 // ============================================================ vector path ===
 #ifndef PA_DECODE_NW
@@ -145,12 +175,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
         vsc = (float)a.vs[(int64_t)phys * a.hkv + h];
       }
       const int tok0 = b * kBlockSize + grp;
-      if (b * kBlockSize + kBlockSize > kend) {  // last block of the range: drop V of keys past it
+      const bool tail = b * kBlockSize + kBlockSize > kend;  // wave-uniform: last block of the range
+      if (tail) {  // drop V of keys past the range (their slots may hold anything)
 #pragma unroll
         for (int i = 0; i < NL; ++i)
           if (tok0 + i * TPL >= kend) vr[i] = make_uint4(0, 0, 0, 0);
       }
 
+      // scores of this lane group's NL tokens for the G rows (base 2)
       float s[NL][G];
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
@@ -168,60 +200,85 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
           float d = 0.f;
 #pragma unroll
           for (int c = 0; c < E2; ++c) d = __builtin_amdgcn_fdot2(qh[g][c], kh[c], d, false);
-          d = group_sum<LPT>(d);
-          s[i][g] = (tok0 + i * TPL < kend) ? d * ksc : -__builtin_inff();
+          s[i][g] = group_sum<LPT>(d) * ksc;
         }
       }
-
-      float vf[NL][E];
+      if (tail) {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const uint32_t w4[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-        if constexpr (I8) {
+        for (int i = 0; i < NL; ++i)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            half2_t lo, hi;
-            i8x4_to_h2(w4[c], lo, hi);
-            vf[i][4 * c + 0] = (float)lo.x * vsc;
-            vf[i][4 * c + 1] = (float)lo.y * vsc;
-            vf[i][4 * c + 2] = (float)hi.x * vsc;
-            vf[i][4 * c + 3] = (float)hi.y * vsc;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const half2_t p2 = __builtin_bit_cast(half2_t, w4[c]);
-            vf[i][2 * c + 0] = (float)p2.x;
-            vf[i][2 * c + 1] = (float)p2.y;
-          }
-        }
+          for (int g = 0; g < G; ++g)
+            if (tok0 + i * TPL >= kend) s[i][g] = -__builtin_inff();
       }
 
+      // The running max moves only when a score exceeds it by more than
+      // kRescale (log2 units), so weights stay <= 2^kRescale and the
+      // accumulators are rescaled rarely.
+      bool grow = false;
+      float mb[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float mb = s[0][g];
+        mb[g] = s[0][g];
 #pragma unroll
-        for (int i = 1; i < NL; ++i) mb = fmaxf(mb, s[i][g]);
-        const float mn = fmaxf(m[g], mb);
-        const float alpha = fast_exp2(m[g] - mn);
-        m[g] = mn;
-        float p[NL];
-        float ps = 0.f;
+        for (int i = 1; i < NL; ++i) mb[g] = fmaxf(mb[g], s[i][g]);
+        grow |= mb[g] > m[g] + kRescale;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          p[i] = fast_exp2(s[i][g] - mn);
-          ps += p[i];
-        }
-        l[g] = l[g] * alpha + ps;
+        for (int g = 0; g < G; ++g) {
+          if (mb[g] > m[g] + kRescale) {
+            const float al = fast_exp2(m[g] - mb[g]);
+            m[g] = mb[g];
+            l[g] *= al;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          float x = acc[g][e] * alpha;
-#pragma unroll
-          for (int i = 0; i < NL; ++i) x = fmaf(p[i], vf[i][e], x);
-          acc[g][e] = x;
+            for (int e = 0; e < E; ++e) acc[g][e] *= al;
+          }
         }
       }
 
+      if constexpr (NL >= 2) {
+        // P.V on v_dot2_f32_f16 over token pairs: vp[e] = (V[tok 2j][e], V[tok 2j+1][e])
+#pragma unroll
+        for (int j = 0; j < NL / 2; ++j) {
+          half2_t vp[E];
+          v_token_pairs<I8>(vr[2 * j], vr[2 * j + 1], vp);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float p0 = fast_exp2(s[2 * j][g] - m[g]), p1 = fast_exp2(s[2 * j + 1][g] - m[g]);
+            half2_t pp;
+            if constexpr (I8) {
+              l[g] += p0 + p1;
+              pp = (half2_t){(half_t)(p0 * vsc), (half_t)(p1 * vsc)};
+            } else {
+              pp = (half2_t){(half_t)p0, (half_t)p1};
+              // sum the rounded weights the product uses, so the output stays a convex combination
+              l[g] = __builtin_amdgcn_fdot2(pp, (half2_t){(half_t)1.f, (half_t)1.f}, l[g], false);
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[g][e] = __builtin_amdgcn_fdot2(pp, vp[e], acc[g][e], false);
+          }
+        }
+      } else {
+        // one token row per lane per block (int8, head_dim 64)
+        float vf[E];
+        const uint32_t w4[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          half2_t lo, hi;
+          i8x4_to_h2(w4[c], lo, hi);
+          vf[4 * c + 0] = (float)lo.x * vsc;
+          vf[4 * c + 1] = (float)lo.y * vsc;
+          vf[4 * c + 2] = (float)hi.x * vsc;
+          vf[4 * c + 3] = (float)hi.y * vsc;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p0 = fast_exp2(s[0][g] - m[g]);
+          l[g] += p0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p0, vf[e], acc[g][e]);
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
@@ -311,161 +368,228 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
 }
 
 // ============================================================== MFMA path ===
-template <int D, int G, bool I8>
-__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
-  constexpr int KS = D / 32;   // k-steps of 32 over the head dim
-  constexpr int NT = D / 16;   // 16-wide output column tiles
-  constexpr int BN = 32;       // keys per step (two blocks)
-  constexpr int LDV = D + 8;   // LDS row stride of the V tile, in halves
-  __shared__ __attribute__((aligned(16))) half_t vlds[BN * LDV];
+// One workgroup = 4 waves = 128 query rows of one (sequence, KV head); each
+// wave owns 32 rows as two 16-row MFMA blocks, so every K or V operand read
+// from LDS feeds two MFMAs.  Keys advance 64 at a time (four 16-key blocks):
+// the next 64-key K and V tiles are loaded from HBM into registers while the
+// current tiles in LDS are used, then written to the other LDS buffer; one
+// barrier per step.
+constexpr int kMfmaWaves = 4;
+constexpr int kMfmaBN = 64;
 
-  const int u = blockIdx.x, h = blockIdx.y;
-  const int2 mu = a.munit[u];
+template <int D, int G, bool I8>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;        // k-steps of 32 over the head dim
+  constexpr int NT = D / 16;        // 16-wide output column tiles
+  constexpr int BN = kMfmaBN;       // keys per step
+  constexpr int KB = BN / 16;       // 16-key blocks per step
+  constexpr int RB = 2;             // 16-row MFMA blocks per wave
+  constexpr int LD = D + 8;         // LDS row stride (halves)
+  constexpr int EB = I8 ? 1 : 2;
+  constexpr int CPR = D * EB / 16;  // 16-byte chunks per key row in the pool
+  constexpr int PT = BN * CPR / 256;  // chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) half_t lds[2][2][BN * LD];  // [buffer][K, V]
+
+  const int id = blockIdx.x;
+  const int h = id % a.hkv;         // consecutive workgroups = consecutive KV heads (one XCD each when hkv = 8)
+  const int2 mu = a.munit[id / a.hkv];
   if (mu.x < 0) return;
   const SeqInfo si = a.seqs[mu.x];
   const int L = si.kv_len, Q = si.q_len, rows = Q * G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int r0 = mu.y * kMfmaRows;
-  const int myrow = r0 + wave * 16 + l16;
-  const bool rvalid = myrow < rows;
-  const int tq = rvalid ? myrow / G : 0;
-  const int gq = myrow % G;
-  const int qpos = rvalid ? L - Q + tq : -1;
   const int last_row = min(rows, r0 + kMfmaRows) - 1;
   const int kmax = min(L, L - Q + last_row / G + 1);
   const int32_t* tbl = a.block_tables + (int64_t)mu.x * a.max_blocks;
-  const int64_t orow = ((int64_t)(si.q_start + tq) * a.hq + (int64_t)h * G + gq) * D;
 
-  half8_t qop[KS];
+  int qpos[RB];
+  int64_t orow[RB];
+  bool rvalid[RB];
+  half8_t qop[RB][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (rvalid) qop[ks] = *(const half8_t*)(a.q + orow + ks * 32 + 8 * grp);
-    else qop[ks] = (half8_t)(half_t)0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = r0 + wave * 32 + rb * 16 + l16;
+    rvalid[rb] = row < rows;
+    const int tq = rvalid[rb] ? row / G : 0;
+    qpos[rb] = rvalid[rb] ? L - Q + tq : -1;
+    orow[rb] = ((int64_t)(si.q_start + tq) * a.hq + (int64_t)h * G + row % G) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[rb][ks] = rvalid[rb] ? *(const half8_t*)(a.q + orow[rb] + ks * 32 + 8 * grp) : (half8_t)(half_t)0.f;
   }
 
-  float4_t o[NT];
+  float4_t o[RB][NT];
+  float m[RB], lsum[RB];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] = (float4_t)0.f;
-  float m = kNegBig, lsum = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegBig;
+    lsum[rb] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[rb][nt] = (float4_t)0.f;
+  }
 
-  for (int kt = 0; kt < kmax; kt += BN) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < BN * D / 8; c += 256) {
-      const int key = c / (D / 8), dc = c % (D / 8);
+  uint4 stk[PT], stv[PT];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int key = c / CPR, ch = c % CPR;
       const int kg = kt + key;
-      half8_t val = (half8_t)(half_t)0.f;
       if (kg < L) {
         const int ph = clamp_block(tbl[kg / kBlockSize], a.num_blocks);
-        const int64_t base = (((int64_t)ph * a.hkv + h) * kBlockSize + (kg % kBlockSize)) * D + dc * 8;
-        if constexpr (I8) {
-          const uint2 w = *(const uint2*)((const int8_t*)a.vc + base);
-          half2_t h0, h1, h2, h3;
-          i8x4_to_h2(w.x, h0, h1);
-          i8x4_to_h2(w.y, h2, h3);
-          val = (half8_t){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
-        } else {
-          val = *(const half8_t*)((const half_t*)a.vc + base);
-        }
+        const int64_t off = ((((int64_t)ph * a.hkv + h) * kBlockSize + (kg % kBlockSize)) * D) * EB + ch * 16;
+        stk[i] = *(const uint4*)((const char*)a.kc + off);
+        stv[i] = *(const uint4*)((const char*)a.vc + off);
+      } else {
+        stk[i] = make_uint4(0, 0, 0, 0);
+        stv[i] = make_uint4(0, 0, 0, 0);
       }
-      *(half8_t*)(vlds + key * LDV + dc * 8) = val;
     }
-    __syncthreads();
-
-    // Both 16-key blocks of the step always run their MFMAs: when the second
-    // block lies past the last key it re-reads the first block (always a valid
-    // table entry) and its scores are masked below.  Keeping MFMAs out of
-    // conditional code also keeps every MFMA-result read in straight-line code.
-    float4_t sacc[2];
-    float kscl[2] = {1.f, 1.f}, vscl[2] = {1.f, 1.f};
-    const int kb0 = kt / kBlockSize;
-    const int kb1 = (kb0 + 1) * kBlockSize < kmax ? kb0 + 1 : kb0;
+  };
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = (float4_t)0.f;
-      const int ph = clamp_block(tbl[kb == 0 ? kb0 : kb1], a.num_blocks);
-      const int64_t base = (((int64_t)ph * a.hkv + h) * kBlockSize + l16) * D + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        half8_t kop;
-        if constexpr (I8) {
-          const uint2 w = *(const uint2*)((const int8_t*)a.kc + base + ks * 32);
-          half2_t h0, h1, h2, h3;
-          i8x4_to_h2(w.x, h0, h1);
-          i8x4_to_h2(w.y, h2, h3);
-          kop = (half8_t){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
-        } else {
-          kop = *(const half8_t*)((const half_t*)a.kc + base + ks * 32);
-        }
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[ks], sacc[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int key = c / CPR, ch = c % CPR;
       if constexpr (I8) {
+        half_t* kd = &lds[buf][0][key * LD + ch * 16];
+        half_t* vd = &lds[buf][1][key * LD + ch * 16];
+        const uint32_t kw[4] = {stk[i].x, stk[i].y, stk[i].z, stk[i].w};
+        const uint32_t vw[4] = {stv[i].x, stv[i].y, stv[i].z, stv[i].w};
+        half8_t k0, k1, v0, v1;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          half2_t a0, a1, a2, a3, b0, b1, b2, b3;
+          i8x4_to_h2(kw[2 * c2], a0, a1);
+          i8x4_to_h2(kw[2 * c2 + 1], a2, a3);
+          i8x4_to_h2(vw[2 * c2], b0, b1);
+          i8x4_to_h2(vw[2 * c2 + 1], b2, b3);
+          const half8_t kk = (half8_t){a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+          const half8_t vv = (half8_t){b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+          if (c2 == 0) { k0 = kk; v0 = vv; } else { k1 = kk; v1 = vv; }
+        }
+        *(half8_t*)kd = k0;
+        *(half8_t*)(kd + 8) = k1;
+        *(half8_t*)vd = v0;
+        *(half8_t*)(vd + 8) = v1;
+      } else {
+        *(uint4*)&lds[buf][0][key * LD + ch * 8] = stk[i];
+        *(uint4*)&lds[buf][1][key * LD + ch * 8] = stv[i];
+      }
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  typedef __attribute__((address_space(3))) short4_t lds_short4;
+  int buf = 0;
+  for (int kt = 0; kt < kmax; kt += BN, buf ^= 1) {
+    const bool more = kt + BN < kmax;
+    if (more) gload(kt + BN);
+
+    float kscl[KB], vscl[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      kscl[kb] = 1.f;
+      vscl[kb] = 1.f;
+      if constexpr (I8) {
+        const int kg = kt + kb * kBlockSize;
+        const int ph = kg < L ? clamp_block(tbl[kg / kBlockSize], a.num_blocks) : 0;
         kscl[kb] = (float)a.ks[(int64_t)ph * a.hkv + h];
         vscl[kb] = (float)a.vs[(int64_t)ph * a.hkv + h];
       }
     }
 
-    // this lane: query row l16 of the wave; keys kt + 16 kb + 4 grp + e
-    float sv[8];
+    // S^T = K Q^T: this lane ends with query row l16 of each row block and keys kb*16 + 4*grp + e
+    float4_t s[RB][KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = kt + kb * 16 + 4 * grp + e;
-        const float x = sacc[kb][e] * (a.scale_log2 * kscl[kb]);
-        sv[kb * 4 + e] = key <= qpos ? x : -__builtin_inff();
-      }
-    float mloc = sv[0];
+      for (int rb = 0; rb < RB; ++rb) s[rb][kb] = (float4_t)0.f;
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sv[j]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float mn = fmaxf(m, mloc);
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    half8_t pop;
-    float ps = 0.f;
+      for (int ks = 0; ks < KS; ++ks) {
+        const half8_t kop = *(const half8_t*)&lds[buf][0][(kb * 16 + l16) * LD + ks * 32 + 8 * grp];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = fast_exp2(sv[j] - mn);
-      if constexpr (I8) {
-        ps += p;
-        pop[j] = (half_t)(p * vscl[j / 4]);
-      } else {
-        const half_t ph = (half_t)p;  // the weight the product uses is also the one summed
-        ps += (float)ph;
-        pop[j] = ph;
+        for (int rb = 0; rb < RB; ++rb)
+          s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rb][ks], s[rb][kb], 0, 0, 0);
       }
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
 
-    typedef __attribute__((address_space(3))) short4_t lds_short4;
+    half8_t pop[RB][BN / 32];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float sv[KB * 4];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kt + kb * 16 + 4 * grp + e;
+          const float x = s[rb][kb][e] * (a.scale_log2 * kscl[kb]);
+          sv[kb * 4 + e] = key <= qpos[rb] ? x : -__builtin_inff();
+        }
+      float mloc = sv[0];
+#pragma unroll
+      for (int j = 1; j < KB * 4; ++j) mloc = fmaxf(mloc, sv[j]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float mn = fmaxf(m[rb], mloc);
+      const float alpha = fast_exp2(m[rb] - mn);
+      m[rb] = mn;
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < KB * 4; ++j) {
+        const float p = fast_exp2(sv[j] - mn);
+        half_t ph;
+        if constexpr (I8) {
+          ps += p;
+          ph = (half_t)(p * vscl[j / 4]);
+        } else {
+          ph = (half_t)p;  // the weight the product uses is also the one summed
+          ps += (float)ph;
+        }
+        // k-step j/8 of the PV product; slot (j % 8): keys 4*grp + [0..3] of blocks 2*(j/8) and 2*(j/8)+1
+        pop[rb][j / 8][j % 8] = ph;
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      lsum[rb] = lsum[rb] * alpha + ps;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[rb][nt] *= alpha;
+    }
+
+    // O^T += V^T P^T
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const half_t* p1 = vlds + (4 * grp + (l16 >> 2)) * LDV + nt * 16 + 4 * (l16 & 3);
-      const half_t* p2 = p1 + 16 * LDV;
-      const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
-      const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p2);
-      const half4_t h1 = __builtin_bit_cast(half4_t, v1), h2 = __builtin_bit_cast(half4_t, v2);
-      const half8_t vop = (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w};
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, o[nt], 0, 0, 0);
+#pragma unroll
+      for (int pk = 0; pk < BN / 32; ++pk) {
+        const half_t* p1 = &lds[buf][1][(pk * 32 + 4 * grp + (l16 >> 2)) * LD + nt * 16 + 4 * (l16 & 3)];
+        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
+        const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1 + 16 * LD));
+        const half4_t h1 = __builtin_bit_cast(half4_t, v1), h2 = __builtin_bit_cast(half4_t, v2);
+        const half8_t vop = (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[rb][pk], o[rb][nt], 0, 0, 0);
+      }
     }
+
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
   }
 
-  if (rvalid) {
-    const float inv = 1.f / lsum;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!rvalid[rb]) continue;
+    const float inv = 1.f / lsum[rb];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       half4_t r;
-      r.x = (half_t)(o[nt][0] * inv);
-      r.y = (half_t)(o[nt][1] * inv);
-      r.z = (half_t)(o[nt][2] * inv);
-      r.w = (half_t)(o[nt][3] * inv);
-      *(half4_t*)(a.out + orow + nt * 16 + 4 * grp) = r;
+      r.x = (half_t)(o[rb][nt][0] * inv);
+      r.y = (half_t)(o[rb][nt][1] * inv);
+      r.z = (half_t)(o[rb][nt][2] * inv);
+      r.w = (half_t)(o[rb][nt][3] * inv);
+      *(half4_t*)(a.out + orow[rb] + nt * 16 + 4 * grp) = r;
     }
   }
 }
@@ -508,12 +632,12 @@ hipError_t launch_reduce(const AttnArgs& a, int head_dim, int group, int n_vtok,
 
 template <int D, bool I8>
 static hipError_t prefill_g(const AttnArgs& a, int g, int n, hipStream_t s) {
-  dim3 grid(n, a.hkv);
+  const dim3 grid(n * a.hkv);   // workgroup id = row tile * hkv + KV head
   switch (g) {
-    case 1: prefill_kernel<D, 1, I8><<<grid, 256, 0, s>>>(a); break;
-    case 2: prefill_kernel<D, 2, I8><<<grid, 256, 0, s>>>(a); break;
-    case 4: prefill_kernel<D, 4, I8><<<grid, 256, 0, s>>>(a); break;
-    case 8: prefill_kernel<D, 8, I8><<<grid, 256, 0, s>>>(a); break;
+    case 1: prefill_kernel<D, 1, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 2: prefill_kernel<D, 2, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 4: prefill_kernel<D, 4, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 8: prefill_kernel<D, 8, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -17,7 +17,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBlockSize = 16;     // tokens per block (the only size built)
 constexpr int kWave = 64;
-constexpr int kMfmaRows = 64;      // query rows per MFMA workgroup (4 waves x 16)
+constexpr int kMfmaRows = 128;     // query rows per MFMA workgroup (4 waves x 32)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
 
