@@ -155,7 +155,8 @@ size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
  *   q_lens        int32 [num_seqs]: query rows of sequence i (0 allowed).
  *   h_seq_lens, h_q_lens  host copies of the same values; the launch shape is
  *                 chosen from them, so they must equal the device arrays.
- *   scale         multiplier of q.k (normally head_dim ** -0.5).
+ *   scale         multiplier of q.k (normally head_dim ** -0.5); must be
+ *                 positive and finite (PA_ERR_SHAPE otherwise).
  *   out           fp16 [total_q][num_q_heads][head_dim].
  *   workspace     device scratch of at least pa_attend_workspace_bytes.
  *

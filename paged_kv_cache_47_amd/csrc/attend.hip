@@ -75,13 +75,9 @@ constexpr float kRescale = 8.0f;
 #ifndef PA_DECODE_NW
 #define PA_DECODE_NW 4   // waves per workgroup
 #endif
-#ifndef PA_DECODE_PF
-#define PA_DECODE_PF 1   // tiles in flight ahead of the one being processed
-#endif
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1   // 1: K/V tile loads carry the nontemporal hint (each tile is read once)
 #endif
-constexpr int PF = PA_DECODE_PF;
 
 __device__ __forceinline__ uint4 load16(const uint4* p) {
 #if PA_DECODE_NT
@@ -102,6 +98,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   constexpr int NL = kBlockSize / TPL; // loads per (block, head) tile
   constexpr int E2 = E / 2;            // fp16 pairs per lane per row
   constexpr int64_t TILE = (int64_t)kBlockSize * D * EB;
+#ifndef PA_DECODE_PINGPONG_I8
+#define PA_DECODE_PINGPONG_I8 0
+#endif
+  // two alternating tile buffers for fp16; int8 keeps one loop body (fewer live registers)
+  constexpr bool PINGPONG = I8 ? (PA_DECODE_PINGPONG_I8 != 0) : true;
 
   __shared__ float sm[NW][G], sl[NW][G];
   __shared__ float so[NW][G][D];
@@ -155,141 +156,158 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) vd[i] = load16(vt2 + i * 64 + lane);
   };
-  // Software pipeline: tiles for the next PF blocks of this wave are in flight
-  // while the current one is processed.
-  uint4 kbuf[PF + 1][NL], vbuf[PF + 1][NL];
-  int pbuf[PF + 1];
+  // One block of this wave: scores, softmax bookkeeping, P.V.  `kr`/`vr` hold
+  // the block's K and V tile rows of this lane.
+  auto process = [&](uint4* kr, uint4* vr, const int phys, const int blk) {
+    float ksc = a.scale_log2, vsc = 1.f;
+    if constexpr (I8) {
+      ksc *= (float)a.ks[(int64_t)phys * a.hkv + h];
+      vsc = (float)a.vs[(int64_t)phys * a.hkv + h];
+    }
+    const int tok0 = blk * kBlockSize + grp;
+    const bool tail = blk * kBlockSize + kBlockSize > kend;  // wave-uniform: last block of the range
+    if (tail) {  // drop V of keys past the range (their slots may hold anything)
 #pragma unroll
-  for (int j = 0; j < PF; ++j)
-    if (b + j * NW < bend) load_tile(b + j * NW, kbuf[j], vbuf[j], pbuf[j]);
+      for (int i = 0; i < NL; ++i)
+        if (tok0 + i * TPL >= kend) vr[i] = make_uint4(0, 0, 0, 0);
+    }
 
-  while (b < bend) {
-    if (b + PF * NW < bend) load_tile(b + PF * NW, kbuf[PF], vbuf[PF], pbuf[PF]);
-    {
-      uint4* kr = kbuf[0];
-      uint4* vr = vbuf[0];
-      const int phys = pbuf[0];
-      float ksc = a.scale_log2, vsc = 1.f;
+    // raw dot products q.k of this lane group's NL tokens for the G rows;
+    // the score (base 2) is d * ksc, ksc > 0
+    float s[NL][G];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      half2_t kh[E2];
+      const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
       if constexpr (I8) {
-        ksc *= (float)a.ks[(int64_t)phys * a.hkv + h];
-        vsc = (float)a.vs[(int64_t)phys * a.hkv + h];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) i8x4_to_h2(w4[c], kh[2 * c], kh[2 * c + 1]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kh[c] = __builtin_bit_cast(half2_t, w4[c]);
       }
-      const int tok0 = b * kBlockSize + grp;
-      const bool tail = b * kBlockSize + kBlockSize > kend;  // wave-uniform: last block of the range
-      if (tail) {  // drop V of keys past the range (their slots may hold anything)
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-          if (tok0 + i * TPL >= kend) vr[i] = make_uint4(0, 0, 0, 0);
-      }
-
-      // scores of this lane group's NL tokens for the G rows (base 2)
-      float s[NL][G];
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        half2_t kh[E2];
-        const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-        if constexpr (I8) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) i8x4_to_h2(w4[c], kh[2 * c], kh[2 * c + 1]);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) kh[c] = __builtin_bit_cast(half2_t, w4[c]);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.f;
-#pragma unroll
-          for (int c = 0; c < E2; ++c) d = __builtin_amdgcn_fdot2(qh[g][c], kh[c], d, false);
-          s[i][g] = group_sum<LPT>(d) * ksc;
-        }
-      }
-      if (tail) {
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-            if (tok0 + i * TPL >= kend) s[i][g] = -__builtin_inff();
-      }
-
-      // The running max moves only when a score exceeds it by more than
-      // kRescale (log2 units), so weights stay <= 2^kRescale and the
-      // accumulators are rescaled rarely.
-      bool grow = false;
-      float mb[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        mb[g] = s[0][g];
+        float d = 0.f;
 #pragma unroll
-        for (int i = 1; i < NL; ++i) mb[g] = fmaxf(mb[g], s[i][g]);
-        grow |= mb[g] > m[g] + kRescale;
+        for (int c = 0; c < E2; ++c) d = __builtin_amdgcn_fdot2(qh[g][c], kh[c], d, false);
+        s[i][g] = d;
       }
-      if (__builtin_amdgcn_ballot_w64(grow)) {
+    }
+    group_sum_all<LPT, NL * G>(&s[0][0]);
+    if (tail) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if (mb[g] > m[g] + kRescale) {
-            const float al = fast_exp2(m[g] - mb[g]);
-            m[g] = mb[g];
-            l[g] *= al;
+      for (int i = 0; i < NL; ++i)
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[g][e] *= al;
-          }
-        }
-      }
+        for (int g = 0; g < G; ++g)
+          if (tok0 + i * TPL >= kend) s[i][g] = -__builtin_inff();
+    }
 
-      if constexpr (NL >= 2) {
-        // P.V on v_dot2_f32_f16 over token pairs: vp[e] = (V[tok 2j][e], V[tok 2j+1][e])
+    // The running max moves only when a score exceeds it by more than
+    // kRescale (log2 units), so weights stay <= 2^kRescale and the
+    // accumulators are rescaled rarely.
+    bool grow = false;
+    float mb[G];
 #pragma unroll
-        for (int j = 0; j < NL / 2; ++j) {
-          half2_t vp[E];
-          v_token_pairs<I8>(vr[2 * j], vr[2 * j + 1], vp);
+    for (int g = 0; g < G; ++g) {
+      float x = s[0][g];
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float p0 = fast_exp2(s[2 * j][g] - m[g]), p1 = fast_exp2(s[2 * j + 1][g] - m[g]);
-            half2_t pp;
-            if constexpr (I8) {
-              l[g] += p0 + p1;
-              pp = (half2_t){(half_t)(p0 * vsc), (half_t)(p1 * vsc)};
-            } else {
-              pp = (half2_t){(half_t)p0, (half_t)p1};
-              // sum the rounded weights the product uses, so the output stays a convex combination
-              l[g] = __builtin_amdgcn_fdot2(pp, (half2_t){(half_t)1.f, (half_t)1.f}, l[g], false);
-            }
+      for (int i = 1; i < NL; ++i) x = fmaxf(x, s[i][g]);
+      mb[g] = x * ksc;
+      grow |= mb[g] > m[g] + kRescale;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[g][e] = __builtin_amdgcn_fdot2(pp, vp[e], acc[g][e], false);
-          }
-        }
-      } else {
-        // one token row per lane per block (int8, head_dim 64)
-        float vf[E];
-        const uint32_t w4[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+      for (int g = 0; g < G; ++g) {
+        if (mb[g] > m[g] + kRescale) {
+          const float al = fast_exp2(m[g] - mb[g]);
+          m[g] = mb[g];
+          l[g] *= al;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          half2_t lo, hi;
-          i8x4_to_h2(w4[c], lo, hi);
-          vf[4 * c + 0] = (float)lo.x * vsc;
-          vf[4 * c + 1] = (float)lo.y * vsc;
-          vf[4 * c + 2] = (float)hi.x * vsc;
-          vf[4 * c + 3] = (float)hi.y * vsc;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float p0 = fast_exp2(s[0][g] - m[g]);
-          l[g] += p0;
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p0, vf[e], acc[g][e]);
+          for (int e = 0; e < E; ++e) acc[g][e] *= al;
         }
       }
     }
+
+    if constexpr (NL >= 2) {
+      // P.V on v_dot2_f32_f16 over token pairs: vp[e] = (V[tok 2j][e], V[tok 2j+1][e])
 #pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      pbuf[j] = pbuf[j + 1];
+      for (int j = 0; j < NL / 2; ++j) {
+        half2_t vp[E];
+        v_token_pairs<I8>(vr[2 * j], vr[2 * j + 1], vp);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p0 = fast_exp2(fmaf(s[2 * j][g], ksc, -m[g]));
+          const float p1 = fast_exp2(fmaf(s[2 * j + 1][g], ksc, -m[g]));
+          half2_t pp;
+          if constexpr (I8) {
+            l[g] += p0 + p1;
+            pp = (half2_t){(half_t)(p0 * vsc), (half_t)(p1 * vsc)};
+          } else {
+            pp = (half2_t){(half_t)p0, (half_t)p1};
+            // sum the rounded weights the product uses, so the output stays a convex combination
+            l[g] = __builtin_amdgcn_fdot2(pp, (half2_t){(half_t)1.f, (half_t)1.f}, l[g], false);
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[g][e] = __builtin_amdgcn_fdot2(pp, vp[e], acc[g][e], false);
+        }
+      }
+    } else {
+      // one token row per lane per block (int8, head_dim 64)
+      float vf[E];
+      const uint32_t w4[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        half2_t lo, hi;
+        i8x4_to_h2(w4[c], lo, hi);
+        vf[4 * c + 0] = (float)lo.x * vsc;
+        vf[4 * c + 1] = (float)lo.y * vsc;
+        vf[4 * c + 2] = (float)hi.x * vsc;
+        vf[4 * c + 3] = (float)hi.y * vsc;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p0 = fast_exp2(fmaf(s[0][g], ksc, -m[g]));
+        l[g] += p0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p0, vf[e], acc[g][e]);
+      }
+    }
+  };
+
+  // The wave's next block is in flight while the current one is processed.
+  if constexpr (PINGPONG) {
+    // two tile buffers used in turn (no register copies between iterations)
+    uint4 ka[NL], va[NL], kb[NL], vb[NL];
+    int pha = 0, phb = 0;
+    if (b < bend) load_tile(b, ka, va, pha);
+    while (b < bend) {
+      if (b + NW < bend) load_tile(b + NW, kb, vb, phb);
+      process(ka, va, pha, b);
+      b += NW;
+      if (b >= bend) break;
+      if (b + NW < bend) load_tile(b + NW, ka, va, pha);
+      process(kb, vb, phb, b);
+      b += NW;
+    }
+  } else {
+    // one loop body; the prefetched tile moves into the current one
+    uint4 kc[NL], vc[NL];
+    int phc = 0;
+    if (b < bend) load_tile(b, kc, vc, phc);
+    while (b < bend) {
+      uint4 kn[NL], vn[NL];
+      int phn = 0;
+      if (b + NW < bend) load_tile(b + NW, kn, vn, phn);
+      process(kc, vc, phc, b);
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        kbuf[j][i] = kbuf[j + 1][i];
-        vbuf[j][i] = vbuf[j + 1][i];
+        kc[i] = kn[i];
+        vc[i] = vn[i];
       }
+      phc = phn;
+      b += NW;
     }
-    b += NW;
   }
 
   // merge the TPL token-row streams of this wave (lane groups), then the waves

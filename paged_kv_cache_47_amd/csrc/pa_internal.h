@@ -106,6 +106,29 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// group_sum over COUNT independent values, step-major: the COUNT adds of
+// one butterfly step are independent, so they fill the wait states a DPP read
+// of a just-written register needs.
+template <int N, int COUNT>
+__device__ __forceinline__ void group_sum_all(float* x) {
+  if constexpr (N >= 2) {
+#pragma unroll
+    for (int k = 0; k < COUNT; ++k) x[k] += dpp<0xB1>(x[k]);
+  }
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int k = 0; k < COUNT; ++k) x[k] += dpp<0x4E>(x[k]);
+  }
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int k = 0; k < COUNT; ++k) x[k] += dpp<0x141>(x[k]);
+  }
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int k = 0; k < COUNT; ++k) x[k] += dpp<0x140>(x[k]);
+  }
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
   return x;
