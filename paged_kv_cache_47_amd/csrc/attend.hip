@@ -108,7 +108,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   __shared__ float so[NW][G][D];
 
   const int u = blockIdx.x, h = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps block indices scalar
   const int2 un = a.vunit[u];
   if (un.x < 0) return;
   const VTok vt = a.vtok[un.x];
@@ -414,7 +415,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   if (mu.x < 0) return;
   const SeqInfo si = a.seqs[mu.x];
   const int L = si.kv_len, Q = si.q_len, rows = Q * G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps block indices scalar
   const int l16 = lane & 15, grp = lane >> 4;
   const int r0 = mu.y * kMfmaRows;
   const int last_row = min(rows, r0 + kMfmaRows) - 1;
