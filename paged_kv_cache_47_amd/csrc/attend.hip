@@ -44,15 +44,19 @@ __device__ __forceinline__ void i8x4_to_h2(uint32_t w, half2_t& lo, half2_t& hi)
 // V of two token rows (same dims) -> (row0, row1) fp16 pairs per dim, the
 // operand layout of v_dot2 over tokens.  fp16: one byte permute per pair.
 // int8: interleave the two rows' codes, then the 0x64XX fp16 trick.
-template <bool I8>
-__device__ __forceinline__ void v_token_pairs(const uint4& r0, const uint4& r1, half2_t* vp) {
-  const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w};
-  const uint32_t b[4] = {r1.x, r1.y, r1.z, r1.w};
+// N dwords of one lane's share of a token row (8 or 16 bytes per load).
+template <int N>
+struct Dw {
+  uint32_t v[N];
+};
+
+template <bool I8, int N>
+__device__ __forceinline__ void v_token_pairs(const Dw<N>& r0, const Dw<N>& r1, half2_t* vp) {
   if constexpr (I8) {
     const half2_t bias = {(half_t)1152.0f, (half_t)1152.0f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t x = a[c] ^ 0x80808080u, y = b[c] ^ 0x80808080u;
+    for (int c = 0; c < N; ++c) {
+      const uint32_t x = r0.v[c] ^ 0x80808080u, y = r1.v[c] ^ 0x80808080u;
       const uint32_t t01 = __builtin_amdgcn_perm(y, x, 0x05010400u);  // x.b0 y.b0 x.b1 y.b1
       const uint32_t t23 = __builtin_amdgcn_perm(y, x, 0x07030602u);  // x.b2 y.b2 x.b3 y.b3
       vp[4 * c + 0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, t01, 0x04010400u)) - bias;
@@ -62,14 +66,22 @@ __device__ __forceinline__ void v_token_pairs(const uint4& r0, const uint4& r1, 
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      vp[2 * c + 0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b[c], a[c], 0x05040100u));
-      vp[2 * c + 1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(b[c], a[c], 0x07060302u));
+    for (int c = 0; c < N; ++c) {
+      vp[2 * c + 0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(r1.v[c], r0.v[c], 0x05040100u));
+      vp[2 * c + 1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(r1.v[c], r0.v[c], 0x07060302u));
     }
   }
 }
 
 constexpr float kRescale = 8.0f;
+
+// fp16 scale at a wave-uniform index, read as the aligned dword that holds it
+// (a scalar load; 16-bit loads would go through the vector memory path).
+__device__ __forceinline__ float scale_at(const half_t* base, int64_t idx) {
+  const uint32_t w = ((const uint32_t*)base)[idx >> 1];
+  const uint16_t bits = (idx & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
+  return (float)__builtin_bit_cast(half_t, bits);
+}
 
 // ============================================================ vector path ===
 #ifndef PA_DECODE_NW
@@ -79,20 +91,25 @@ constexpr float kRescale = 8.0f;
 #define PA_DECODE_NT 1   // 1: K/V tile loads carry the nontemporal hint (each tile is read once)
 #endif
 
-__device__ __forceinline__ uint4 load16(const uint4* p) {
+template <int N>
+__device__ __forceinline__ Dw<N> load_dw(const uint32_t* p) {
+  typedef uint32_t vec_t __attribute__((ext_vector_type(N)));
 #if PA_DECODE_NT
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
-  return make_uint4(v.x, v.y, v.z, v.w);
+  const vec_t x = __builtin_nontemporal_load((const vec_t*)p);
 #else
-  return *p;
+  const vec_t x = *(const vec_t*)p;
 #endif
+  Dw<N> r;
+#pragma unroll
+  for (int c = 0; c < N; ++c) r.v[c] = x[c];
+  return r;
 }
 
-template <int D, int G, bool I8, int NW>
+template <int D, int G, bool I8, int NW, int VB>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   constexpr int EB = I8 ? 1 : 2;       // bytes per element
-  constexpr int E = 16 / EB;           // elements per lane per 16-byte load
+  constexpr int ND = VB / 4;           // dwords per lane per load (VB = 8 or 16 bytes)
+  constexpr int E = VB / EB;           // elements per lane per load
   constexpr int LPT = D / E;           // lanes per token row
   constexpr int TPL = 64 / LPT;        // token rows per wave-wide load
   constexpr int NL = kBlockSize / TPL; // loads per (block, head) tile
@@ -147,30 +164,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 
   const int bend = (kend + kBlockSize - 1) / kBlockSize;
   int b = kbeg / kBlockSize + wave;
-  auto load_tile = [&](int blk, uint4* kd, uint4* vd, int& ph) {
+  auto load_tile = [&](int blk, Dw<ND>* kd, Dw<ND>* vd, int& ph) {
     ph = clamp_block(tbl[blk], a.num_blocks);
     const int64_t off = ((int64_t)ph * a.hkv + h) * TILE;
-    const uint4* kt = (const uint4*)((const char*)a.kc + off);
-    const uint4* vt2 = (const uint4*)((const char*)a.vc + off);
+    const uint32_t* kt = (const uint32_t*)((const char*)a.kc + off);
+    const uint32_t* vt2 = (const uint32_t*)((const char*)a.vc + off);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) kd[i] = load16(kt + i * 64 + lane);
+    for (int i = 0; i < NL; ++i) kd[i] = load_dw<ND>(kt + (i * 64 + lane) * ND);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vd[i] = load16(vt2 + i * 64 + lane);
+    for (int i = 0; i < NL; ++i) vd[i] = load_dw<ND>(vt2 + (i * 64 + lane) * ND);
   };
   // One block of this wave: scores, softmax bookkeeping, P.V.  `kr`/`vr` hold
   // the block's K and V tile rows of this lane.
-  auto process = [&](uint4* kr, uint4* vr, const int phys, const int blk) {
+  auto process = [&](Dw<ND>* kr, Dw<ND>* vr, const int phys, const int blk) {
     float ksc = a.scale_log2, vsc = 1.f;
     if constexpr (I8) {
-      ksc *= (float)a.ks[(int64_t)phys * a.hkv + h];
-      vsc = (float)a.vs[(int64_t)phys * a.hkv + h];
+      ksc *= scale_at(a.ks, (int64_t)phys * a.hkv + h);
+      vsc = scale_at(a.vs, (int64_t)phys * a.hkv + h);
     }
     const int tok0 = blk * kBlockSize + grp;
     const bool tail = blk * kBlockSize + kBlockSize > kend;  // wave-uniform: last block of the range
     if (tail) {  // drop V of keys past the range (their slots may hold anything)
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        if (tok0 + i * TPL >= kend) vr[i] = make_uint4(0, 0, 0, 0);
+        if (tok0 + i * TPL >= kend) vr[i] = Dw<ND>{};
     }
 
     // raw dot products q.k of this lane group's NL tokens for the G rows;
@@ -179,13 +196,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       half2_t kh[E2];
-      const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
       if constexpr (I8) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) i8x4_to_h2(w4[c], kh[2 * c], kh[2 * c + 1]);
+        for (int c = 0; c < ND; ++c) i8x4_to_h2(kr[i].v[c], kh[2 * c], kh[2 * c + 1]);
       } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kh[c] = __builtin_bit_cast(half2_t, w4[c]);
+        for (int c = 0; c < ND; ++c) kh[c] = __builtin_bit_cast(half2_t, kr[i].v[c]);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -235,7 +251,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < NL / 2; ++j) {
         half2_t vp[E];
-        v_token_pairs<I8>(vr[2 * j], vr[2 * j + 1], vp);
+        v_token_pairs<I8, ND>(vr[2 * j], vr[2 * j + 1], vp);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float p0 = fast_exp2(fmaf(s[2 * j][g], ksc, -m[g]));
@@ -256,11 +272,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     } else {
       // one token row per lane per block (int8, head_dim 64)
       float vf[E];
-      const uint32_t w4[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < ND; ++c) {
         half2_t lo, hi;
-        i8x4_to_h2(w4[c], lo, hi);
+        i8x4_to_h2(vr[0].v[c], lo, hi);
         vf[4 * c + 0] = (float)lo.x * vsc;
         vf[4 * c + 1] = (float)lo.y * vsc;
         vf[4 * c + 2] = (float)hi.x * vsc;
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   // The wave's next block is in flight while the current one is processed.
   if constexpr (PINGPONG) {
     // two tile buffers used in turn (no register copies between iterations)
-    uint4 ka[NL], va[NL], kb[NL], vb[NL];
+    Dw<ND> ka[NL], va[NL], kb[NL], vb[NL];
     int pha = 0, phb = 0;
     if (b < bend) load_tile(b, ka, va, pha);
     while (b < bend) {
@@ -293,11 +308,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     }
   } else {
     // one loop body; the prefetched tile moves into the current one
-    uint4 kc[NL], vc[NL];
+    Dw<ND> kc[NL], vc[NL];
     int phc = 0;
     if (b < bend) load_tile(b, kc, vc, phc);
     while (b < bend) {
-      uint4 kn[NL], vn[NL];
+      Dw<ND> kn[NL], vn[NL];
       int phn = 0;
       if (b + NW < bend) load_tile(b + NW, kn, vn, phn);
       process(kc, vc, phc, b);
@@ -615,14 +630,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
 }
 
 // =============================================================== dispatch ===
+#ifndef PA_DECODE_VB_I8
+#define PA_DECODE_VB_I8 16  // bytes per lane per load for int8 pools (8: twice the lanes per row)
+#endif
+
 template <int D, bool I8>
 static hipError_t decode_g(const AttnArgs& a, int g, int n, hipStream_t s) {
+  // 16-byte loads per lane; 8-byte int8 loads halve the per-lane registers
+  // (4 waves/SIMD) but add reduction and softmax work, and measure slower
+  constexpr int kVB = I8 ? PA_DECODE_VB_I8 : 16;
   dim3 grid(n, a.hkv);
   switch (g) {
-    case 1: decode_kernel<D, 1, I8, PA_DECODE_NW><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
-    case 2: decode_kernel<D, 2, I8, PA_DECODE_NW><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
-    case 4: decode_kernel<D, 4, I8, PA_DECODE_NW><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
-    case 8: decode_kernel<D, 8, I8, PA_DECODE_NW><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 1: decode_kernel<D, 1, I8, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 2: decode_kernel<D, 2, I8, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 4: decode_kernel<D, 4, I8, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 8: decode_kernel<D, 8, I8, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

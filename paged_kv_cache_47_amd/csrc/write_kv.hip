@@ -45,33 +45,20 @@ hipError_t launch_write_f16(const pa_cache_desc& d, const void* k, const void* v
 }
 
 // ---------------------------------------------------------------- int8 ----
-// One wave per (run of tokens writing one block, KV head, K or V).  A run
-// starts at a token whose predecessor does not write the previous slot of the
-// same block; it continues while the next token writes the next slot.  The
-// block's codes live in registers as exact small floats (EPL dims per lane),
-// and each token of the run is replayed in order:
+// A run starts at a token whose predecessor does not write the previous slot
+// of the same block; it continues while the next token writes the next slot.
+// A wave replays a run on one (block, KV head, K or V): the block's codes live
+// in registers as exact small floats (EPL dims per lane), and each token of
+// the run is replayed in order:
 //   x_j = code_j * scale (j < o), x_o = new, scale = fp16(max|x| / 127),
 //   code_j = clamp(rint(x_j / scale), -127, 127)   (zero if scale == 0).
 // fp32 division is IEEE (the build does not use fast-math) so the codes match
 // a CPU evaluation of the same formula bit for bit.
 template <int D>
-__global__ __launch_bounds__(64) void write_i8_kernel(const half_t* __restrict__ k, const half_t* __restrict__ v,
-                                                      const int32_t* __restrict__ slots, int32_t T, int32_t hkv,
-                                                      int64_t num_slots, int8_t* __restrict__ kc,
-                                                      int8_t* __restrict__ vc, half_t* __restrict__ ks,
-                                                      half_t* __restrict__ vs) {
+__device__ void replay_run_i8(const half_t* __restrict__ src, const int32_t s, const int t, const int n,
+                              const int h, const int hkv, int8_t* __restrict__ cache, half_t* __restrict__ scales) {
   constexpr int EPL = D / 64;  // dims per lane: 2 (d128) or 1 (d64)
-  const int t = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
   const int lane = threadIdx.x;
-  const int32_t s = slots[t];
-  if (s < 0 || s >= num_slots) return;
-  if (t > 0 && (s % kBlockSize) != 0 && slots[t - 1] == s - 1) return;  // not the first token of its run
-  int n = 1;
-  while (t + n < T && ((s + n) % kBlockSize) != 0 && slots[t + n] == s + n) ++n;
-
-  const half_t* src = which ? v : k;
-  int8_t* cache = which ? vc : kc;
-  half_t* scales = which ? vs : ks;
   const int64_t blk = s / kBlockSize;
   const int o0 = s % kBlockSize;
   int8_t* tile = cache + (blk * hkv + h) * (int64_t)kBlockSize * D;
@@ -118,9 +105,36 @@ __global__ __launch_bounds__(64) void write_i8_kernel(const half_t* __restrict__
   if (lane == 0) scales[sidx] = (half_t)sc;
 }
 
+// One wave per (kI8Window consecutive tokens, KV head, K or V): it replays, in
+// token order, every run that starts in its window (a run may continue past
+// the window; the tokens it covers there are not run starts and are skipped
+// by the next window's wave).
+constexpr int kI8Window = 8;
+
+template <int D>
+__global__ __launch_bounds__(64) void write_i8_kernel(const half_t* __restrict__ k, const half_t* __restrict__ v,
+                                                      const int32_t* __restrict__ slots, int32_t T, int32_t hkv,
+                                                      int64_t num_slots, int8_t* __restrict__ kc,
+                                                      int8_t* __restrict__ vc, half_t* __restrict__ ks,
+                                                      half_t* __restrict__ vs) {
+  const int h = blockIdx.y, which = blockIdx.z;
+  const half_t* src = which ? v : k;
+  int8_t* cache = which ? vc : kc;
+  half_t* scales = which ? vs : ks;
+  const int t_end = min(T, (int)(blockIdx.x + 1) * kI8Window);
+  for (int t = blockIdx.x * kI8Window; t < t_end; ++t) {
+    const int32_t s = slots[t];
+    if (s < 0 || s >= num_slots) continue;
+    if (t > 0 && (s % kBlockSize) != 0 && slots[t - 1] == s - 1) continue;  // inside a run started earlier
+    int n = 1;
+    while (t + n < T && ((s + n) % kBlockSize) != 0 && slots[t + n] == s + n) ++n;
+    replay_run_i8<D>(src, s, t, n, h, hkv, cache, scales);
+  }
+}
+
 hipError_t launch_write_i8(const pa_cache_desc& d, const void* k, const void* v, const int32_t* slots,
                            int32_t T, void* kc, void* vc, void* ks, void* vs, hipStream_t s) {
-  dim3 grid(T, d.num_kv_heads, 2);
+  dim3 grid((T + kI8Window - 1) / kI8Window, d.num_kv_heads, 2);
   const int64_t ns = (int64_t)d.num_blocks * kBlockSize;
   if (d.head_dim == 128)
     write_i8_kernel<128><<<grid, 64, 0, s>>>((const half_t*)k, (const half_t*)v, slots, T, d.num_kv_heads, ns,
