@@ -60,6 +60,41 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* lds, int4& total) {
 
 __device__ __forceinline__ int parts_for(int nvis, int part) { return part <= 0 ? 1 : (nvis + part - 1) / part; }
 
+// Row tiles of the MFMA path go out longest first.  A tile's cost is its
+// number of visible keys (causal: the last row's), and tiles that attend over
+// long contexts would otherwise start late and finish after the rest of the
+// grid; with 64-key cost buckets in descending order (a counting sort over
+// the workgroup) the dispatcher fills the machine greedily, longest job first.
+// The order within a bucket is whatever the atomics give: every tile writes
+// its own rows, so the results do not depend on it.
+constexpr int kCostBuckets = kPlanThreads;
+
+__device__ int tile_cost_bucket(const PlanArgs& a, int2 mu) {
+  const SeqInfo si = a.seqs[mu.x];
+  const int rows = si.q_len * a.group;
+  const int last_row = min(rows, (mu.y + 1) * kMfmaRows) - 1;
+  const int kmax = min(si.kv_len, si.kv_len - si.q_len + last_row / a.group + 1);
+  return min(kmax / 64, kCostBuckets - 1);
+}
+
+__device__ void order_row_tiles(const PlanArgs& a, int n) {
+  __shared__ int slot[kCostBuckets];
+  __shared__ int4 scan_lds[kPlanWaves];
+  slot[threadIdx.x] = 0;
+  __syncthreads();   // also makes this workgroup's writes of seqs and munit_tmp visible to all its threads
+  for (int u = threadIdx.x; u < n; u += kPlanThreads)
+    atomicAdd(&slot[kCostBuckets - 1 - tile_cost_bucket(a, a.munit_tmp[u])], 1);
+  __syncthreads();
+  int4 tot;
+  const int first = block_exclusive_scan4(make_int4(slot[threadIdx.x], 0, 0, 0), scan_lds, tot).x;
+  slot[threadIdx.x] = first;
+  __syncthreads();
+  for (int u = threadIdx.x; u < n; u += kPlanThreads) {
+    const int2 mu = a.munit_tmp[u];
+    a.munit[atomicAdd(&slot[kCostBuckets - 1 - tile_cost_bucket(a, mu)], 1)] = mu;
+  }
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int4 lds[kPlanWaves];
   int base_q = 0, base_vt = 0, base_vu = 0, base_mu = 0;
@@ -94,7 +129,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       si.pad = 0;
       a.seqs[i] = si;
       for (int r = 0; r < nmu; ++r)
-        if (mu0 + r < a.cap_munit) a.munit[mu0 + r] = make_int2(i, r);
+        if (mu0 + r < a.cap_munit) a.munit_tmp[mu0 + r] = make_int2(i, r);
       int u = vu0;
       for (int t = 0; t < nvt; ++t) {
         const int parts = parts_for(L - Q + t + 1, a.part);
@@ -126,6 +161,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   for (int u = base_vu + threadIdx.x; u < a.cap_vunit; u += kPlanThreads) a.vunit[u] = make_int2(-1, 0);
   for (int u = base_mu + threadIdx.x; u < a.cap_munit; u += kPlanThreads) a.munit[u] = make_int2(-1, 0);
+  order_row_tiles(a, min(base_mu, a.cap_munit));
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
@@ -138,7 +174,8 @@ struct HostPlan {
   int32_t part = 0, min_rows = 16, total_q = 0;
   int64_t n_vtok = 0, n_vunit = 0, n_munit = 0;
   int32_t max_parts = 0;
-  size_t off_seqs = 0, off_vtok = 0, off_vunit = 0, off_munit = 0, off_lse = 0, off_po = 0, bytes = 0;
+  size_t off_seqs = 0, off_vtok = 0, off_vunit = 0, off_munit = 0, off_munit_tmp = 0, off_lse = 0, off_po = 0;
+  size_t bytes = 0;
 };
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -215,6 +252,8 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   P.off_vunit = off;
   off = align_up(off + sizeof(int2) * (size_t)std::max<int64_t>(P.n_vunit, 1), 256);
   P.off_munit = off;
+  off = align_up(off + sizeof(int2) * (size_t)std::max<int64_t>(P.n_munit, 1), 256);
+  P.off_munit_tmp = off;
   off = align_up(off + sizeof(int2) * (size_t)std::max<int64_t>(P.n_munit, 1), 256);
   const bool split = P.max_parts > 1;
   P.off_lse = off;
@@ -313,6 +352,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   pl.vtok = (VTok*)(ws + P.off_vtok);
   pl.vunit = (int2*)(ws + P.off_vunit);
   pl.munit = (int2*)(ws + P.off_munit);
+  pl.munit_tmp = (int2*)(ws + P.off_munit_tmp);
   pl.num_seqs = num_seqs;
   pl.group = g;
   pl.part = P.part;

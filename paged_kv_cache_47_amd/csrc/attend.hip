@@ -410,6 +410,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
 // barrier per step.
 constexpr int kMfmaWaves = 4;
 constexpr int kMfmaBN = 64;
+// Lazy-rescale threshold of the MFMA path (log2 units): weights stay below
+// 2^6, so an int8 weight times its V scale (at most 65504 / 127) stays finite in fp16.
+constexpr float kRescalePf = 6.0f;
 
 template <int D, int G, bool I8>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
@@ -437,6 +440,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   const int last_row = min(rows, r0 + kMfmaRows) - 1;
   const int kmax = min(L, L - Q + last_row / G + 1);
   const int32_t* tbl = a.block_tables + (int64_t)mu.x * a.max_blocks;
+  const int qmin = L - Q + (r0 + wave * 32) / G;  // query position of this wave's first row
 
   int qpos[RB];
   int64_t orow[RB];
@@ -465,7 +469,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   }
 
   uint4 stk[PT], stv[PT];
+  float nks[KB], nvs[KB];  // int8: K and V scales of the 16-key blocks of the tiles in flight
   auto gload = [&](int kt) {
+    if constexpr (I8) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int kg = kt + kb * kBlockSize;
+        const int ph = kg < L ? clamp_block(tbl[kg / kBlockSize], a.num_blocks) : 0;
+        nks[kb] = scale_at(a.ks, (int64_t)ph * a.hkv + h);
+        nvs[kb] = scale_at(a.vs, (int64_t)ph * a.hkv + h);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int c = threadIdx.x + 256 * i;
@@ -522,20 +536,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   int buf = 0;
   for (int kt = 0; kt < kmax; kt += BN, buf ^= 1) {
     const bool more = kt + BN < kmax;
-    if (more) gload(kt + BN);
 
-    float kscl[KB], vscl[KB];
+    // score scale per 16-key block (base 2; int8 folds in the block's K scale, >= 0)
+    float cks[KB], vscl[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      kscl[kb] = 1.f;
-      vscl[kb] = 1.f;
-      if constexpr (I8) {
-        const int kg = kt + kb * kBlockSize;
-        const int ph = kg < L ? clamp_block(tbl[kg / kBlockSize], a.num_blocks) : 0;
-        kscl[kb] = (float)a.ks[(int64_t)ph * a.hkv + h];
-        vscl[kb] = (float)a.vs[(int64_t)ph * a.hkv + h];
-      }
+      cks[kb] = I8 ? a.scale_log2 * nks[kb] : a.scale_log2;
+      vscl[kb] = I8 ? nvs[kb] : 1.f;
     }
+    if (more) gload(kt + BN);
 
     // S^T = K Q^T: this lane ends with query row l16 of each row block and keys kb*16 + 4*grp + e
     float4_t s[RB][KB];
@@ -552,30 +561,43 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
       }
     }
 
+    // Online softmax.  Steps whose keys all precede this wave's first query
+    // position need no causal mask (wave-uniform test); there the block max is
+    // taken on raw scores and scaled once, and the scale is fused into the
+    // exponent's FMA.  The running max moves only when a score exceeds it by
+    // more than kRescalePf (log2 units), so the accumulators are rescaled rarely.
+    const bool full = kt + BN - 1 <= qmin;
     half8_t pop[RB][BN / 32];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float sv[KB * 4];
+      float mb = -__builtin_inff();
+      if (full) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = kt + kb * 16 + 4 * grp + e;
-          const float x = s[rb][kb][e] * (a.scale_log2 * kscl[kb]);
-          sv[kb * 4 + e] = key <= qpos[rb] ? x : -__builtin_inff();
+        for (int kb = 0; kb < KB; ++kb) {
+          const float r = fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3]));
+          mb = fmaxf(mb, r * cks[kb]);
         }
-      float mloc = sv[0];
+      } else {
 #pragma unroll
-      for (int j = 1; j < KB * 4; ++j) mloc = fmaxf(mloc, sv[j]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float mn = fmaxf(m[rb], mloc);
-      const float alpha = fast_exp2(m[rb] - mn);
-      m[rb] = mn;
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = kt + kb * 16 + 4 * grp + e;
+            if (key <= qpos[rb]) mb = fmaxf(mb, s[rb][kb][e] * cks[kb]);
+          }
+      }
+      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      const bool grow = mb > m[rb] + kRescalePf;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float al = grow ? fast_exp2(m[rb] - mb) : 1.f;
+        m[rb] = grow ? mb : m[rb];
+        lsum[rb] *= al;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[rb][nt] *= al;
+      }
       float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < KB * 4; ++j) {
-        const float p = fast_exp2(sv[j] - mn);
+      auto weight = [&](float p, int j) {
         half_t ph;
         if constexpr (I8) {
           ps += p;
@@ -586,12 +608,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
         }
         // k-step j/8 of the PV product; slot (j % 8): keys 4*grp + [0..3] of blocks 2*(j/8) and 2*(j/8)+1
         pop[rb][j / 8][j % 8] = ph;
-      }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      lsum[rb] = lsum[rb] * alpha + ps;
+      };
+      if (full) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[rb][nt] *= alpha;
+        for (int j = 0; j < KB * 4; ++j) weight(fast_exp2(fmaf(s[rb][j / 4][j % 4], cks[j / 4], -m[rb])), j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < KB * 4; ++j) {
+          const int key = kt + (j / 4) * 16 + 4 * grp + (j % 4);
+          const float p = fast_exp2(fmaf(s[rb][j / 4][j % 4], cks[j / 4], -m[rb]));
+          weight(key <= qpos[rb] ? p : 0.f, j);
+        }
+      }
+      lsum[rb] += ps;   // this lane's share of the row sum; the row's four lanes are added at the end
     }
 
     // O^T += V^T P^T
@@ -615,6 +644,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
+    lsum[rb] += __shfl_xor(lsum[rb], 16, 64);
+    lsum[rb] += __shfl_xor(lsum[rb], 32, 64);
     if (!rvalid[rb]) continue;
     const float inv = 1.f / lsum[rb];
 #pragma unroll

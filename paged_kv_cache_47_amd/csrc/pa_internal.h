@@ -62,6 +62,7 @@ struct PlanArgs {
   VTok* vtok;
   int2* vunit;
   int2* munit;
+  int2* munit_tmp;     // row tiles in sequence order, before the longest-first ordering
   int32_t num_seqs;
   int32_t group;
   int32_t part;        // <= 0: one partition per row
