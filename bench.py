@@ -84,10 +84,14 @@ class TimingEvents:
         return float(ms.value)
 
 
+# the sources of the vector-path kernel whose HBM traffic the PMC summary records
+DECODE_SOURCES = ("decode.hip", "pa_internal.h")
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_47_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in DECODE_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -165,6 +169,88 @@ def cpu_baseline(w, step: int, budget_s: float):
     }
 
 
+# ------------------------------------------------------------ profile summaries ----
+# Run on the host after the profiler runs (no GPU needed); they read the
+# rocprofv3 CSV files and write the summaries kept under profiles/.
+
+def _step_lengths(w, s: int = 0):
+    """Post-write kv lengths and query rows of step ``s`` (host bookkeeping only)."""
+    from paged_kv_cache_47_amd.workload import build_manager
+    mgr, ids = build_manager(w)
+    for i in range(s + 1):
+        b = mgr.step(ids, w.step(i).q_lens)
+    return b.seq_lens.astype(np.int64), b.q_lens.astype(np.int64)
+
+
+def _read_counters(path: str):
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.setdefault((int(r["Dispatch_Id"]), r["Kernel_Name"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    return rows
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, kernel_prefix: str, out: str, cmds) -> dict:
+    """HBM bytes per launch of the decode kernel from one FETCH_SIZE run and
+    one WRITE_SIZE run, each scaled by what the same counter reads for the
+    plain device copy of ``copy_mib`` MiB that bench.py makes at the end of
+    those runs (--copy-calibration-mib)."""
+    copy_bytes = copy_mib << 20
+    res = {"kernel_prefix": kernel_prefix, "commands": list(cmds)}
+    per = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _read_counters(path)
+        copies = [c[name] for (d, k), c in rows.items() if k.startswith("__amd_rocclr_copyBuffer") and name in c]
+        calib = max(copies)                                     # KiB read (or written) for the big copy
+        vals = [c[name] for (d, k), c in rows.items() if k.startswith(kernel_prefix) and name in c]
+        per[name] = {"launches": len(vals), "KiB_per_launch": float(np.mean(vals)), "copy_KiB": calib,
+                     "scale": copy_bytes / (calib * 1024.0)}
+    fetch = per["FETCH_SIZE"]["KiB_per_launch"] * 1024 * per["FETCH_SIZE"]["scale"]
+    write = per["WRITE_SIZE"]["KiB_per_launch"] * 1024 * per["WRITE_SIZE"]["scale"]
+    import synthetic
+    w = synthetic.CONFIGS[3]()
+    L, Q = _step_lengths(w, 0)
+    alg = work_split(w, L, Q)[0]
+    res.update({"copy_bytes": copy_bytes, "counters": per,
+                "hbm_bytes_per_launch": int(round(fetch + write)),
+                "algorithmic_bytes_per_launch": int(alg),
+                "traffic_over_algorithmic": round((fetch + write) / alg, 4),
+                "source_hash": source_hash(), "source_files": list(DECODE_SOURCES)})
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
+def summarize_trace(stats_csv: str, out: str, cmd: str, title: str, alg_bytes: int = 0, alg_flops: int = 0,
+                    kernel_prefix: str = "") -> None:
+    """Kernel table from a rocprofv3 --kernel-trace --stats run, with the
+    algorithmic rate of one kernel at its trace-average duration."""
+    import csv
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"# {title}", "", "Command (repository root, one MI355X):", "", f"    {cmd}", "",
+             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    avg = None
+    for r in rows:
+        name = r["Name"]
+        lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+        if kernel_prefix and name.startswith(kernel_prefix) and avg is None:
+            avg = float(r["AverageNs"]) * 1e-9
+    lines.append("")
+    if avg and alg_bytes:
+        lines.append(f"Algorithmic bytes per launch of `{kernel_prefix}`: {alg_bytes:,}; at the trace average "
+                     f"({avg * 1e6:.1f} us) {alg_bytes / avg / 1e9:.0f} GB/s ({alg_bytes / avg / 1e9 / PEAK_HBM_GBS:.1%} "
+                     f"of {PEAK_HBM_GBS:.0f} GB/s).")
+    if avg and alg_flops:
+        lines.append(f"Algorithmic flops per launch of `{kernel_prefix}`: {alg_flops:,}; at the trace average "
+                     f"({avg * 1e6:.1f} us) {alg_flops / avg / 1e12:.1f} TFLOP/s "
+                     f"({alg_flops / avg / 1e12 / PEAK_MFMA_F16_TFLOPS:.1%} of {PEAK_MFMA_F16_TFLOPS:.0f} TFLOP/s).")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,7 +262,32 @@ def main(argv=None) -> int:
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (profiler byte-counter scale)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                    help="write the HBM-traffic summary of the decode kernel from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) made with --copy-calibration-mib; no GPU is used")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
+                    help="write a kernel-trace summary from a rocprofv3 --stats file; no GPU is used")
+    ap.add_argument("--summary-kernel", default="void pa::decode_kernel<128, 4, false",
+                    help="kernel-name prefix the summaries rate")
+    ap.add_argument("--summary-title", default="")
+    ap.add_argument("--pmc-commands", nargs="*", default=[])
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        r = summarize_pmc(*args.summarize_pmc[:2], args.copy_calibration_mib or 1024, args.summary_kernel,
+                          args.summarize_pmc[2], args.pmc_commands)
+        print(json.dumps({k: r[k] for k in ("hbm_bytes_per_launch", "algorithmic_bytes_per_launch",
+                                             "traffic_over_algorithmic", "source_hash")}))
+        return 0
+    if args.summarize_trace:
+        import synthetic
+        w = synthetic.CONFIGS[args.workload]()
+        L, Q = _step_lengths(w, 1 if args.workload == 2 else 0)
+        vb, mf, _ = work_split(w, L, Q)
+        mfma = "prefill" in args.summary_kernel
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.summarize_trace[2],
+                        args.summary_title or f"{args.summary_kernel}: kernel trace",
+                        0 if mfma else vb, mf if mfma else 0, args.summary_kernel)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)

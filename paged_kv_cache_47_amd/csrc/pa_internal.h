@@ -137,4 +137,14 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ int clamp_block(int b, int nb) { return (unsigned)b < (unsigned)nb ? b : 0; }
 
+// bytes b0 b1 of a dword of int8 codes -> exact fp16 pair, via 0x64XX = 1024 + XX
+__device__ __forceinline__ void i8x4_to_h2(uint32_t w, half2_t& lo, half2_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;  // biased: XX = code + 128
+  const uint32_t l = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t h = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const half2_t bias = {(half_t)1152.0f, (half_t)1152.0f};
+  lo = __builtin_bit_cast(half2_t, l) - bias;
+  hi = __builtin_bit_cast(half2_t, h) - bias;
+}
+
 }  // namespace pa

@@ -1,0 +1,346 @@
+// Paged attention, MFMA path (prefill and chunked prefill), for gfx950.
+//
+// What is computed ([pytorch] "Compute reference attention without hiding
+// the layout"): for each query row, scores q.k * scale over the keys it may
+// see, softmax, weighted sum of V; KV head = query head / group.  The block
+// table is walked inside the kernel, so no contiguous K/V copy is made
+// ([pytorch] "Map the PyTorch design to vLLM PagedAttention").  Query row t of
+// a sequence with q_len rows and kv_len keys sits at position
+// kv_len - q_len + t and sees keys 0 .. that position ([engine] "03
+// Correctness, and the bugs a real model found").  int8 blocks are
+// dequantised before the two products ([engine] "INT8 KV cache design").
+//
+// Sequences with q_len * G >= 16 rows take this path: 128 query rows per
+// workgroup (4 waves x 32), 64 keys per step, S^T = K Q^T and O^T = V^T P^T
+// on v_mfma_f32_16x16x32_f16.  Computing the transposes makes each lane own
+// one query row in both accumulators, and the P accumulator already sits in
+// the B-operand layout of the second product.  V is staged in LDS and read
+// with the gfx950 transposing LDS read.
+#include "pa_internal.h"
+
+namespace pa {
+
+// ============================================================== MFMA path ===
+// One workgroup = 4 waves = 128 query rows of one (sequence, KV head); each
+// wave owns 32 rows as two 16-row MFMA blocks, so every K or V operand read
+// from LDS feeds two MFMAs.  Keys advance 64 at a time (four 16-key blocks):
+// the next 64-key K and V tiles are loaded from HBM into registers while the
+// current tiles in LDS are used, then written to the other LDS buffer; one
+// barrier per step.
+constexpr int kMfmaWaves = 4;
+constexpr int kMfmaBN = 64;
+#ifndef PA_PF_PADK
+#define PA_PF_PADK 16  // K tile row padding (halves)
+#endif
+#ifndef PA_PF_PADV
+#define PA_PF_PADV 16  // V tile row padding (halves)
+#endif
+#ifndef PA_PF_WSWAP
+#define PA_PF_WSWAP 0  // int8 tiles: stagger the order of each thread's two LDS stores
+#endif
+// Lazy-rescale threshold of the MFMA path (log2 units): weights stay below
+// 2^6, so an int8 weight times its V scale (at most 65504 / 127) stays finite in fp16.
+constexpr float kRescalePf = 6.0f;
+
+template <int D, int G, bool I8>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;        // k-steps of 32 over the head dim
+  constexpr int NT = D / 16;        // 16-wide output column tiles
+  constexpr int BN = kMfmaBN;       // keys per step
+  constexpr int KB = BN / 16;       // 16-key blocks per step
+  constexpr int RB = 2;             // 16-row MFMA blocks per wave
+  constexpr int LDK = D + PA_PF_PADK;  // LDS row strides (halves) of the K and V tiles
+  constexpr int LDV = D + PA_PF_PADV;
+  constexpr int EB = I8 ? 1 : 2;
+  constexpr int CPR = D * EB / 16;  // 16-byte chunks per key row in the pool
+  constexpr int PT = BN * CPR / 256;  // chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) half_t ldk[2][BN * LDK];  // [buffer]
+  __shared__ __attribute__((aligned(16))) half_t ldv[2][BN * LDV];
+
+  const int id = blockIdx.x;
+  const int h = id % a.hkv;         // consecutive workgroups = consecutive KV heads (one XCD each when hkv = 8)
+  const int2 mu = a.munit[id / a.hkv];
+  if (mu.x < 0) return;
+  const SeqInfo si = a.seqs[mu.x];
+  const int L = si.kv_len, Q = si.q_len, rows = Q * G;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps block indices scalar
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int r0 = mu.y * kMfmaRows;
+  const int last_row = min(rows, r0 + kMfmaRows) - 1;
+  const int kmax = min(L, L - Q + last_row / G + 1);
+  const int32_t* tbl = a.block_tables + (int64_t)mu.x * a.max_blocks;
+  const int qmin = L - Q + (r0 + wave * 32) / G;  // query position of this wave's first row
+
+  int qpos[RB];
+  int64_t orow[RB];
+  bool rvalid[RB];
+  half8_t qop[RB][KS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = r0 + wave * 32 + rb * 16 + l16;
+    rvalid[rb] = row < rows;
+    const int tq = rvalid[rb] ? row / G : 0;
+    qpos[rb] = rvalid[rb] ? L - Q + tq : -1;
+    orow[rb] = ((int64_t)(si.q_start + tq) * a.hq + (int64_t)h * G + row % G) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[rb][ks] = rvalid[rb] ? *(const half8_t*)(a.q + orow[rb] + ks * 32 + 8 * grp) : (half8_t)(half_t)0.f;
+  }
+
+  float4_t o[RB][NT];
+  float m[RB], lsum[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegBig;
+    lsum[rb] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[rb][nt] = (float4_t)0.f;
+  }
+
+  uint4 stk[PT], stv[PT];
+  float nks[KB], nvs[KB];  // int8: K and V scales of the 16-key blocks of the tiles in flight
+  // Physical blocks, read one step before the tiles they address: per 16-key
+  // block of the step (int8: for its scales), and per staging chunk of this
+  // wave (its 64 lanes cover 64 / CPR <= 16 aligned keys, one 16-key block).
+  // Blocks past the sequence repeat its last block (always inside the table
+  // row); no key of theirs is loaded, and their scores are masked.  The reads
+  // go through the vector memory path (vz is a zero the compiler cannot prove
+  // uniform): scalar loads share a counter with LDS reads, so every LDS read
+  // of the step would wait for them.
+  const int last_blk = (L - 1) / kBlockSize;   // L >= q_len >= 1 for a row tile
+  const int vz = lane & (a.hkv >> 30);          // 0 (hkv is small and positive)
+  struct Blocks {
+    int kb[KB];
+    int chunk[PT];
+  };
+  auto table = [&](int kt, Blocks& t) {
+    if constexpr (I8) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) t.kb[kb] = tbl[min(kt / kBlockSize + kb, last_blk) + vz];
+    }
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int key0 = (64 * wave + 256 * i) / CPR;
+      t.chunk[i] = tbl[min((kt + key0) / kBlockSize, last_blk) + vz];
+    }
+  };
+  auto gload = [&](int kt, const Blocks& t) {
+    if constexpr (I8) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int64_t sidx = (int64_t)clamp_block(t.kb[kb], a.num_blocks) * a.hkv + h;
+        nks[kb] = (float)a.ks[sidx];
+        nvs[kb] = (float)a.vs[sidx];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int key = c / CPR, ch = c % CPR;
+      const int kg = kt + key;
+      if (kg < L) {
+        const int ph = clamp_block(t.chunk[i], a.num_blocks);
+        const int64_t off = ((((int64_t)ph * a.hkv + h) * kBlockSize + (kg % kBlockSize)) * D) * EB + ch * 16;
+        stk[i] = *(const uint4*)((const char*)a.kc + off);
+        stv[i] = *(const uint4*)((const char*)a.vc + off);
+      } else {
+        stk[i] = make_uint4(0, 0, 0, 0);
+        stv[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int key = c / CPR, ch = c % CPR;
+      if constexpr (I8) {
+        half_t* kd = &ldk[buf][key * LDK + ch * 16];
+        half_t* vd = &ldv[buf][key * LDV + ch * 16];
+        const uint32_t kw[4] = {stk[i].x, stk[i].y, stk[i].z, stk[i].w};
+        const uint32_t vw[4] = {stv[i].x, stv[i].y, stv[i].z, stv[i].w};
+        half8_t k0, k1, v0, v1;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          half2_t a0, a1, a2, a3, b0, b1, b2, b3;
+          i8x4_to_h2(kw[2 * c2], a0, a1);
+          i8x4_to_h2(kw[2 * c2 + 1], a2, a3);
+          i8x4_to_h2(vw[2 * c2], b0, b1);
+          i8x4_to_h2(vw[2 * c2 + 1], b2, b3);
+          const half8_t kk = (half8_t){a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+          const half8_t vv = (half8_t){b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+          if (c2 == 0) { k0 = kk; v0 = vv; } else { k1 = kk; v1 = vv; }
+        }
+        if (PA_PF_WSWAP && (ch & 4)) {  // upper half of the row first: the two stores of 8 lanes hit distinct banks
+          *(half8_t*)(kd + 8) = k1;
+          *(half8_t*)(vd + 8) = v1;
+          *(half8_t*)kd = k0;
+          *(half8_t*)vd = v0;
+        } else {
+          *(half8_t*)kd = k0;
+          *(half8_t*)vd = v0;
+          *(half8_t*)(kd + 8) = k1;
+          *(half8_t*)(vd + 8) = v1;
+        }
+      } else {
+        *(uint4*)&ldk[buf][key * LDK + ch * 8] = stk[i];
+        *(uint4*)&ldv[buf][key * LDV + ch * 8] = stv[i];
+      }
+    }
+  };
+
+  Blocks tn, tn2;
+  table(0, tn);
+  gload(0, tn);
+  lstore(0);
+  table(BN, tn);
+  __syncthreads();
+  typedef __attribute__((address_space(3))) short4_t lds_short4;
+  int buf = 0;
+  // One 64-key step: S = K Q^T for the four 16-key blocks (this lane: query
+  // row l16 of each row block, keys 16*kb + 4*grp + e), the online-softmax
+  // max, then the fp16 weights and O^T += V^T P^T per 32-key half, so that the
+  // second half's vector work sits beside the first half's matrix products,
+  // and the next tiles' staging beside the second half's.
+  //
+  // Only steps that reach past this wave's first query position need the
+  // causal mask (a wave-uniform test); it sets the hidden raw scores to -inf.
+  // The max is taken on raw scores and scaled once per 16-key block (scales
+  // are positive), and the scale rides in the exponent's FMA.  The running max
+  // moves only when a score exceeds it by more than kRescalePf (log2 units),
+  // so the accumulators are rescaled rarely.
+  for (int kt = 0; kt < kmax; kt += BN, buf ^= 1) {
+    const bool more = kt + BN < kmax;
+    // score scale per 16-key block (base 2; int8 folds in the block's K scale).  A zero K scale
+    // (an all-zero block) becomes the least normal float: its scores stay 0, and -inf stays -inf.
+    float cks[KB], vscl[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      cks[kb] = I8 ? fmaxf(a.scale_log2 * nks[kb], 1.17549435e-38f) : a.scale_log2;
+      vscl[kb] = I8 ? nvs[kb] : 1.f;
+    }
+    // the staging at the end of the step is unconditional, so it can share a block with the
+    // matrix work; after the last step it rewrites the idle buffer with tiles nothing reads
+    if (more) {
+      gload(kt + BN, tn);
+      table(kt + 2 * BN, tn2);
+    }
+
+    float4_t s[RB][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[rb][kb] = (float4_t)0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const half8_t kop = *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + ks * 32 + 8 * grp];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rb][ks], s[rb][kb], 0, 0, 0);
+      }
+    }
+    if (kt + BN - 1 > qmin) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (kt + kb * 16 + 4 * grp + e > qpos[rb]) s[rb][kb][e] = -__builtin_inff();
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float mb = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const float r = fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3]));
+        mb = fmaxf(mb, r * cks[kb]);
+      }
+      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+      const bool grow = mb > m[rb] + kRescalePf;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float al = grow ? fast_exp2(m[rb] - mb) : 1.f;
+        m[rb] = grow ? mb : m[rb];
+        lsum[rb] *= al;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[rb][nt] *= al;
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      half8_t p[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kb = 2 * hh + j / 4;
+          const float w = fast_exp2(fmaf(s[rb][kb][j % 4], cks[kb], -m[rb]));
+          half_t ph;
+          if constexpr (I8) {
+            ps += w;
+            ph = (half_t)(w * vscl[kb]);
+          } else {
+            ph = (half_t)w;  // the weight the product uses is also the one summed
+            ps += (float)ph;
+          }
+          // slot j of the k-step: keys 4*grp + [0..3] of the half's first and second 16-key block
+          p[rb][j] = ph;
+        }
+        lsum[rb] += ps;   // this lane's share of the row sum; the row's four lanes are added at the end
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const half_t* p1 = &ldv[buf][(hh * 32 + 4 * grp + (l16 >> 2)) * LDV + nt * 16 + 4 * (l16 & 3)];
+        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
+        const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1 + 16 * LDV));
+        const half4_t h1 = __builtin_bit_cast(half4_t, v1), h2 = __builtin_bit_cast(half4_t, v2);
+        const half8_t vop = (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, p[rb], o[rb][nt], 0, 0, 0);
+      }
+    }
+    lstore(buf ^ 1);
+    if (more) tn = tn2;
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    lsum[rb] += __shfl_xor(lsum[rb], 16, 64);
+    lsum[rb] += __shfl_xor(lsum[rb], 32, 64);
+    if (!rvalid[rb]) continue;
+    const float inv = 1.f / lsum[rb];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      half4_t r;
+      r.x = (half_t)(o[rb][nt][0] * inv);
+      r.y = (half_t)(o[rb][nt][1] * inv);
+      r.z = (half_t)(o[rb][nt][2] * inv);
+      r.w = (half_t)(o[rb][nt][3] * inv);
+      *(half4_t*)(a.out + orow[rb] + nt * 16 + 4 * grp) = r;
+    }
+  }
+}
+
+template <int D, bool I8>
+static hipError_t prefill_g(const AttnArgs& a, int g, int n, hipStream_t s) {
+  const dim3 grid(n * a.hkv);   // workgroup id = row tile * hkv + KV head
+  switch (g) {
+    case 1: prefill_kernel<D, 1, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 2: prefill_kernel<D, 2, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 4: prefill_kernel<D, 4, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 8: prefill_kernel<D, 8, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, int group, bool i8, int n, hipStream_t s) {
+  if (head_dim == 128) return i8 ? prefill_g<128, true>(a, group, n, s) : prefill_g<128, false>(a, group, n, s);
+  return i8 ? prefill_g<64, true>(a, group, n, s) : prefill_g<64, false>(a, group, n, s);
+}
+
+}  // namespace pa
