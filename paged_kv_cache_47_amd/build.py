@@ -30,6 +30,12 @@ HIP_FLAGS = [
 ]
 
 
+# Per-file additions.  The MFMA kernel never sees a NaN score (hidden keys
+# are -inf, rows past a sequence are read from its last real row), so its
+# maxima need no NaN-quieting canonicalisation: 16 fewer VALU per 64-key step.
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -59,7 +65,8 @@ def build(debug: bool = False, verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        msg = _run([cc, *HIP_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj])
+        flags = [*HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra]
+        msg = _run([cc, *flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj])
         if verbose and msg:
             print(msg, file=sys.stderr)
         return obj

@@ -35,12 +35,8 @@ constexpr int kMfmaBN = 64;
 #ifndef PA_PF_PADV
 #define PA_PF_PADV 16  // V tile row padding (halves)
 #endif
-#ifndef PA_PF_WSWAP
-#define PA_PF_WSWAP 0  // int8 tiles: stagger the order of each thread's two LDS stores
-#endif
-// Lazy-rescale threshold of the MFMA path (log2 units): weights stay below
-// 2^6, so an int8 weight times its V scale (at most 65504 / 127) stays finite in fp16.
-constexpr float kRescalePf = 6.0f;
+// Lazy-rescale threshold of the MFMA path (log2 units): weights stay below 2^8.
+constexpr float kRescalePf = 8.0f;
 
 template <int D, int G, bool I8>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
@@ -89,25 +85,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   }
 
   float4_t o[RB][NT];
-  float m[RB], lsum[RB];
+  float m[RB];
+  float4_t lsum[RB];   // row sums of the fp16 weights, accumulated on the matrix cores (all 4 entries equal)
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m[rb] = kNegBig;
-    lsum[rb] = 0.f;
+    lsum[rb] = (float4_t)0.f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) o[rb][nt] = (float4_t)0.f;
   }
 
   uint4 stk[PT], stv[PT];
-  float nks[KB], nvs[KB];  // int8: K and V scales of the 16-key blocks of the tiles in flight
+  float nks[KB];  // int8: K scales of the four 16-key blocks of the tiles in flight
+  float nvc[PT];  // int8: V scale of the 16-key block of each of this thread's staging chunks
   // Physical blocks, read one step before the tiles they address: per 16-key
   // block of the step (int8: for its scales), and per staging chunk of this
   // wave (its 64 lanes cover 64 / CPR <= 16 aligned keys, one 16-key block).
-  // Blocks past the sequence repeat its last block (always inside the table
-  // row); no key of theirs is loaded, and their scores are masked.  The reads
-  // go through the vector memory path (vz is a zero the compiler cannot prove
-  // uniform): scalar loads share a counter with LDS reads, so every LDS read
-  // of the step would wait for them.
+  // The reads go through the vector memory path at a uniform address (vz is a
+  // zero the compiler cannot prove uniform): scalar loads share a counter with
+  // LDS reads, so every LDS read of the step would wait for them.  The values
+  // are made scalar again when used.
   const int last_blk = (L - 1) / kBlockSize;   // L >= q_len >= 1 for a row tile
   const int vz = lane & (a.hkv >> 30);          // 0 (hkv is small and positive)
   struct Blocks {
@@ -117,50 +114,57 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   auto table = [&](int kt, Blocks& t) {
     if constexpr (I8) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) t.kb[kb] = tbl[min(kt / kBlockSize + kb, last_blk) + vz];
+      for (int kb = 0; kb < KB; ++kb) t.kb[kb] = (tbl + min(kt / kBlockSize + kb, last_blk))[vz];
     }
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int key0 = (64 * wave + 256 * i) / CPR;
-      t.chunk[i] = tbl[min((kt + key0) / kBlockSize, last_blk) + vz];
+      t.chunk[i] = (tbl + min((kt + key0) / kBlockSize, last_blk))[vz];
     }
   };
+  // Keys past the sequence are read from its last key instead (a real,
+  // finite row): their scores are masked to -inf and their weights are 0, so
+  // no stale slot is read and no zero fill is needed.  Per lane only a 32-bit
+  // offset inside the (block, head) tile varies; the tile base is scalar.
+  constexpr int64_t kTileBytes = (int64_t)kBlockSize * D * EB;
   auto gload = [&](int kt, const Blocks& t) {
     if constexpr (I8) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int64_t sidx = (int64_t)clamp_block(t.kb[kb], a.num_blocks) * a.hkv + h;
-        nks[kb] = (float)a.ks[sidx];
-        nvs[kb] = (float)a.vs[sidx];
+        const int64_t sidx =
+            (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.kb[kb]), a.num_blocks) * a.hkv + h;
+        nks[kb] = (float)(a.ks + sidx)[vz];
       }
     }
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int c = threadIdx.x + 256 * i;
       const int key = c / CPR, ch = c % CPR;
-      const int kg = kt + key;
-      if (kg < L) {
-        const int ph = clamp_block(t.chunk[i], a.num_blocks);
-        const int64_t off = ((((int64_t)ph * a.hkv + h) * kBlockSize + (kg % kBlockSize)) * D) * EB + ch * 16;
-        stk[i] = *(const uint4*)((const char*)a.kc + off);
-        stv[i] = *(const uint4*)((const char*)a.vc + off);
-      } else {
-        stk[i] = make_uint4(0, 0, 0, 0);
-        stv[i] = make_uint4(0, 0, 0, 0);
-      }
+      const int kg = min(kt + key, L - 1);
+      const int64_t tile = (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.chunk[i]), a.num_blocks) * a.hkv + h;
+      if constexpr (I8) nvc[i] = (float)(a.vs + tile)[vz];
+      const uint32_t off = (uint32_t)((kg % kBlockSize) * D * EB + ch * 16);
+      stk[i] = *(const uint4*)((const char*)a.kc + tile * kTileBytes + off);
+      stv[i] = *(const uint4*)((const char*)a.vc + tile * kTileBytes + off);
     }
   };
+  // int8 tiles become fp16: K as exact codes (its scale multiplies the
+  // scores), V as code * (scale / 2) of its 16-key block, rounded to fp16, so
+  // the weights that multiply V are the plain softmax weights.  The half keeps
+  // 127 * scale finite (scale <= 65504 / 127 rounds up to 516); the output
+  // takes the factor 2 back.
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int c = threadIdx.x + 256 * i;
       const int key = c / CPR, ch = c % CPR;
       if constexpr (I8) {
+        const half_t vh = (half_t)(0.5f * nvc[i]);
+        const half2_t vs2 = {vh, vh};
         half_t* kd = &ldk[buf][key * LDK + ch * 16];
         half_t* vd = &ldv[buf][key * LDV + ch * 16];
         const uint32_t kw[4] = {stk[i].x, stk[i].y, stk[i].z, stk[i].w};
         const uint32_t vw[4] = {stv[i].x, stv[i].y, stv[i].z, stv[i].w};
-        half8_t k0, k1, v0, v1;
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           half2_t a0, a1, a2, a3, b0, b1, b2, b3;
@@ -168,20 +172,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
           i8x4_to_h2(kw[2 * c2 + 1], a2, a3);
           i8x4_to_h2(vw[2 * c2], b0, b1);
           i8x4_to_h2(vw[2 * c2 + 1], b2, b3);
-          const half8_t kk = (half8_t){a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
-          const half8_t vv = (half8_t){b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
-          if (c2 == 0) { k0 = kk; v0 = vv; } else { k1 = kk; v1 = vv; }
-        }
-        if (PA_PF_WSWAP && (ch & 4)) {  // upper half of the row first: the two stores of 8 lanes hit distinct banks
-          *(half8_t*)(kd + 8) = k1;
-          *(half8_t*)(vd + 8) = v1;
-          *(half8_t*)kd = k0;
-          *(half8_t*)vd = v0;
-        } else {
-          *(half8_t*)kd = k0;
-          *(half8_t*)vd = v0;
-          *(half8_t*)(kd + 8) = k1;
-          *(half8_t*)(vd + 8) = v1;
+          b0 *= vs2;
+          b1 *= vs2;
+          b2 *= vs2;
+          b3 *= vs2;
+          *(half8_t*)(kd + 8 * c2) = (half8_t){a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+          *(half8_t*)(vd + 8 * c2) = (half8_t){b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
         }
       } else {
         *(uint4*)&ldk[buf][key * LDK + ch * 8] = stk[i];
@@ -198,6 +194,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   __syncthreads();
   typedef __attribute__((address_space(3))) short4_t lds_short4;
   int buf = 0;
+  const half8_t kOnes8 = (half8_t)(half_t)1.0f;
+
   // One 64-key step: S = K Q^T for the four 16-key blocks (this lane: query
   // row l16 of each row block, keys 16*kb + 4*grp + e), the online-softmax
   // max, then the fp16 weights and O^T += V^T P^T per 32-key half, so that the
@@ -214,12 +212,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
     const bool more = kt + BN < kmax;
     // score scale per 16-key block (base 2; int8 folds in the block's K scale).  A zero K scale
     // (an all-zero block) becomes the least normal float: its scores stay 0, and -inf stays -inf.
-    float cks[KB], vscl[KB];
+    float cks[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      cks[kb] = I8 ? fmaxf(a.scale_log2 * nks[kb], 1.17549435e-38f) : a.scale_log2;
-      vscl[kb] = I8 ? nvs[kb] : 1.f;
-    }
+    for (int kb = 0; kb < KB; ++kb) cks[kb] = I8 ? fmaxf(a.scale_log2 * nks[kb], 1.17549435e-38f) : a.scale_log2;
     // the staging at the end of the step is unconditional, so it can share a block with the
     // matrix work; after the last step it rewrites the idle buffer with tiles nothing reads
     if (more) {
@@ -249,6 +244,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
           for (int e = 0; e < 4; ++e)
             if (kt + kb * 16 + 4 * grp + e > qpos[rb]) s[rb][kb][e] = -__builtin_inff();
     }
+    // Each lane tests its own 16 scores against its row's running max; only
+    // when some score of the wave exceeds it by more than kRescalePf are the
+    // row maxima formed across the row's four lanes and the rows rescaled.
+    float mloc[RB];
+    bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float mb = -__builtin_inff();
@@ -257,12 +257,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
         const float r = fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3]));
         mb = fmaxf(mb, r * cks[kb]);
       }
-      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      const bool grow = mb > m[rb] + kRescalePf;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float al = grow ? fast_exp2(m[rb] - mb) : 1.f;
-        m[rb] = grow ? mb : m[rb];
+      mloc[rb] = mb;
+      grow |= mb > m[rb] + kRescalePf;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mb = fmaxf(mloc[rb], __shfl_xor(mloc[rb], 16, 64));
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const bool g = mb > m[rb] + kRescalePf;   // the same for the row's four lanes
+        const float al = g ? fast_exp2(m[rb] - mb) : 1.f;
+        m[rb] = g ? mb : m[rb];
         lsum[rb] *= al;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) o[rb][nt] *= al;
@@ -273,23 +278,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
       half8_t p[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float ps = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int kb = 2 * hh + j / 4;
-          const float w = fast_exp2(fmaf(s[rb][kb][j % 4], cks[kb], -m[rb]));
-          half_t ph;
-          if constexpr (I8) {
-            ps += w;
-            ph = (half_t)(w * vscl[kb]);
-          } else {
-            ph = (half_t)w;  // the weight the product uses is also the one summed
-            ps += (float)ph;
-          }
           // slot j of the k-step: keys 4*grp + [0..3] of the half's first and second 16-key block
-          p[rb][j] = ph;
+          const int kb = 2 * hh + j / 4;
+          p[rb][j] = (half_t)fast_exp2(fmaf(s[rb][kb][j % 4], cks[kb], -m[rb]));
         }
-        lsum[rb] += ps;   // this lane's share of the row sum; the row's four lanes are added at the end
+        // row sums of exactly the weights the product uses: ones^T P^T on the matrix cores
+        lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kOnes8, p[rb], lsum[rb], 0, 0, 0);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -309,10 +305,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    lsum[rb] += __shfl_xor(lsum[rb], 16, 64);
-    lsum[rb] += __shfl_xor(lsum[rb], 32, 64);
     if (!rvalid[rb]) continue;
-    const float inv = 1.f / lsum[rb];
+    const float inv = (I8 ? 2.f : 1.f) / lsum[rb][0];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       half4_t r;
