@@ -10,8 +10,8 @@
 // Correctness, and the bugs a real model found").  int8 blocks are
 // dequantised before the two products ([engine] "INT8 KV cache design").
 //
-// Sequences with q_len * G >= 16 rows take this path: 128 query rows per
-// workgroup (4 waves x 32), 64 keys per step, S^T = K Q^T and O^T = V^T P^T
+// Sequences with q_len * G >= 16 rows take this path: kMfmaRows query rows
+// per workgroup (kMfmaWaves waves x 32), 64 keys per step, S^T = K Q^T and O^T = V^T P^T
 // on v_mfma_f32_16x16x32_f16.  Computing the transposes makes each lane own
 // one query row in both accumulators, and the P accumulator already sits in
 // the B-operand layout of the second product.  V is staged in LDS and read
@@ -21,14 +21,17 @@
 namespace pa {
 
 // ============================================================== MFMA path ===
-// One workgroup = 4 waves = 128 query rows of one (sequence, KV head); each
-// wave owns 32 rows as two 16-row MFMA blocks, so every K or V operand read
-// from LDS feeds two MFMAs.  Keys advance 64 at a time (four 16-key blocks):
-// the next 64-key K and V tiles are loaded from HBM into registers while the
-// current tiles in LDS are used, then written to the other LDS buffer; one
-// barrier per step.
-constexpr int kMfmaWaves = 4;
+// One workgroup = kMfmaWaves waves = kMfmaRows query rows of one (sequence,
+// KV head); each wave owns 32 rows as two 16-row MFMA blocks, so every K or V
+// operand read from LDS feeds two MFMAs.  Keys advance 64 at a time (four
+// 16-key blocks): the next 64-key K and V tiles are loaded from HBM into
+// registers while the current tiles in LDS are used, then written to the
+// other LDS buffer; one barrier per step.  The more waves share a tile, the
+// less staging (loads, int8 conversion, LDS stores) each wave does per step.
 constexpr int kMfmaBN = 64;
+#ifndef PA_PF_PRIO
+#define PA_PF_PRIO 0   // 1: raise the wave's issue priority over the S = K Q^T products
+#endif
 #ifndef PA_PF_PADK
 #define PA_PF_PADK 16  // K tile row padding (halves)
 #endif
@@ -39,7 +42,7 @@ constexpr int kMfmaBN = 64;
 constexpr float kRescalePf = 8.0f;
 
 template <int D, int G, bool I8>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kernel(AttnArgs a) {
   constexpr int KS = D / 32;        // k-steps of 32 over the head dim
   constexpr int NT = D / 16;        // 16-wide output column tiles
   constexpr int BN = kMfmaBN;       // keys per step
@@ -49,7 +52,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   constexpr int LDV = D + PA_PF_PADV;
   constexpr int EB = I8 ? 1 : 2;
   constexpr int CPR = D * EB / 16;  // 16-byte chunks per key row in the pool
-  constexpr int PT = BN * CPR / 256;  // chunks per thread per tile
+  constexpr int NTH = 64 * kMfmaWaves;
+  constexpr int NCH = BN * CPR;                    // 16-byte chunks per tile
+  constexpr int PT = NCH >= NTH ? NCH / NTH : 1;   // chunks per thread per tile
+  static_assert(NCH % NTH == 0 || NTH % NCH == 0, "chunks must tile the workgroup");
   __shared__ __attribute__((aligned(16))) half_t ldk[2][BN * LDK];  // [buffer]
   __shared__ __attribute__((aligned(16))) half_t ldv[2][BN * LDV];
 
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      const int key0 = (64 * wave + 256 * i) / CPR;
+      const int key0 = ((64 * wave + NTH * i) % NCH) / CPR;
       t.chunk[i] = (tbl + min((kt + key0) / kBlockSize, last_blk))[vz];
     }
   };
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = (threadIdx.x + NTH * i) % NCH;   // threads past the chunks repeat the first ones
       const int key = c / CPR, ch = c % CPR;
       const int kg = min(kt + key, L - 1);
       const int64_t tile = (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.chunk[i]), a.num_blocks) * a.hkv + h;
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = (threadIdx.x + NTH * i) % NCH;   // threads past the chunks repeat the first ones
       const int key = c / CPR, ch = c % CPR;
       if constexpr (I8) {
         const half_t vh = (half_t)(0.5f * nvc[i]);
@@ -222,18 +228,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
       table(kt + 2 * BN, tn2);
     }
 
+    // S^T = K Q^T, k-step outer so the eight accumulators interleave, with the
+    // next k-step's four K operands read from LDS while this one's products run
     float4_t s[RB][KB];
+    half8_t kq[2][KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) kq[0][kb] = *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + 8 * grp];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s[rb][kb] = (float4_t)0.f;
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const half8_t kop = *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + ks * 32 + 8 * grp];
+        for (int kb = 0; kb < KB; ++kb)
+          kq[(ks + 1) & 1][kb] = *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + (ks + 1) * 32 + 8 * grp];
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rb][ks], s[rb][kb], 0, 0, 0);
-      }
+          s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kq[ks & 1][kb], qop[rb][ks],
+                                                            ks == 0 ? (float4_t)0.f : s[rb][kb], 0, 0, 0);
     }
     if (kt + BN - 1 > qmin) {
 #pragma unroll
@@ -275,6 +288,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
+      // this half's V operands (transposing LDS reads) are requested before its weights are formed
+      half8_t vq[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const half_t* p1 = &ldv[buf][(hh * 32 + 4 * grp + (l16 >> 2)) * LDV + nt * 16 + 4 * (l16 & 3)];
+        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
+        const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1 + 16 * LDV));
+        const half4_t h1 = __builtin_bit_cast(half4_t, v1), h2 = __builtin_bit_cast(half4_t, v2);
+        vq[nt] = (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w};
+      }
       half8_t p[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -288,15 +311,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
         lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kOnes8, p[rb], lsum[rb], 0, 0, 0);
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const half_t* p1 = &ldv[buf][(hh * 32 + 4 * grp + (l16 >> 2)) * LDV + nt * 16 + 4 * (l16 & 3)];
-        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
-        const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1 + 16 * LDV));
-        const half4_t h1 = __builtin_bit_cast(half4_t, v1), h2 = __builtin_bit_cast(half4_t, v2);
-        const half8_t vop = (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w};
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, p[rb], o[rb][nt], 0, 0, 0);
-      }
+        for (int rb = 0; rb < RB; ++rb) o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vq[nt], p[rb], o[rb][nt], 0, 0, 0);
     }
     lstore(buf ^ 1);
     if (more) tn = tn2;
