@@ -3,7 +3,7 @@
 #include <climits>
 #include <cstring>
 
-#include "pa_internal.h"
+#include "mfma_tile.h"
 
 namespace pa {
 

@@ -17,11 +17,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBlockSize = 16;     // tokens per block (the only size built)
 constexpr int kWave = 64;
-#ifndef PA_PF_WAVES
-#define PA_PF_WAVES 4
-#endif
-constexpr int kMfmaWaves = PA_PF_WAVES;     // waves per MFMA workgroup, 32 query rows each
-constexpr int kMfmaRows = 32 * kMfmaWaves;  // query rows per MFMA workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
 

@@ -42,6 +42,16 @@ def test_rows_at_the_mfma_threshold():
     _check_step(_run(w), OracleSide(w), 0, ({}, {"partition_tokens": 16}))
 
 
+def test_rows_at_the_row_tile_edges():
+    # q_len * group = 127, 128, 129, 255, 256, 257, 511, 513 rows: partial, full and spilling row tiles
+    lens = [300, 300, 300, 600, 600, 600, 900, 900]
+    qls = [127, 128, 129, 255, 256, 257, 511, 513]
+    w = synthetic.custom(16, lens, qls, 2, 2, 64)
+    _check_step(_run(w), OracleSide(w), 0, ({},))
+    w = synthetic.custom(17, [1000, 700], [400, 65], 8, 2, 128, "i8")
+    _check_step(_run(w), OracleSide(w), 0, ({},))
+
+
 def test_zero_query_rows_and_empty_batch():
     from paged_kv_cache_47_amd import pa
     w = synthetic.custom(8, [5, 40, 1, 300, 17], [0, 1, 0, 20, 0], 8, 2, 128)
