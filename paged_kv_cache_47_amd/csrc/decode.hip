@@ -55,7 +55,12 @@ __device__ __forceinline__ void v_token_pairs(const Dw<N>& r0, const Dw<N>& r1, 
   }
 }
 
-constexpr float kRescale = 8.0f;
+// Lazy-rescale thresholds (log2 units): weights stay below 2^threshold.  For
+// int8 pools a weight is multiplied by its block's V scale in fp16 before the
+// product; scales reach 65504 / 127 (fp16 516), so 2^6.5 * 516 < 65504 keeps
+// that product finite.
+constexpr float kRescaleF16 = 8.0f;
+constexpr float kRescaleI8 = 6.5f;
 
 // fp16 scale at a wave-uniform index, read as the aligned dword that holds it
 // (a scalar load; 16-bit loads would go through the vector memory path).
@@ -205,6 +210,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     // The running max moves only when a score exceeds it by more than
     // kRescale (log2 units), so weights stay <= 2^kRescale and the
     // accumulators are rescaled rarely.
+    constexpr float kRescale = I8 ? kRescaleI8 : kRescaleF16;
     bool grow = false;
     float mb[G];
 #pragma unroll

@@ -126,6 +126,29 @@ def test_int8_write_special_values():
     _check_step(_run(w), OracleSide(w), 0, ({},))
 
 
+def test_int8_values_near_the_fp16_limit():
+    # V rows of +-60000 give block scales near the fp16 limit (60000 / 127 -> 472.5): the weight
+    # times V scale products of both paths must stay finite; the new keys are aligned with their
+    # queries so the decode rows also weight them heavily
+    lens, qls = [120, 100, 90, 300], [40, 1, 1, 1]   # 160 rows on the MFMA path, three decode rows
+    w = synthetic.custom(18, lens, qls, 8, 2, 128, "i8")
+    st = w.step(0)
+    st.new_v[:, :, 0::2] = np.float16(60000)
+    st.new_v[:, :, 1::2] = np.float16(-60000)
+    st.new_k[:] = (0.6 * st.q[:, ::4, :].astype(np.float32)).astype(np.float16)
+    run, ora = _run(w), OracleSide(w)
+    x = run.prepare(0)
+    slots, copies = ora.reserve(0)
+    run.write(x)
+    ora.write(0, slots, copies)
+    ref = ora.attend(0)
+    for opts in ({}, {"partition_tokens": 32}, {"mfma_min_rows": 1}):
+        got = run.attend(x, **opts).cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), opts
+        err = np.abs(got - ref)
+        assert np.all(err <= np.maximum(5e-2, 1e-2 * np.abs(ref))), (opts, float((err / np.maximum(np.abs(ref), 1)).max()))
+
+
 def test_write_skips_negative_and_out_of_range_slots():
     from paged_kv_cache_47_amd import pa
     rng = np.random.default_rng(13)
