@@ -16,7 +16,7 @@
 // one query row in both accumulators, and the P accumulator already sits in
 // the B-operand layout of the second product.  V is staged in LDS and read
 // with the gfx950 transposing LDS read.
-#include "pa_internal.h"
+#include "mfma_tile.h"
 
 namespace pa {
 
