@@ -32,26 +32,9 @@ struct Dw {
   uint32_t v[N];
 };
 
-#ifndef PA_DECODE_SDWA
-#define PA_DECODE_SDWA 1
-#endif
-// int8 codes -> exact fp16 with sub-dword operand selection: one conversion
-// per code, written straight into the low or high half of the result
-// (signed byte -> int16 -> fp16 is exact for |code| <= 127).
-template <int B0, int B1>
-__device__ __forceinline__ half2_t sdwa_pair(uint32_t lo_src, uint32_t hi_src) {
-  uint32_t r;
-  asm(
-      "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%c3\n\t"
-      "v_cvt_f16_i16_sdwa %0, sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%c4"
-      : "=&v"(r)
-      : "v"(lo_src), "v"(hi_src), "n"(B0), "n"(B1));
-  return __builtin_bit_cast(half2_t, r);
-}
-
 template <bool I8, int N>
 __device__ __forceinline__ void v_token_pairs(const Dw<N>& r0, const Dw<N>& r1, half2_t* vp) {
-  if constexpr (I8 && PA_DECODE_SDWA) {
+  if constexpr (I8 && PA_I8_SDWA) {
 #pragma unroll
     for (int c = 0; c < N; ++c) {
       vp[4 * c + 0] = sdwa_pair<0, 0>(r0.v[c], r1.v[c]);
@@ -211,7 +194,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       if constexpr (I8) {
 #pragma unroll
         for (int c = 0; c < ND; ++c) {
-          if constexpr (PA_DECODE_SDWA) {
+          if constexpr (PA_I8_SDWA) {
             kh[2 * c] = sdwa_pair<0, 1>(kr[i].v[c], kr[i].v[c]);
             kh[2 * c + 1] = sdwa_pair<2, 3>(kr[i].v[c], kr[i].v[c]);
           } else {

@@ -136,6 +136,23 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ int clamp_block(int b, int nb) { return (unsigned)b < (unsigned)nb ? b : 0; }
 
+#ifndef PA_I8_SDWA
+#define PA_I8_SDWA 1
+#endif
+// int8 codes -> exact fp16 with sub-dword operand selection: one conversion
+// per code, written straight into the low or high half of the result
+// (signed byte -> int16 -> fp16 is exact for |code| <= 127).
+template <int B0, int B1>
+__device__ __forceinline__ half2_t sdwa_pair(uint32_t lo_src, uint32_t hi_src) {
+  uint32_t r;
+  asm(
+      "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_%c3\n\t"
+      "v_cvt_f16_i16_sdwa %0, sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_%c4"
+      : "=&v"(r)
+      : "v"(lo_src), "v"(hi_src), "n"(B0), "n"(B1));
+  return __builtin_bit_cast(half2_t, r);
+}
+
 // bytes b0 b1 of a dword of int8 codes -> exact fp16 pair, via 0x64XX = 1024 + XX
 __device__ __forceinline__ void i8x4_to_h2(uint32_t w, half2_t& lo, half2_t& hi) {
   const uint32_t u = w ^ 0x80808080u;  // biased: XX = code + 128

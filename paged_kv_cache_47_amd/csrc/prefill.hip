@@ -173,11 +173,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
         const uint32_t vw[4] = {stv[i].x, stv[i].y, stv[i].z, stv[i].w};
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-          half2_t a0, a1, a2, a3, b0, b1, b2, b3;
-          i8x4_to_h2(kw[2 * c2], a0, a1);
-          i8x4_to_h2(kw[2 * c2 + 1], a2, a3);
-          i8x4_to_h2(vw[2 * c2], b0, b1);
-          i8x4_to_h2(vw[2 * c2 + 1], b2, b3);
+          const half2_t a0 = sdwa_pair<0, 1>(kw[2 * c2], kw[2 * c2]), a1 = sdwa_pair<2, 3>(kw[2 * c2], kw[2 * c2]);
+          const half2_t a2 = sdwa_pair<0, 1>(kw[2 * c2 + 1], kw[2 * c2 + 1]);
+          const half2_t a3 = sdwa_pair<2, 3>(kw[2 * c2 + 1], kw[2 * c2 + 1]);
+          half2_t b0 = sdwa_pair<0, 1>(vw[2 * c2], vw[2 * c2]), b1 = sdwa_pair<2, 3>(vw[2 * c2], vw[2 * c2]);
+          half2_t b2 = sdwa_pair<0, 1>(vw[2 * c2 + 1], vw[2 * c2 + 1]);
+          half2_t b3 = sdwa_pair<2, 3>(vw[2 * c2 + 1], vw[2 * c2 + 1]);
           b0 *= vs2;
           b1 *= vs2;
           b2 *= vs2;
