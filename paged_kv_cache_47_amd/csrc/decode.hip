@@ -32,6 +32,12 @@ struct Dw {
   uint32_t v[N];
 };
 
+__device__ __forceinline__ float dot2_first(half2_t a, half2_t b) {
+  float r;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 template <bool I8, int N>
 __device__ __forceinline__ void v_token_pairs(const Dw<N>& r0, const Dw<N>& r1, half2_t* vp) {
   if constexpr (I8 && PA_I8_SDWA) {
@@ -207,9 +213,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float d = 0.f;
+        // the first pair product starts the sum (the three-operand form takes a
+        // zero addend, so no register has to be cleared first)
+        float d = dot2_first(qh[g][0], kh[0]);
 #pragma unroll
-        for (int c = 0; c < E2; ++c) d = __builtin_amdgcn_fdot2(qh[g][c], kh[c], d, false);
+        for (int c = 1; c < E2; ++c) d = __builtin_amdgcn_fdot2(qh[g][c], kh[c], d, false);
         s[i][g] = d;
       }
     }
