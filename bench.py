@@ -132,6 +132,26 @@ def work_split(w, L, Q):
     return vec_bytes, mfma_flops, total
 
 
+def _blas_name() -> str:
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')}"
+    except Exception:   # older numpy: no dict form
+        return "unknown"
+
+
+def unique_kv_bytes(w, tables, L) -> int:
+    """KV bytes of the distinct physical blocks a step reads (a block shared
+    by several sequences counts once, with its largest valid-token count)."""
+    eb = 1 if w.kv_dtype == "i8" else 2
+    valid = {}
+    for row, n in zip(tables, L.tolist()):
+        for j in range(-(-n // w.block_size)):
+            b = int(row[j])
+            valid[b] = max(valid.get(b, 0), min(w.block_size, n - j * w.block_size))
+    return sum(valid.values()) * w.num_kv_heads * w.head_dim * 2 * eb
+
+
 def cpu_baseline(w, step: int, budget_s: float):
     """The oracle (gather through the block table + fp64 attention) on the
     first sequences of the same step, until ``budget_s`` of CPU time."""
@@ -160,7 +180,7 @@ def cpu_baseline(w, step: int, budget_s: float):
     dt = time.perf_counter() - t0
     return {
         "value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
-        "kind": "oracle",
+        "kind": "oracle", "blas": _blas_name(),
         "sample": f"first {done} of {len(st.tables)} sequences ({kv_bytes / 1e6:.1f} MB of KV), attention only "
                   f"(numpy fp64, BLAS threads={os.environ.get('OMP_NUM_THREADS', 'default')}), {dt:.1f} s"
                   + (" (on the pool as drawn: the int8 context replay is not part of the timed oracle work)"
@@ -251,6 +271,55 @@ def summarize_trace(stats_csv: str, out: str, cmd: str, title: str, alg_bytes: i
         f.write("\n".join(lines) + "\n")
 
 
+def end_to_end(args, w) -> dict:
+    """Workload 2 run as a server would: the prefill step, then every decode
+    step with its host bookkeeping (table growth, slot mapping), the copies of
+    its metadata and new rows to the device, the KV write and the attention.
+    Wall time over all steps (host included) and device time per step."""
+    import torch
+    from paged_kv_cache_47_amd.workload import DeviceRun
+    run = DeviceRun(w)
+    acts = [run.activations(s) for s in range(w.num_steps)]   # the model's outputs, already on the device
+    # the set-up above leaves the GPU idle long enough to drop its clocks: bring them back with ~0.2 s
+    # of unrelated device work before timing
+    a_ = torch.randn(4096, 4096, device="cuda", dtype=torch.float16)
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.2:
+        a_ = a_ @ a_
+        a_ = a_ / a_.abs().amax()
+        torch.cuda.synchronize()
+    del a_
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.num_steps)]
+    for a_, b_ in ev:
+        a_.record()
+        b_.record()
+    torch.cuda.synchronize()
+    x = run.prepare(0, acts=acts[0])
+    ev[0][0].record()
+    run.run(x)
+    ev[0][1].record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(1, w.num_steps):
+        x = run.prepare(s, acts=acts[s])
+        ev[s][0].record()
+        run.run(x)
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev = [a_.elapsed_time(b_) for a_, b_ in ev]
+    seqs = len(run.ids)
+    dec = w.num_steps - 1
+    return {"prefill_ms": round(dev[0], 5), "decode_steps": dec, "seq_steps": seqs * dec,
+            "wall_s_decode_steps": round(wall, 5),
+            "seq_steps_per_s_wall": round(seqs * dec / wall, 1),
+            "seq_steps_per_s_device": round(seqs * dec / (sum(dev[1:]) * 1e-3), 1),
+            "note": "wall: host bookkeeping + metadata H2D + write + attend of every decode step "
+                    "(new K/V and queries already on the device); "
+                    "device: the write + attend events of each decode step; prefill: the first step's events"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +329,11 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--cold", type=int, default=-1, choices=(-1, 0, 1),
+                    help="also time steps after a 1 GiB scratch write that evicts the 256 MB MALL "
+                         "(default: for working sets under 512 MB, workloads 1, 2 and 4)")
+    ap.add_argument("--no-share", action="store_true",
+                    help="workload 4 control: every sequence owns its own copy of the prefix (no sharing, no forks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (profiler byte-counter scale)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
@@ -299,7 +373,7 @@ def main(argv=None) -> int:
     from paged_kv_cache_47_amd.workload import DeviceRun
 
     torch.cuda.set_device(0)
-    w = synthetic.CONFIGS[args.workload]()
+    w = synthetic.config4(share=False) if (args.workload == 4 and args.no_share) else synthetic.CONFIGS[args.workload]()
     run = DeviceRun(w)
     step_index = 0
     if args.workload == 2:            # prefill (step 0) first; the timed step is the first decode step
@@ -347,6 +421,7 @@ def main(argv=None) -> int:
         step(i)
     ms = timed(range(args.warmup, n), True)          # the timed region
     ms_plain = timed(range(args.warmup, n), False)   # the same steps without the kernel events
+    e2e = end_to_end(args, w) if args.workload == 2 else None
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -357,21 +432,51 @@ def main(argv=None) -> int:
 
     roof = []
     if vec_bytes:
-        k_ms = float(np.mean([evs.elapsed_ms(4 * i, 4 * i + 1) for i in range(args.warmup, n)]))
+        k_all = [evs.elapsed_ms(4 * i, 4 * i + 1) for i in range(args.warmup, n)]
+        k_ms = float(np.mean(k_all))
         ach = vec_bytes / (k_ms * 1e-3) / 1e9
         roof.append({"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(ach / PEAK_HBM_GBS, 4),
                      "traffic": traffic_from_profile() if args.workload == 3 and not args.partition_tokens else None,
                      "kernel": "decode_kernel (split-K vector path)", "kernel_ms": round(k_ms, 5),
+                     "kernel_ms_median": round(float(np.median(k_all)), 5),
                      "algorithmic_bytes_per_launch": vec_bytes})
     if mfma_flops:
-        k_ms = float(np.mean([evs.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(args.warmup, n)]))
+        k_all = [evs.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(args.warmup, n)]
+        k_ms = float(np.mean(k_all))
         ach = mfma_flops / (k_ms * 1e-3) / 1e12
         roof.append({"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None,
                      "kernel": "prefill_kernel (MFMA path, fp16 16x16x32)", "kernel_ms": round(k_ms, 5),
+                     "kernel_ms_median": round(float(np.median(k_all)), 5),
                      "algorithmic_flops_per_launch": mfma_flops})
     roof.sort(key=lambda r: -r["kernel_ms"])       # the dominant kernel first
+    # cold steps last: they re-record the per-step kernel events read above
+    cold = None
+    if args.cold == 1 or (args.cold == -1 and args.workload in (1, 2, 4)):
+        # each step after a 1 GiB scratch write (more than the 256 MB MALL): the step's own
+        # device time from events right around it, the kernels' from the library's events
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a_, b_ in ce:
+            a_.record()
+            b_.record()
+        torch.cuda.synchronize()
+        for j, i in enumerate(range(args.warmup, n)):
+            scratch.fill_(j & 0xff)
+            ce[j][0].record()
+            step(i)
+            ce[j][1].record()
+        torch.cuda.synchronize()
+        st_ms = [a_.elapsed_time(b_) for a_, b_ in ce]
+        cold = {"ms_per_step_median": round(float(np.median(st_ms)), 5),
+                "value_median": round(kv_bytes / (float(np.median(st_ms)) * 1e-3) / 1e9, 2),
+                "note": "each step after a 1 GiB scratch write evicting the MALL; median over the timed steps"}
+        if vec_bytes:
+            kc = float(np.median([evs.elapsed_ms(4 * i, 4 * i + 1) for i in range(args.warmup, n)]))
+            cold.update({"decode_kernel_ms_median": round(kc, 5),
+                         "decode_kernel_gbs": round(vec_bytes / (kc * 1e-3) / 1e9, 2)})
+        del scratch
     res = {
         "metric": "paged decode attn: achieved KV-read HBM GB/s (% of peak); seq-steps/s",
         "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
@@ -385,7 +490,9 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "i8" if w.kv_dtype == "i8" else "f16",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload], "num_seqs": S, "kv_tokens": int(L.sum()),
+        "config": {"workload": WORKLOADS[args.workload] + (" [control: every sequence owns its prefix copy]"
+                                                          if args.workload == 4 and args.no_share else ""),
+                   "num_seqs": S, "kv_tokens": int(L.sum()),
                    "query_rows": int(Q.sum()), "num_blocks": w.num_blocks,
                    "partition_tokens": args.partition_tokens},
         "pct_of_peak": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
@@ -397,6 +504,16 @@ def main(argv=None) -> int:
     }
     if len(roof) > 1:
         res["roofline_other"] = roof[1:]
+    if cold is not None:
+        res["cold"] = cold
+    if e2e is not None:
+        res["end_to_end"] = e2e
+    if args.workload == 4:
+        ub = unique_kv_bytes(w, x.batch.block_tables, L)
+        res["unique_kv_bytes_per_step"] = ub
+        res["value_unique"] = round(ub / (ms * 1e-3) / 1e9, 2)
+        res["pct_of_peak"] = round(100 * ub / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)   # of unique bytes
+        res["config"]["shared_prefix"] = not args.no_share
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, step_index, args.cpu_budget)
     print(json.dumps(res), flush=True)

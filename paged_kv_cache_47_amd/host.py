@@ -49,7 +49,7 @@ class BlockAllocator:
             raise ValueError("first_pops must be a permutation of range(num_blocks)")
         # the stack's top is the end of the list: reverse so successive pops follow `order`
         self._free: List[int] = order[::-1].tolist()
-        self._refs = np.zeros(num_blocks, np.int64)
+        self._refs: List[int] = [0] * self.num_blocks   # a list: per-token scalar lookups stay cheap
 
     @property
     def num_free(self) -> int:
@@ -75,7 +75,7 @@ class BlockAllocator:
         return 0 <= b < self.num_blocks and self._refs[b] > 0
 
     def refcount(self, b: int) -> int:
-        return int(self._refs[b])
+        return self._refs[b]
 
     def retain(self, b: int) -> None:
         if not self.is_allocated(b):
@@ -105,7 +105,7 @@ class BlockAllocator:
             self.free(b)
 
     def allocated_ids(self) -> np.ndarray:
-        return np.nonzero(self._refs)[0]
+        return np.nonzero(np.asarray(self._refs))[0]
 
     def free_ids(self) -> List[int]:
         return list(self._free)
@@ -136,6 +136,9 @@ class PagedKVManager:
         self.block_size = int(block_size)
         self.alloc = BlockAllocator(num_blocks, first_pops)
         self._seqs: List[_Seq] = []
+        self._tab = None          # last block-table array built, its sequence list and row contents
+        self._tab_ids: List[int] = []
+        self._tab_rows: List[tuple] = []
 
     # -- sequences --------------------------------------------------------
     def add_sequence(self, num_tokens: int = 0, shared_from: Optional[int] = None, shared_tokens: int = 0) -> int:
@@ -186,23 +189,25 @@ class PagedKVManager:
         return (bl[pos // self.block_size] * self.block_size + pos % self.block_size).astype(np.int32)
 
     # -- writes -----------------------------------------------------------
-    def append(self, sid: int, n: int):
-        """Reserve the next ``n`` positions of ``sid``: returns (slots, copy_pairs)."""
+    def append(self, sid: int, n: int, slots: Optional[list] = None, copies: Optional[list] = None):
+        """Reserve the next ``n`` positions of ``sid``: returns (slots, copy_pairs)
+        (appended to the given lists when passed)."""
         s = self._seqs[sid]
         bs = self.block_size
-        slots, copies = [], []
+        blocks, refs, alloc = s.blocks, self.alloc._refs, self.alloc
+        slots = [] if slots is None else slots
+        copies = [] if copies is None else copies
         for pos in range(s.length, s.length + int(n)):
             idx, off = divmod(pos, bs)
-            if idx == len(s.blocks):
-                s.blocks.append(self.alloc.allocate())
-            else:
-                b = s.blocks[idx]
-                if self.alloc.refcount(b) > 1:       # shared: copy before the first divergent write
-                    nb = self.alloc.allocate()
-                    copies.append((b, nb))
-                    self.alloc.release(b)
-                    s.blocks[idx] = nb
-            slots.append(s.blocks[idx] * bs + off)
+            if idx == len(blocks):
+                blocks.append(alloc.allocate())
+            elif refs[blocks[idx]] > 1:              # shared: copy before the first divergent write
+                b = blocks[idx]
+                nb = alloc.allocate()
+                copies.append((b, nb))
+                alloc.release(b)
+                blocks[idx] = nb
+            slots.append(blocks[idx] * bs + off)
         s.length += int(n)
         return slots, copies
 
@@ -212,9 +217,7 @@ class PagedKVManager:
         slots: List[int] = []
         copies: List[tuple] = []
         for sid, n in zip(seq_ids, q_lens):
-            sl, cp = self.append(sid, n)
-            slots += sl
-            copies += cp
+            self.append(sid, n, slots, copies)
         return StepBatch(
             seq_ids=list(seq_ids),
             slot_mapping=np.asarray(slots, np.int32),
@@ -225,12 +228,25 @@ class PagedKVManager:
         )
 
     def block_tables(self, seq_ids: Sequence[int], width: Optional[int] = None) -> np.ndarray:
-        need = max([len(self._seqs[s].blocks) for s in seq_ids] + [1])
+        """[S, width] int32 tables (zero past each sequence's blocks).  Rows that
+        did not change since the last call for the same sequences and width
+        are taken from that call's array."""
+        seqs = self._seqs
+        rows = [tuple(seqs[s].blocks) for s in seq_ids]
+        need = max([len(r) for r in rows] + [1])
         width = need if width is None else int(width)
         if width < need:
             raise ValueError(f"table width {width} < {need} blocks")
-        out = np.zeros((len(seq_ids), width), np.int32)
-        for r, s in enumerate(seq_ids):
-            bl = self._seqs[s].blocks
-            out[r, : len(bl)] = bl
+        prev = self._tab
+        if prev is not None and prev.shape == (len(rows), width) and self._tab_ids == list(seq_ids):
+            out = prev.copy()
+            for r, (new, old) in enumerate(zip(rows, self._tab_rows)):
+                if new != old:
+                    out[r, :] = 0
+                    out[r, : len(new)] = new
+        else:
+            out = np.zeros((len(rows), width), np.int32)
+            for r, bl in enumerate(rows):
+                out[r, : len(bl)] = bl
+        self._tab, self._tab_ids, self._tab_rows = out, list(seq_ids), rows
         return out

@@ -66,6 +66,38 @@ class DeviceRun:
         self.v_scale = torch.from_numpy(w.pool_v_scale).to(self.device) if self.i8 else None
         if w.context is not None:
             self._write_context(context_batch_tokens)
+        self._pinned = [None, None]   # two pinned staging buffers for step metadata, used in turn
+        self._copied = [None, None]   # event after the last copy out of each
+        self._turn = 0
+        self._ws = None               # attention workspace, grown as needed
+
+    def _upload_i32(self, arrays) -> list:
+        """The step's int32 metadata arrays packed into one pinned host buffer
+        and copied to the device in one asynchronous transfer on the current
+        stream; returns device views shaped like the inputs.  The device
+        buffer is fresh each step, so earlier steps' views stay valid."""
+        flat = [np.ascontiguousarray(a, dtype=np.int32).reshape(-1) for a in arrays]
+        n = max(1, sum(a.size for a in flat))
+        t = self._turn = self._turn ^ 1
+        if self._copied[t] is not None:
+            self._copied[t].synchronize()          # the copy that last read this buffer is done
+        if self._pinned[t] is None or self._pinned[t].numel() < n:
+            self._pinned[t] = torch.empty(2 * n, dtype=torch.int32, pin_memory=True)
+        host = self._pinned[t].numpy()
+        off = 0
+        for a in flat:
+            host[off:off + a.size] = a
+            off += a.size
+        dev = torch.empty(n, dtype=torch.int32, device=self.device)
+        dev.copy_(self._pinned[t][:n], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._copied[t] = ev
+        out, off = [], 0
+        for a, f in zip(arrays, flat):
+            out.append(dev[off:off + f.size].view(np.shape(a)))
+            off += f.size
+        return out
 
     def _write_context(self, batch_tokens: int) -> None:
         pend_k, pend_v, pend_s, n = [], [], [], 0
@@ -92,7 +124,17 @@ class DeviceRun:
                 flush()
         flush()
 
-    def prepare(self, s: int = 0, width: Optional[int] = None) -> StepInputs:
+    def activations(self, s: int) -> tuple:
+        """Step ``s``'s new K, new V and queries on the device (what a model
+        would hand over), drawn and copied outside any timed region."""
+        st = self.w.step(s)
+        d = self.device
+        return tuple(torch.from_numpy(np.ascontiguousarray(a)).to(d) for a in (st.new_k, st.new_v, st.q))
+
+    def prepare(self, s: int = 0, width: Optional[int] = None, acts: Optional[tuple] = None) -> StepInputs:
+        """Host bookkeeping of step ``s`` (table growth, slots, copy-on-write
+        pairs) and the copies of its metadata to the device; the activations
+        are copied too unless ``acts`` (from ``activations``) is given."""
         st = self.w.step(s)
         b = self.mgr.step(self.ids, st.q_lens, width)
         d = self.device
@@ -100,8 +142,9 @@ class DeviceRun:
         def dev(a):
             return torch.from_numpy(np.ascontiguousarray(a)).to(d)
 
-        return StepInputs(b, dev(b.slot_mapping), dev(b.copy_pairs), dev(b.block_tables), dev(b.seq_lens),
-                          dev(b.q_lens), dev(st.new_k), dev(st.new_v), dev(st.q))
+        nk, nv, q = acts if acts is not None else (dev(st.new_k), dev(st.new_v), dev(st.q))
+        sm, cp, bt, sl, ql = self._upload_i32([b.slot_mapping, b.copy_pairs, b.block_tables, b.seq_lens, b.q_lens])
+        return StepInputs(b, sm, cp, bt, sl, ql, nk, nv, q)
 
     def write(self, x: StepInputs) -> None:
         if x.copy_pairs.shape[0]:
@@ -109,6 +152,13 @@ class DeviceRun:
         pa.pa_write_kv(x.new_k, x.new_v, x.slot_mapping, self.k_cache, self.v_cache, self.k_scale, self.v_scale)
 
     def attend(self, x: StepInputs, out=None, workspace=None, **opts) -> torch.Tensor:
+        if workspace is None:
+            need = pa.pa_attend_workspace_bytes(self.k_cache, self.w.num_q_heads, x.batch.seq_lens,
+                                                x.batch.q_lens, opts.get("partition_tokens", 0),
+                                                opts.get("mfma_min_rows", 0))
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(2 * need, dtype=torch.uint8, device=self.device)
+            workspace = self._ws
         return pa.pa_attend(x.q, self.k_cache, self.v_cache, x.block_tables, x.seq_lens, x.q_lens,
                             x.batch.seq_lens, x.batch.q_lens, self.w.scale, out=out, workspace=workspace,
                             k_scale=self.k_scale, v_scale=self.v_scale, **opts)

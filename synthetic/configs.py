@@ -121,6 +121,7 @@ class Workload:
     context: Optional[Callable[[int], tuple]] = None
 
     _cache: dict = field(default_factory=dict, repr=False)
+    _step_cache: dict = field(default_factory=dict, repr=False)
 
     def _pool(self, name):
         if name not in self.pool_draws:
@@ -154,8 +155,11 @@ class Workload:
         return self.num_q_heads // self.num_kv_heads
 
     def step(self, s: int) -> StepDraw:
+        """Step ``s``'s draws; the same object on every call (callers may edit it)."""
         if callable(self.steps):
-            return self.steps(s)
+            if s not in self._step_cache:
+                self._step_cache[s] = self.steps(s)
+            return self._step_cache[s]
         return self.steps[s]
 
     @property
@@ -248,11 +252,14 @@ def config3(seed: int = 47003, num_seqs: int = 256, max_len: int = 4096, min_len
 
 
 def config4(seed: int = 47004, num_requests: int = 64, prefix: int = 1024, min_suffix: int = 16,
-            max_suffix: int = 256, beam_requests: int = 16, beam_width: int = 4) -> Workload:
+            max_suffix: int = 256, beam_requests: int = 16, beam_width: int = 4, share: bool = True) -> Workload:
     """Shared prefix + beam copy-on-write: every request's table starts with
     the same ``prefix``-token chain; suffixes U[16,256]; requests
     0..beam_requests-1 are forked into ``beam_width`` sequences; one decode
-    token per sequence.  Free list is a seeded permutation."""
+    token per sequence.  Free list is a seeded permutation.
+
+    ``share=False`` is the control with the same sequences and lengths but
+    nothing shared: every sequence (each beam too) owns all of its blocks."""
     hq, hkv, d = 32, 8, 128
     rng = np.random.default_rng([seed, S_META])
     suffix = rng.integers(min_suffix, max_suffix + 1, num_requests).astype(np.int64)
@@ -262,6 +269,16 @@ def config4(seed: int = 47004, num_requests: int = 64, prefix: int = 1024, min_s
     nb = int(math.ceil(1.1 * need))
     perm = rng.permutation(nb)
     nseq = int(np.sum(beams))
+    if not share:
+        lens = np.repeat(prefix + suffix, beams)
+        nb = int(math.ceil(1.1 * int(np.sum(_ceil_div(lens + 1, BLOCK_SIZE)))))
+        return Workload(
+            name="prefix-copies-control", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+            block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
+            first_pops=rng.permutation(nb), ctx_lens=lens,
+            pool_draws=_f16_pool(seed, nb, hkv, d),
+            steps=[_step(seed, (0,), np.ones(nseq, np.int64), hq, hkv, d)],
+        )
     return Workload(
         name="prefix-share-beam-cow", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
         block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
