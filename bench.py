@@ -242,6 +242,47 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, kernel_prefix: 
     return res
 
 
+def summarize_counters(csv_path: str, out: str, cmd: str, title: str, prefixes) -> None:
+    """Per-dispatch averages of the SQ/GRBM counters of one rocprofv3 --pmc
+    run for the kernels named by ``prefixes``, with the derived shares: MFMA
+    busy and VALU issue per SIMD (1024 SIMDs, 32 shader engines, 8 XCDs on
+    this part; per-SE counters are summed over the SEs, per-SIMD ones over the
+    SIMDs, GRBM_GUI_ACTIVE over the XCDs)."""
+    rows = _read_counters(csv_path)
+    lines = [f"# {title}", "", "Command (repository root, one MI355X):", "", f"    {cmd}", ""]
+    for pre in prefixes:
+        per = {}
+        n = 0
+        for (d, k), c in rows.items():
+            if k.startswith(pre):
+                n += 1
+                for name, v in c.items():
+                    per[name] = per.get(name, 0.0) + v
+        if not n:
+            continue
+        avg = {k: v / n for k, v in per.items()}
+        lines += [f"## `{pre}` ({n} dispatches)", "", "| counter | per dispatch |", "|---|---|"]
+        lines += [f"| {k} | {v:,.0f} |" for k, v in sorted(avg.items())]
+        cyc = avg.get("GRBM_GUI_ACTIVE", 0) / 8 or avg.get("SQ_BUSY_CYCLES", 0) / 32
+        if cyc:
+            lines.append("")
+            lines.append(f"Kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs): {cyc:,.0f}.")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                lines.append(f"MFMA busy: {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / cyc:.1%} of SIMD cycles.")
+            if "SQ_ACTIVE_INST_VALU" in avg:
+                lines.append(f"VALU issue: {avg['SQ_ACTIVE_INST_VALU'] * 4 / 1024 / cyc:.1%} of SIMD cycles "
+                             "(quad-cycle units).")
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and avg.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                lines.append(f"VALU issued while the MFMA unit was busy: "
+                             f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.1%} of MFMA-busy cycles.")
+            if "SQ_INSTS_VALU" in avg and "SQ_WAVES" in avg and avg["SQ_WAVES"]:
+                lines.append(f"VALU instructions per wave: {avg['SQ_INSTS_VALU'] / avg['SQ_WAVES']:,.0f}; "
+                             f"MFMA per wave: {avg.get('SQ_INSTS_MFMA', 0) / avg['SQ_WAVES']:,.0f}.")
+        lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_trace(stats_csv: str, out: str, cmd: str, title: str, alg_bytes: int = 0, alg_flops: int = 0,
                     kernel_prefix: str = "") -> None:
     """Kernel table from a rocprofv3 --kernel-trace --stats run, with the
@@ -341,6 +382,9 @@ def main(argv=None) -> int:
                          "(FETCH_SIZE, WRITE_SIZE) made with --copy-calibration-mib; no GPU is used")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "COMMAND"),
                     help="write a kernel-trace summary from a rocprofv3 --stats file; no GPU is used")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("PMC_CSV", "OUT_MD", "COMMAND"),
+                    help="write per-dispatch SQ/GRBM counter averages of --summary-kernel (semicolon-separated "
+                         "prefixes) from a rocprofv3 --pmc run; no GPU is used")
     ap.add_argument("--summary-kernel", default="void pa::decode_kernel<128, 4, false",
                     help="kernel-name prefix the summaries rate")
     ap.add_argument("--summary-title", default="")
@@ -351,6 +395,10 @@ def main(argv=None) -> int:
                           args.summarize_pmc[2], args.pmc_commands)
         print(json.dumps({k: r[k] for k in ("hbm_bytes_per_launch", "algorithmic_bytes_per_launch",
                                              "traffic_over_algorithmic", "source_hash")}))
+        return 0
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.summarize_counters[2],
+                           args.summary_title or "SQ counters", args.summary_kernel.split(";"))
         return 0
     if args.summarize_trace:
         import synthetic
