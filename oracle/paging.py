@@ -17,6 +17,13 @@ Written from:
 Readings where the pages are silent: a block whose refcount reaches zero goes
 straight back on the free stack; a slot number is ``block * bs + offset``; all
 copy-on-write copies of a step happen before that step's writes.
+
+Sliding window ([pytorch] "PagedAttention vs sliding-window attention,
+RadixAttention, and SSMs": the window caps retained history while paging
+manages the blocks that hold it).  Reading: after a sequence's new positions
+are reserved, every block of it that holds no position at or after the
+step's earliest visible key (``L - Q - w + 1``, L after the step) is
+released, in table order; its table entry becomes -1.
 """
 from __future__ import annotations
 
@@ -175,13 +182,27 @@ def build_state(w) -> RefState:
     return st
 
 
-def apply_step(st: RefState, q_lens):
-    """Reserve every sequence's new positions; returns (slot_mapping, copies)."""
+def release_out_of_window(st: RefState, i: int, q_len: int, window: int) -> None:
+    """Release sequence ``i``'s blocks that only hold positions before the
+    step's earliest visible key; their table entries become -1."""
+    lo = max(0, st.lens[i] - int(q_len) - int(window) + 1)
+    table = st.tables[i]
+    for lb in range(min(lo // st.bs, len(table))):
+        if table[lb] >= 0:
+            st.pool.release(table[lb])
+            table[lb] = -1
+
+
+def apply_step(st: RefState, q_lens, window: int = 0):
+    """Reserve every sequence's new positions; returns (slot_mapping, copies).
+    With ``window > 0`` each sequence then releases its out-of-window blocks."""
     slots, copies = [], []
     for i, n in enumerate(q_lens):
         s, c = st.append(i, int(n))
         slots += s
         copies += c
+        if window:
+            release_out_of_window(st, i, int(n), window)
     return np.asarray(slots, np.int64), copies
 
 

@@ -475,3 +475,102 @@ def test_scale_enters_scores():
     assert np.allclose(a, b, rtol=0, atol=1e-13)
     c = oatt.paged_attention(q, K, V, st.tables, [10], [1], 1.0, 4)
     assert not np.allclose(a, c, atol=1e-6)
+
+
+# --------------------------------------------------------- sliding window ----
+# [pytorch] "PagedAttention vs sliding-window attention, RadixAttention, and
+# SSMs": each query attends only to the most recent w tokens; the window caps
+# the retained history while paging manages the blocks that hold it.
+
+def test_window_attention_equals_sdpa_on_the_window():
+    """Row at position P with window w == SDPA (fp64) over keys max(0, P-w+1)..P of
+    the contiguous originals; w >= L is plain causal attention, bit for bit."""
+    rng = np.random.default_rng(41)
+    hq, hkv, d, bs = 8, 2, 16, 4
+    lens, qls = [1, 9, 23, 17], [1, 3, 7, 17]
+    nb = sum(opg.blocks_for(L, bs) for L in lens) + 2
+    st = opg.RefState(nb, bs, first_pops=rng.permutation(nb))
+    K = rng.standard_normal((nb, hkv, bs, d)).astype(np.float16)
+    V = rng.standard_normal((nb, hkv, bs, d)).astype(np.float16)
+    conts = []
+    for L in lens:
+        i = st.add(0)
+        slots, _ = st.append(i, L)
+        ck = rng.standard_normal((L, hkv, d)).astype(np.float16)
+        cv = rng.standard_normal((L, hkv, d)).astype(np.float16)
+        K, V = okv.write_f16(K, V, ck, cv, slots, bs)
+        conts.append((ck, cv))
+    q = rng.standard_normal((sum(qls), hq, d)).astype(np.float16)
+    F = torch.nn.functional
+    full = oatt.paged_attention(q, K, V, st.tables, lens, qls, 0.25, bs)
+    assert np.array_equal(oatt.paged_attention(q, K, V, st.tables, lens, qls, 0.25, bs, window=max(lens)), full)
+    for w in (1, 2, 5, 8):
+        out = oatt.paged_attention(q, K, V, st.tables, lens, qls, 0.25, bs, window=w)
+        r = 0
+        for (ck, cv), L, Q in zip(conts, lens, qls):
+            for t in range(Q):
+                P = L - Q + t
+                lo = max(0, P - w + 1)
+                kt = torch.from_numpy(ck[lo:P + 1].astype(np.float64)).permute(1, 0, 2)[None]
+                vt = torch.from_numpy(cv[lo:P + 1].astype(np.float64)).permute(1, 0, 2)[None]
+                qt = torch.from_numpy(q[r + t].astype(np.float64))[None, :, None, :]
+                ref = F.scaled_dot_product_attention(qt, kt, vt, scale=0.25, enable_gqa=True)
+                assert np.allclose(out[r + t], ref[0, :, 0].numpy(), rtol=0, atol=1e-12), (w, L, t)
+                if w == 1:   # one visible key: its V exactly
+                    assert np.array_equal(out[r + t], np.repeat(cv[P].astype(np.float64), hq // hkv, axis=0))
+            r += Q
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_window_brute_force_tiny(int8):
+    rng = np.random.default_rng(43 + int8)
+    hq, hkv, d, bs = 4, 2, 4, 4
+    lens, qls = [5, 11, 7], [1, 4, 7]
+    nb = sum(opg.blocks_for(L, bs) for L in lens) + 1
+    st = opg.RefState(nb, bs, first_pops=rng.permutation(nb))
+    for L in lens:
+        st.add(L)
+    if int8:
+        K = rng.integers(-127, 128, (nb, hkv, bs, d)).astype(np.int8)
+        V = rng.integers(-127, 128, (nb, hkv, bs, d)).astype(np.int8)
+        ks = rng.uniform(0.01, 0.05, (nb, hkv)).astype(np.float16)
+        vs = rng.uniform(0.01, 0.05, (nb, hkv)).astype(np.float16)
+    else:
+        K = rng.standard_normal((nb, hkv, bs, d)).astype(np.float16)
+        V = rng.standard_normal((nb, hkv, bs, d)).astype(np.float16)
+        ks = vs = None
+    q = rng.standard_normal((sum(qls), hq, d)).astype(np.float16)
+    for w in (1, 3, 6):
+        vec = oatt.paged_attention(q, K, V, st.tables, lens, qls, 0.5, bs, ks, vs, window=w)
+        bf = brute.paged_attention(q.tolist(), K.tolist(), V.tolist(), st.tables, lens, qls, 0.5, bs,
+                                   None if ks is None else ks.tolist(), None if vs is None else vs.tolist(), window=w)
+        assert np.allclose(vec, np.array(bf), rtol=0, atol=1e-12)
+
+
+def test_window_releases_blocks_that_leave_it():
+    """bs 4, w 6, one sequence growing by decode steps from 3 tokens: after the
+    step that makes it L tokens long, keys before L - 1 - 6 + 1 = L - 6 are
+    out of every present and future window, so blocks whose last position is
+    below L - 6 are released (table entry -1) and come back on the stack."""
+    st = opg.RefState(8, 4)                 # first pops 0, 1, 2, ...
+    st.add(3)                               # [0]
+    held = []
+    for L in range(4, 21):
+        opg.apply_step(st, [1], window=6)
+        held.append(list(st.tables[0]))
+        lo = max(0, L - 6)
+        for lb, b in enumerate(st.tables[0]):
+            assert (b == -1) == ((lb + 1) * 4 <= lo), (L, st.tables[0])
+        live = [b for b in st.tables[0] if b >= 0]
+        assert len(live) <= -(-6 // 4) + 1
+        assert sorted(live + st.pool.stack) == list(range(8))
+    # L = 10 releases block 0 (positions 0-3 < 4); block 0 is then reused at L = 13 for logical
+    # block 3, and L = 14 releases block 1 (positions 4-7 < 8)
+    assert held[10 - 4] == [-1, 1, 2]
+    assert held[13 - 4] == [-1, 1, 2, 0]
+    assert held[14 - 4] == [-1, -1, 2, 0]
+    # a step with 3 query tokens keeps what its first query still sees
+    st = opg.RefState(8, 4)
+    st.add(10)                              # blocks 0, 1, 2 (positions 0-9)
+    opg.apply_step(st, [3], window=4)       # L = 13, earliest visible key 13 - 3 - 4 + 1 = 7
+    assert st.tables[0] == [-1, 1, 2, 3]
