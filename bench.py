@@ -111,24 +111,35 @@ def traffic_from_profile():
     return p.get("hbm_bytes_per_launch")
 
 
+def window_lo(pos: int, window: int) -> int:
+    """First key a query at ``pos`` sees (0 without a sliding window)."""
+    return max(0, pos - window + 1) if window > 0 else 0
+
+
 def work_split(w, L, Q):
     """Algorithmic work of one step: (vector-path KV bytes, MFMA-path flops,
-    total KV bytes).  Rows with q_len * group >= 16 go to the MFMA path."""
+    total KV bytes).  Rows with q_len * group >= 16 go to the MFMA path.  A
+    vector-path row reads the K and V of the keys it sees (int8: plus one
+    scale per block and head for each); a sequence's total counts the keys
+    any of its rows sees once; with a sliding window only keys inside it."""
     eb = 1 if w.kv_dtype == "i8" else 2
+    bs = w.block_size
     per_tok = w.num_kv_heads * w.head_dim * 2 * eb
+    per_blk = w.num_kv_heads * 2 * 2 if w.kv_dtype == "i8" else 0
+
+    def keys_bytes(lo, hi):       # keys lo .. hi-1
+        return (hi - lo) * per_tok + (-(-hi // bs) - lo // bs) * per_blk if hi > lo else 0
+
     vec_bytes, mfma_flops, total = 0, 0, 0
     for l, q in zip(L.tolist(), Q.tolist()):
-        kv = l * per_tok
-        if w.kv_dtype == "i8":
-            kv += -(-l // w.block_size) * w.num_kv_heads * 2 * 2
-        total += kv
+        total += keys_bytes(window_lo(l - q, w.window), l)
         if q == 0:
             continue
         if q * w.group >= 16:
-            vis = sum(l - q + t + 1 for t in range(q))
+            vis = sum(l - q + t + 1 - window_lo(l - q + t, w.window) for t in range(q))
             mfma_flops += 4 * w.head_dim * w.num_q_heads * vis
         else:
-            vec_bytes += kv * q
+            vec_bytes += sum(keys_bytes(window_lo(l - q + t, w.window), l - q + t + 1) for t in range(q))
     return vec_bytes, mfma_flops, total
 
 
@@ -140,13 +151,13 @@ def _blas_name() -> str:
         return "unknown"
 
 
-def unique_kv_bytes(w, tables, L) -> int:
+def unique_kv_bytes(w, tables, L, Q) -> int:
     """KV bytes of the distinct physical blocks a step reads (a block shared
     by several sequences counts once, with its largest valid-token count)."""
     eb = 1 if w.kv_dtype == "i8" else 2
     valid = {}
-    for row, n in zip(tables, L.tolist()):
-        for j in range(-(-n // w.block_size)):
+    for row, n, q in zip(tables, L.tolist(), Q.tolist()):
+        for j in range(window_lo(n - q, w.window) // w.block_size, -(-n // w.block_size)):
             b = int(row[j])
             valid[b] = max(valid.get(b, 0), min(w.block_size, n - j * w.block_size))
     return sum(valid.values()) * w.num_kv_heads * w.head_dim * 2 * eb
@@ -159,7 +170,7 @@ def cpu_baseline(w, step: int, budget_s: float):
     import oracle.paging as opg
     st = opg.build_state(w)
     for s in range(step + 1):
-        opg.apply_step(st, w.step(s).q_lens)
+        opg.apply_step(st, w.step(s).q_lens, w.window)
     sd = w.step(step)
     K, V = w.pool_k, w.pool_v
     bs = w.block_size
@@ -169,12 +180,14 @@ def cpu_baseline(w, step: int, budget_s: float):
     done, kv_bytes = 0, 0
     for i in range(len(st.tables)):
         L, Q = st.lens[i], int(sd.q_lens[i])
-        Kc = oatt.gather(K, st.tables[i], L, bs, w.pool_k_scale)
-        Vc = oatt.gather(V, st.tables[i], L, bs, w.pool_v_scale)
+        lo = oatt.window_start(L, Q, w.window)
+        Kc = oatt.gather(K, st.tables[i], L, bs, w.pool_k_scale, lo)
+        Vc = oatt.gather(V, st.tables[i], L, bs, w.pool_v_scale, lo)
         if Q:
-            oatt.attend(sd.q[starts[i]:starts[i] + Q], oatt.query_positions(L, Q), Kc, Vc, w.scale)
+            oatt.attend(sd.q[starts[i]:starts[i] + Q], oatt.query_positions(L, Q), Kc, Vc, w.scale,
+                        w.window, lo)
         done += 1
-        kv_bytes += L * w.num_kv_heads * w.head_dim * 2 * eb
+        kv_bytes += (L - lo) * w.num_kv_heads * w.head_dim * 2 * eb
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
@@ -373,6 +386,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cold", type=int, default=-1, choices=(-1, 0, 1),
                     help="also time steps after a 1 GiB scratch write that evicts the 256 MB MALL "
                          "(default: for working sets under 512 MB, workloads 1, 2 and 4)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window attention over this many keys (0: full causal attention)")
     ap.add_argument("--no-share", action="store_true",
                     help="workload 4 control: every sequence owns its own copy of the prefix (no sharing, no forks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -403,6 +418,7 @@ def main(argv=None) -> int:
     if args.summarize_trace:
         import synthetic
         w = synthetic.CONFIGS[args.workload]()
+        w.window = args.window
         L, Q = _step_lengths(w, 1 if args.workload == 2 else 0)
         vb, mf, _ = work_split(w, L, Q)
         mfma = "prefill" in args.summary_kernel
@@ -422,6 +438,7 @@ def main(argv=None) -> int:
 
     torch.cuda.set_device(0)
     w = synthetic.config4(share=False) if (args.workload == 4 and args.no_share) else synthetic.CONFIGS[args.workload]()
+    w.window = args.window
     run = DeviceRun(w)
     step_index = 0
     if args.workload == 2:            # prefill (step 0) first; the timed step is the first decode step
@@ -435,7 +452,7 @@ def main(argv=None) -> int:
     vec_bytes, mfma_flops, kv_bytes = work_split(w, L, Q)
     out = torch.empty_like(x.q)
     need = pa.pa_attend_workspace_bytes(run.k_cache, w.num_q_heads, x.batch.seq_lens, x.batch.q_lens,
-                                        partition_tokens=args.partition_tokens)
+                                        partition_tokens=args.partition_tokens, window=w.window)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     n = args.warmup + args.steps
     evs = TimingEvents(4 * n)
@@ -447,7 +464,7 @@ def main(argv=None) -> int:
         ev = tuple(evs.handle(4 * i + j) for j in range(4)) if timed_kernel else None
         pa.pa_attend(x.q, run.k_cache, run.v_cache, x.block_tables, x.seq_lens, x.q_lens, x.batch.seq_lens,
                      x.batch.q_lens, w.scale, out=out, workspace=ws, k_scale=run.k_scale, v_scale=run.v_scale,
-                     partition_tokens=args.partition_tokens, events=ev)
+                     partition_tokens=args.partition_tokens, events=ev, window=w.window)
 
     # the region's own events, created and recorded once before anything is timed
     t0 = torch.cuda.Event(enable_timing=True)
@@ -485,7 +502,8 @@ def main(argv=None) -> int:
         ach = vec_bytes / (k_ms * 1e-3) / 1e9
         roof.append({"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(ach / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profile() if args.workload == 3 and not args.partition_tokens else None,
+                     "traffic": traffic_from_profile() if (args.workload == 3 and not args.partition_tokens
+                                                           and not args.window) else None,
                      "kernel": "decode_kernel (split-K vector path)", "kernel_ms": round(k_ms, 5),
                      "kernel_ms_median": round(float(np.median(k_all)), 5),
                      "algorithmic_bytes_per_launch": vec_bytes})
@@ -539,10 +557,11 @@ def main(argv=None) -> int:
         "dtype": "i8" if w.kv_dtype == "i8" else "f16",
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload] + (" [control: every sequence owns its prefix copy]"
-                                                          if args.workload == 4 and args.no_share else ""),
+                                                          if args.workload == 4 and args.no_share else "")
+                   + (f" [sliding window of {args.window} keys]" if args.window else ""),
                    "num_seqs": S, "kv_tokens": int(L.sum()),
                    "query_rows": int(Q.sum()), "num_blocks": w.num_blocks,
-                   "partition_tokens": args.partition_tokens},
+                   "partition_tokens": args.partition_tokens, "window": args.window},
         "pct_of_peak": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "seq_steps_per_s": round(S / (ms * 1e-3), 1),
         "ms_per_step_without_kernel_events": round(ms_plain, 5),
@@ -557,7 +576,7 @@ def main(argv=None) -> int:
     if e2e is not None:
         res["end_to_end"] = e2e
     if args.workload == 4:
-        ub = unique_kv_bytes(w, x.batch.block_tables, L)
+        ub = unique_kv_bytes(w, x.batch.block_tables, L, Q)
         res["unique_kv_bytes_per_step"] = ub
         res["value_unique"] = round(ub / (ms * 1e-3) / 1e9, 2)
         res["pct_of_peak"] = round(100 * ub / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)   # of unique bytes

@@ -117,6 +117,15 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v,
  *   mfma_begin/end    `stream` immediately before and after the vector-path
  *                     (resp. MFMA-path) attention kernel when that kernel is
  *                     launched; NULL = not recorded.  For per-kernel timing.
+ *   window            sliding window ([pytorch] "PagedAttention vs
+ *                     sliding-window attention, RadixAttention, and SSMs":
+ *                     each query attends only to the most recent `window`
+ *                     tokens): 0 = none; w > 0 = the query at position P
+ *                     sees keys max(0, P - w + 1) .. P.  Table entries of
+ *                     blocks that hold no key at or after the earliest one a
+ *                     step's queries see (seq_len - q_len - w + 1) are never
+ *                     read, so the caller may have released those blocks.
+ *                     Negative: PA_ERR_SHAPE.
  */
 typedef struct {
   int32_t partition_tokens;
@@ -125,6 +134,7 @@ typedef struct {
   hipEvent_t vector_end;
   hipEvent_t mfma_begin;
   hipEvent_t mfma_end;
+  int32_t window;
 } pa_attend_opts;
 
 /*
@@ -161,7 +171,8 @@ size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
  *   workspace     device scratch of at least pa_attend_workspace_bytes.
  *
  * Query row t (0-based) of sequence i sits at position
- * seq_lens[i] - q_lens[i] + t and attends to keys 0 .. that position
+ * seq_lens[i] - q_lens[i] + t and attends to keys 0 .. that position (the
+ * last opts->window of them with a sliding window)
  * ([engine] "03 Correctness, and the bugs a real model found": the mask uses
  * the query's real position).  Query head h reads KV head h / group
  * ([pytorch] reference attention: each KV head repeated group times along a

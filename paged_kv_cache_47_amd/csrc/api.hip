@@ -58,10 +58,25 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* lds, int4& total) {
   return make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
 }
 
-__device__ __forceinline__ int parts_for(int nvis, int part) { return part <= 0 ? 1 : (nvis + part - 1) / part; }
+__host__ __device__ __forceinline__ int parts_for(int nkeys, int part) {
+  return part <= 0 ? 1 : (nkeys + part - 1) / part;
+}
 
-// Row tiles of the MFMA path go out longest first.  A tile's cost is its
-// number of visible keys (causal: the last row's), and tiles that attend over
+// Keys the vector path walks for the query at position `pos`: from the
+// 16-aligned start of its window (0 without one) to the query itself.
+__host__ __device__ __forceinline__ int vector_keys(int pos, int window) {
+  return pos + 1 - (window_lo(pos, window) & ~(kBlockSize - 1));
+}
+
+// First key the MFMA row tile starting at query position `qfirst` stages:
+// the step-aligned start of that row's window.
+__host__ __device__ __forceinline__ int tile_key0(int qfirst, int window) {
+  return window_lo(qfirst, window) & ~(kMfmaBN - 1);
+}
+
+// Row tiles of the MFMA path go out longest first.  A tile's cost is the
+// number of keys it steps over (causal: up to the last row's position; with a
+// window, from the first row's window start), and tiles that attend over
 // long contexts would otherwise start late and finish after the rest of the
 // grid; with 64-key cost buckets in descending order (a counting sort over
 // the workgroup) the dispatcher fills the machine greedily, longest job first.
@@ -74,7 +89,8 @@ __device__ int tile_cost_bucket(const PlanArgs& a, int2 mu) {
   const int rows = si.q_len * a.group;
   const int last_row = min(rows, (mu.y + 1) * kMfmaRows) - 1;
   const int kmax = min(si.kv_len, si.kv_len - si.q_len + last_row / a.group + 1);
-  return min(kmax / 64, kCostBuckets - 1);
+  const int k0 = tile_key0(si.kv_len - si.q_len + mu.y * kMfmaRows / a.group, a.window);
+  return min((kmax - k0) / kMfmaBN, kCostBuckets - 1);
 }
 
 __device__ void order_row_tiles(const PlanArgs& a, int n) {
@@ -116,7 +132,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         nmu = (Q * a.group + kMfmaRows - 1) / kMfmaRows;
       } else {
         nvt = Q;
-        for (int t = 0; t < Q; ++t) nvu += parts_for(L - Q + t + 1, a.part);
+        for (int t = 0; t < Q; ++t) nvu += parts_for(vector_keys(L - Q + t, a.window), a.part);
       }
     }
     const int4 ex = block_exclusive_scan4(make_int4(nvt, nvu, nmu, 0), lds, tot);
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         if (mu0 + r < a.cap_munit) a.munit_tmp[mu0 + r] = make_int2(i, r);
       int u = vu0;
       for (int t = 0; t < nvt; ++t) {
-        const int parts = parts_for(L - Q + t + 1, a.part);
+        const int parts = parts_for(vector_keys(L - Q + t, a.window), a.part);
         const int k = vt0 + t;
         const bool fits = k < a.cap_vtok && u + parts <= a.cap_vunit;
         if (k < a.cap_vtok) {
@@ -171,7 +187,7 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 
 // ------------------------------------------------------------ host plan ----
 struct HostPlan {
-  int32_t part = 0, min_rows = 16, total_q = 0;
+  int32_t part = 0, min_rows = 16, total_q = 0, window = 0;
   int64_t n_vtok = 0, n_vunit = 0, n_munit = 0;
   int32_t max_parts = 0;
   size_t off_seqs = 0, off_vtok = 0, off_vunit = 0, off_munit = 0, off_munit_tmp = 0, off_lse = 0, off_po = 0;
@@ -217,14 +233,16 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   const int g = hq / d->num_kv_heads;
   int32_t req_part = opts ? opts->partition_tokens : 0;
   P.min_rows = (opts && opts->mfma_min_rows > 0) ? opts->mfma_min_rows : 16;
+  P.window = opts ? opts->window : 0;
   if (req_part > 0 && req_part % kBlockSize != 0) return PA_ERR_SHAPE;
+  if (P.window < 0) return PA_ERR_SHAPE;
   const int64_t max_kv = (int64_t)max_blocks * kBlockSize;
   int64_t total_q = 0, vec_keys = 0;
   for (int i = 0; i < num_seqs; ++i) {
     if (hL[i] < 0 || hQ[i] < 0 || hQ[i] > hL[i] || hL[i] > max_kv) return PA_ERR_SHAPE;
     total_q += hQ[i];
     if (!(hQ[i] > 0 && (int64_t)hQ[i] * g >= P.min_rows))
-      for (int t = 0; t < hQ[i]; ++t) vec_keys += hL[i] - hQ[i] + t + 1;
+      for (int t = 0; t < hQ[i]; ++t) vec_keys += vector_keys(hL[i] - hQ[i] + t, P.window);
   }
   if (total_q >= INT32_MAX / 2) return PA_ERR_SHAPE;
   P.total_q = (int32_t)total_q;
@@ -236,8 +254,7 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
     } else {
       P.n_vtok += Q;
       for (int t = 0; t < Q; ++t) {
-        const int nvis = L - Q + t + 1;
-        const int parts = P.part <= 0 ? 1 : (nvis + P.part - 1) / P.part;
+        const int parts = parts_for(vector_keys(L - Q + t, P.window), P.part);
         P.n_vunit += parts;
         P.max_parts = std::max(P.max_parts, parts);
       }
@@ -356,6 +373,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   pl.num_seqs = num_seqs;
   pl.group = g;
   pl.part = P.part;
+  pl.window = P.window;
   pl.min_rows = P.min_rows;
   pl.max_kv = (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * kBlockSize, INT32_MAX);
   pl.total_q = P.total_q;
@@ -383,6 +401,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.hq = num_q_heads;
   a.hkv = desc->num_kv_heads;
   a.part = P.part > 0 ? P.part : INT32_MAX / 2;
+  a.window = P.window;
   a.scale_log2 = scale * kLog2e;
 
   auto mark = [&](hipEvent_t ev) { return ev == nullptr || hipEventRecord(ev, stream) == hipSuccess; };

@@ -7,7 +7,10 @@
 // ([pytorch] "Map the PyTorch design to vLLM PagedAttention").  Query row t of
 // a sequence with q_len rows and kv_len keys sits at position
 // kv_len - q_len + t and sees keys 0 .. that position ([engine] "03
-// Correctness, and the bugs a real model found").  int8 blocks are
+// Correctness, and the bugs a real model found"), or only the last `window`
+// of them ([pytorch] "PagedAttention vs sliding-window attention,
+// RadixAttention, and SSMs"); the walk then starts at the 16-key block that
+// holds the window's first key, and earlier blocks are never read.  int8 blocks are
 // dequantised in registers before each of the two products ([engine] "INT8
 // KV cache design").
 //
@@ -134,7 +137,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   if (vt.seq < 0) return;
   const SeqInfo si = a.seqs[vt.seq];
   const int nvis = si.kv_len - si.q_len + vt.t + 1;
-  const int kbeg = un.y * a.part;
+  const int klo = window_lo(nvis - 1, a.window);        // first visible key
+  const int kbeg = (klo & ~(kBlockSize - 1)) + un.y * a.part;
   const int kend = min(nvis, kbeg + a.part);
   const int grp = lane / LPT, sub = lane % LPT;
   const int64_t row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
@@ -184,11 +188,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       vsc = scale_at(a.vs, (int64_t)phys * a.hkv + h);
     }
     const int tok0 = blk * kBlockSize + grp;
-    const bool tail = blk * kBlockSize + kBlockSize > kend;  // wave-uniform: last block of the range
-    if (tail) {  // drop V of keys past the range (their slots may hold anything)
+    // wave-uniform: the last block of the range, or the block the window starts in
+    const bool edge = blk * kBlockSize + kBlockSize > kend || blk * kBlockSize < klo;
+    // keys outside [klo, kend) (the slots past the range may hold anything)
+    auto hidden = [&](int tok) { return (unsigned)(tok - klo) >= (unsigned)(kend - klo); };
+    if (edge) {  // drop their V
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        if (tok0 + i * TPL >= kend) vr[i] = Dw<ND>{};
+        if (hidden(tok0 + i * TPL)) vr[i] = Dw<ND>{};
     }
 
     // raw dot products q.k of this lane group's NL tokens for the G rows;
@@ -222,12 +229,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       }
     }
     group_sum_all<LPT, NL * G>(&s[0][0]);
-    if (tail) {
+    if (edge) {
 #pragma unroll
       for (int i = 0; i < NL; ++i)
 #pragma unroll
         for (int g = 0; g < G; ++g)
-          if (tok0 + i * TPL >= kend) s[i][g] = -__builtin_inff();
+          if (hidden(tok0 + i * TPL)) s[i][g] = -__builtin_inff();
     }
 
     // The running max moves only when a score exceeds it by more than

@@ -9,6 +9,7 @@ namespace pa {
 #define PA_PF_WAVES 8
 #endif
 constexpr int kMfmaWaves = PA_PF_WAVES;          // waves per MFMA workgroup, 32 query rows each
-constexpr int kMfmaRows = 32 * kMfmaWaves;       // query rows per MFMA workgroup
+constexpr int kMfmaRows = 32 * kMfmaWaves;
+constexpr int kMfmaBN = 64;   // keys per step of a row tile       // query rows per MFMA workgroup
 
 }  // namespace pa

@@ -51,8 +51,14 @@ struct AttnArgs {
   int32_t num_blocks;
   int32_t hq, hkv;
   int32_t part;        // keys per partition (a multiple of 16)
+  int32_t window;      // sliding window in keys; 0 = none
   float scale_log2;    // scale * log2(e)
 };
+
+// First key a query at position `pos` sees (0 without a window).
+__host__ __device__ __forceinline__ int window_lo(int pos, int window) {
+  return window > 0 ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
+}
 
 struct PlanArgs {
   const int32_t* seq_lens;
@@ -65,6 +71,7 @@ struct PlanArgs {
   int32_t num_seqs;
   int32_t group;
   int32_t part;        // <= 0: one partition per row
+  int32_t window;      // sliding window in keys; 0 = none
   int32_t min_rows;
   int32_t max_kv;      // max_blocks_per_seq * block_size
   int32_t total_q;

@@ -7,8 +7,10 @@
 // ([pytorch] "Map the PyTorch design to vLLM PagedAttention").  Query row t of
 // a sequence with q_len rows and kv_len keys sits at position
 // kv_len - q_len + t and sees keys 0 .. that position ([engine] "03
-// Correctness, and the bugs a real model found").  int8 blocks are
-// dequantised before the two products ([engine] "INT8 KV cache design").
+// Correctness, and the bugs a real model found"), or only the last `window`
+// of them ([pytorch] "PagedAttention vs sliding-window attention,
+// RadixAttention, and SSMs").  int8 blocks are dequantised before the two
+// products ([engine] "INT8 KV cache design").
 //
 // Sequences with q_len * G >= 16 rows take this path: kMfmaRows query rows
 // per workgroup (kMfmaWaves waves x 32), 64 keys per step, S^T = K Q^T and O^T = V^T P^T
@@ -28,7 +30,6 @@ namespace pa {
 // registers while the current tiles in LDS are used, then written to the
 // other LDS buffer; one barrier per step.  The more waves share a tile, the
 // less staging (loads, int8 conversion, LDS stores) each wave does per step.
-constexpr int kMfmaBN = 64;
 #ifndef PA_PF_PRIO
 #define PA_PF_PRIO 0   // 1: raise the wave's issue priority over the S = K Q^T products
 #endif
@@ -73,8 +74,15 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   const int kmax = min(L, L - Q + last_row / G + 1);
   const int32_t* tbl = a.block_tables + (int64_t)mu.x * a.max_blocks;
   const int qmin = L - Q + (r0 + wave * 32) / G;  // query position of this wave's first row
+  // With a window the tile starts at the 64-key step holding its first row's
+  // first visible key (klo); keys before klo are read from klo instead, so
+  // blocks the window has left behind are never addressed.  A step needs the
+  // window mask while it starts before the wave's last row's window does.
+  const int klo = window_lo(L - Q + r0 / G, a.window);
+  const int kt0 = klo & ~(kMfmaBN - 1);
+  const int wlo_last = window_lo(L - Q + (min(rows, r0 + wave * 32 + 32) - 1) / G, a.window);
 
-  int qpos[RB];
+  int qpos[RB], qlo[RB];
   int64_t orow[RB];
   bool rvalid[RB];
   half8_t qop[RB][KS];
@@ -84,6 +92,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
     rvalid[rb] = row < rows;
     const int tq = rvalid[rb] ? row / G : 0;
     qpos[rb] = rvalid[rb] ? L - Q + tq : -1;
+    qlo[rb] = window_lo(qpos[rb], a.window);
     orow[rb] = ((int64_t)(si.q_start + tq) * a.hq + (int64_t)h * G + row % G) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -112,6 +121,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   // LDS reads, so every LDS read of the step would wait for them.  The values
   // are made scalar again when used.
   const int last_blk = (L - 1) / kBlockSize;   // L >= q_len >= 1 for a row tile
+  const int first_blk = klo / kBlockSize;
   const int vz = lane & (a.hkv >> 30);          // 0 (hkv is small and positive)
   struct Blocks {
     int kb[KB];
@@ -120,17 +130,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   auto table = [&](int kt, Blocks& t) {
     if constexpr (I8) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) t.kb[kb] = (tbl + min(kt / kBlockSize + kb, last_blk))[vz];
+      for (int kb = 0; kb < KB; ++kb) t.kb[kb] = (tbl + min(max(kt / kBlockSize + kb, first_blk), last_blk))[vz];
     }
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int key0 = ((64 * wave + NTH * i) % NCH) / CPR;
-      t.chunk[i] = (tbl + min((kt + key0) / kBlockSize, last_blk))[vz];
+      t.chunk[i] = (tbl + min(max(kt + key0, klo) / kBlockSize, last_blk))[vz];
     }
   };
-  // Keys past the sequence are read from its last key instead (a real,
-  // finite row): their scores are masked to -inf and their weights are 0, so
-  // no stale slot is read and no zero fill is needed.  Per lane only a 32-bit
+  // Keys past the sequence are read from its last key instead, and keys
+  // before klo from klo (real, finite rows): their scores are masked to -inf
+  // and their weights are 0, so no stale slot is read and no zero fill is
+  // needed.  Per lane only a 32-bit
   // offset inside the (block, head) tile varies; the tile base is scalar.
   constexpr int64_t kTileBytes = (int64_t)kBlockSize * D * EB;
   auto gload = [&](int kt, const Blocks& t) {
@@ -146,7 +157,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
     for (int i = 0; i < PT; ++i) {
       const int c = (threadIdx.x + NTH * i) % NCH;   // threads past the chunks repeat the first ones
       const int key = c / CPR, ch = c % CPR;
-      const int kg = min(kt + key, L - 1);
+      const int kg = min(max(kt + key, klo), L - 1);
       const int64_t tile = (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.chunk[i]), a.num_blocks) * a.hkv + h;
       if constexpr (I8) nvc[i] = (float)(a.vs + tile)[vz];
       const uint32_t off = (uint32_t)((kg % kBlockSize) * D * EB + ch * 16);
@@ -194,10 +205,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   };
 
   Blocks tn, tn2;
-  table(0, tn);
-  gload(0, tn);
+  table(kt0, tn);
+  gload(kt0, tn);
   lstore(0);
-  table(BN, tn);
+  table(kt0 + BN, tn);
   __syncthreads();
   typedef __attribute__((address_space(3))) short4_t lds_short4;
   int buf = 0;
@@ -209,13 +220,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   // second half's vector work sits beside the first half's matrix products,
   // and the next tiles' staging beside the second half's.
   //
-  // Only steps that reach past this wave's first query position need the
-  // causal mask (a wave-uniform test); it sets the hidden raw scores to -inf.
+  // Only steps that reach past this wave's first query position, or start
+  // before its last row's window does, need the mask (a wave-uniform test);
+  // it sets the hidden raw scores to -inf.
   // The max is taken on raw scores and scaled once per 16-key block (scales
   // are positive), and the scale rides in the exponent's FMA.  The running max
   // moves only when a score exceeds it by more than kRescalePf (log2 units),
   // so the accumulators are rescaled rarely.
-  for (int kt = 0; kt < kmax; kt += BN, buf ^= 1) {
+  for (int kt = kt0; kt < kmax; kt += BN, buf ^= 1) {
     const bool more = kt + BN < kmax;
     // score scale per 16-key block (base 2; int8 folds in the block's K scale).  A zero K scale
     // (an all-zero block) becomes the least normal float: its scores stay 0, and -inf stays -inf.
@@ -249,14 +261,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
           s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kq[ks & 1][kb], qop[rb][ks],
                                                             ks == 0 ? (float4_t)0.f : s[rb][kb], 0, 0, 0);
     }
-    if (kt + BN - 1 > qmin) {
+    if (kt + BN - 1 > qmin || kt < wlo_last) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (kt + kb * 16 + 4 * grp + e > qpos[rb]) s[rb][kb][e] = -__builtin_inff();
+          for (int e = 0; e < 4; ++e) {
+            const int key = kt + kb * 16 + 4 * grp + e;
+            if (key > qpos[rb] || key < qlo[rb]) s[rb][kb][e] = -__builtin_inff();
+          }
     }
     // Each lane tests its own 16 scores against its row's running max; only
     // when some score of the wave exceeds it by more than kRescalePf are the

@@ -23,6 +23,11 @@ Behaviour follows the pages:
   finishing a sequence twice is harmless.
 * [pytorch] "Map the PyTorch design to vLLM PagedAttention": a shared block
   is copied on its first divergent write (copy-on-write).
+* [pytorch] "PagedAttention vs sliding-window attention, RadixAttention, and
+  SSMs": with a sliding window of ``w`` tokens, a step's queries see nothing
+  before position ``seq_len - q_len - w + 1``; once a sequence has reserved
+  its positions for the step, every block holding only earlier positions is
+  released (in table order) and its table entry becomes -1.
 A block whose refcount drops to zero goes straight back on the free stack.
 """
 from __future__ import annotations
@@ -130,10 +135,16 @@ class StepBatch:
 
 
 class PagedKVManager:
-    """Block tables and lengths of many sequences over one ``BlockAllocator``."""
+    """Block tables and lengths of many sequences over one ``BlockAllocator``.
+    ``window`` > 0: sliding-window attention of that many tokens (blocks that
+    leave every query's window are released at each step)."""
 
-    def __init__(self, num_blocks: int, block_size: int = 16, first_pops: Optional[Sequence[int]] = None):
+    def __init__(self, num_blocks: int, block_size: int = 16, first_pops: Optional[Sequence[int]] = None,
+                 window: int = 0):
+        if window < 0:
+            raise ValueError("window must be >= 0")
         self.block_size = int(block_size)
+        self.window = int(window)
         self.alloc = BlockAllocator(num_blocks, first_pops)
         self._seqs: List[_Seq] = []
         self._tab = None          # last block-table array built, its sequence list and row contents
@@ -160,7 +171,8 @@ class PagedKVManager:
     def fork(self, sid: int) -> int:
         s = self._seqs[sid]
         for b in s.blocks:
-            self.alloc.retain(b)
+            if b >= 0:
+                self.alloc.retain(b)
         self._seqs.append(_Seq(blocks=list(s.blocks), length=s.length))
         return len(self._seqs) - 1
 
@@ -169,7 +181,8 @@ class PagedKVManager:
         if not s.live:
             return
         for b in s.blocks:
-            self.alloc.release(b)
+            if b >= 0:
+                self.alloc.release(b)
         s.blocks = []
         s.live = False
 
@@ -186,6 +199,8 @@ class PagedKVManager:
             raise ValueError("positions outside the sequence")
         pos = np.arange(start, start + n, dtype=np.int64)
         bl = np.asarray(s.blocks, np.int64)
+        if n and bl[start // self.block_size] < 0:
+            raise ValueError("positions in blocks released by the sliding window")
         return (bl[pos // self.block_size] * self.block_size + pos % self.block_size).astype(np.int32)
 
     # -- writes -----------------------------------------------------------
@@ -211,6 +226,17 @@ class PagedKVManager:
         s.length += int(n)
         return slots, copies
 
+    def release_out_of_window(self, sid: int, q_len: int) -> None:
+        """Release the blocks of ``sid`` that hold no position the step's
+        queries (its last ``q_len`` positions) can see; entries become -1."""
+        s = self._seqs[sid]
+        lo = max(0, s.length - int(q_len) - self.window + 1)
+        blocks = s.blocks
+        for lb in range(min(lo // self.block_size, len(blocks))):
+            if blocks[lb] >= 0:
+                self.alloc.release(blocks[lb])
+                blocks[lb] = -1
+
     def step(self, seq_ids: Sequence[int], q_lens: Sequence[int], width: Optional[int] = None) -> StepBatch:
         """Reserve ``q_lens[i]`` new positions of each listed sequence (in order)
         and return the metadata of the step."""
@@ -218,6 +244,8 @@ class PagedKVManager:
         copies: List[tuple] = []
         for sid, n in zip(seq_ids, q_lens):
             self.append(sid, n, slots, copies)
+            if self.window:
+                self.release_out_of_window(sid, n)
         return StepBatch(
             seq_ids=list(seq_ids),
             slot_mapping=np.asarray(slots, np.int32),

@@ -36,7 +36,8 @@ class CacheDesc(ctypes.Structure):
 class AttendOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("mfma_min_rows", ctypes.c_int32),
                 ("vector_begin", ctypes.c_void_p), ("vector_end", ctypes.c_void_p),
-                ("mfma_begin", ctypes.c_void_p), ("mfma_end", ctypes.c_void_p)]
+                ("mfma_begin", ctypes.c_void_p), ("mfma_end", ctypes.c_void_p),
+                ("window", ctypes.c_int32)]
 
 
 _lib = None
@@ -119,9 +120,10 @@ def _hp(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def _opts(partition_tokens: int = 0, mfma_min_rows: int = 0, events=None) -> AttendOpts:
+def _opts(partition_tokens: int = 0, mfma_min_rows: int = 0, events=None, window: int = 0) -> AttendOpts:
     ev = list(events) if events is not None else [None] * 4
-    return AttendOpts(int(partition_tokens), int(mfma_min_rows), *[None if e is None else int(e) for e in ev])
+    return AttendOpts(int(partition_tokens), int(mfma_min_rows), *[None if e is None else int(e) for e in ev],
+                      int(window))
 
 
 def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, stream=None) -> None:
@@ -143,11 +145,11 @@ def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None
 
 
 def pa_attend_workspace_bytes(k_cache, num_q_heads: int, h_seq_lens, h_q_lens,
-                              partition_tokens: int = 0, mfma_min_rows: int = 0) -> int:
+                              partition_tokens: int = 0, mfma_min_rows: int = 0, window: int = 0) -> int:
     lib = load_library()
     desc = cache_desc(k_cache)
     hl, hq = _host_i32(h_seq_lens), _host_i32(h_q_lens)
-    opts = _opts(partition_tokens, mfma_min_rows)
+    opts = _opts(partition_tokens, mfma_min_rows, window=window)
     n = lib.pa_attend_workspace_bytes(ctypes.byref(desc), int(num_q_heads), len(hl), _hp(hl), _hp(hq),
                                       ctypes.byref(opts))
     if n == 0:
@@ -157,8 +159,11 @@ def pa_attend_workspace_bytes(k_cache, num_q_heads: int, h_seq_lens, h_q_lens,
 
 def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
               out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
-              mfma_min_rows: int = 0, events=None, stream=None) -> torch.Tensor:
+              mfma_min_rows: int = 0, events=None, stream=None, window: int = 0) -> torch.Tensor:
     """Paged attention of the packed batch ``q [T, Hq, D]``; returns ``out [T, Hq, D]`` (fp16).
+
+    ``window`` > 0: each query sees only the last ``window`` keys up to its own
+    position (sliding-window attention); 0 = all of them.
 
     ``events``: optional (vector_begin, vector_end, mfma_begin, mfma_end) raw
     hipEvent_t handles (ints or None) recorded around the two attention kernels."""
@@ -184,7 +189,7 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
         _need(out, "out", torch.float16, 3)
         if out.shape != q.shape:
             raise ValueError("out must match q")
-    opts = _opts(partition_tokens, mfma_min_rows, events)
+    opts = _opts(partition_tokens, mfma_min_rows, events, window)
     need = lib.pa_attend_workspace_bytes(ctypes.byref(desc), q.shape[1], S, _hp(hl), _hp(hq), ctypes.byref(opts))
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)

@@ -23,7 +23,7 @@ from .host import PagedKVManager, StepBatch
 
 def build_manager(w) -> tuple:
     """(manager, sequence ids in the workload's canonical order)."""
-    mgr = PagedKVManager(w.num_blocks, w.block_size, w.first_pops)
+    mgr = PagedKVManager(w.num_blocks, w.block_size, w.first_pops, window=w.window)
     if w.beams is None:
         return mgr, [mgr.add_sequence(int(c)) for c in w.ctx_lens]
     reqs: List[int] = []
@@ -155,13 +155,13 @@ class DeviceRun:
         if workspace is None:
             need = pa.pa_attend_workspace_bytes(self.k_cache, self.w.num_q_heads, x.batch.seq_lens,
                                                 x.batch.q_lens, opts.get("partition_tokens", 0),
-                                                opts.get("mfma_min_rows", 0))
+                                                opts.get("mfma_min_rows", 0), self.w.window)
             if self._ws is None or self._ws.numel() < need:
                 self._ws = torch.empty(2 * need, dtype=torch.uint8, device=self.device)
             workspace = self._ws
         return pa.pa_attend(x.q, self.k_cache, self.v_cache, x.block_tables, x.seq_lens, x.q_lens,
                             x.batch.seq_lens, x.batch.q_lens, self.w.scale, out=out, workspace=workspace,
-                            k_scale=self.k_scale, v_scale=self.v_scale, **opts)
+                            k_scale=self.k_scale, v_scale=self.v_scale, window=self.w.window, **opts)
 
     def run(self, x: StepInputs, **opts) -> torch.Tensor:
         self.write(x)

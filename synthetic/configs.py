@@ -119,6 +119,8 @@ class Workload:
     # int8 pools: the fp16 K/V of the cached context of sequence i, written
     # token by token into the pool before the first step.
     context: Optional[Callable[[int], tuple]] = None
+    # sliding-window attention over this many tokens (0 = full causal)
+    window: int = 0
 
     _cache: dict = field(default_factory=dict, repr=False)
     _step_cache: dict = field(default_factory=dict, repr=False)
@@ -330,7 +332,7 @@ CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
 def custom(seed: int, kv_lens, q_lens, num_q_heads: int = 8, num_kv_heads: int = 2, head_dim: int = 128,
-           kv_dtype: str = "f16", extra_blocks: int = 3, permute: bool = True) -> Workload:
+           kv_dtype: str = "f16", extra_blocks: int = 3, permute: bool = True, window: int = 0) -> Workload:
     """A one-step workload with explicit post-write lengths ``kv_lens`` and
     query rows ``q_lens`` (the cached context is kv_len - q_len tokens).  For
     int8 pools the cached context is drawn as N(0,1) fp16 and written token
@@ -359,5 +361,5 @@ def custom(seed: int, kv_lens, q_lens, num_q_heads: int = 8, num_kv_heads: int =
     return Workload(
         name=f"custom-{seed}", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=BLOCK_SIZE,
         kv_dtype=kv_dtype, scale=1.0 / math.sqrt(d), num_blocks=nb, first_pops=perm, ctx_lens=ctx,
-        pool_draws=draws, steps=[_step(seed, (0,), ql, hq, hkv, d)], context=context,
+        pool_draws=draws, steps=[_step(seed, (0,), ql, hq, hkv, d)], context=context, window=int(window),
     )

@@ -57,7 +57,7 @@ class OracleSide:
 
     def reserve(self, s: int):
         """Reserve step ``s``'s positions: (slot_mapping, copies)."""
-        return opg.apply_step(self.st, self.w.step(s).q_lens)
+        return opg.apply_step(self.st, self.w.step(s).q_lens, self.w.window)
 
     def write(self, s: int, slots, copies) -> None:
         w = self.w
@@ -73,7 +73,7 @@ class OracleSide:
         w = self.w
         step = w.step(s)
         return oatt.paged_attention(step.q, self.K, self.V, self.st.tables, self.st.lens, step.q_lens, w.scale,
-                                    w.block_size, self.KS, self.VS, seqs=seqs)
+                                    w.block_size, self.KS, self.VS, seqs=seqs, window=self.w.window)
 
     def row_ranges(self, s: int):
         q = np.asarray(self.w.step(s).q_lens)

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import synthetic
+from oracle import paging as opg
 from tests.oracle_side import OracleSide, assert_attn_close
 
 pytestmark = pytest.mark.gpu
@@ -27,6 +28,8 @@ def _check_step(run, ora, s, opts_list=({},), check_pool=True):
     assert np.array_equal(x.batch.slot_mapping, slots.astype(np.int32))
     assert [tuple(p) for p in x.batch.copy_pairs.tolist()] == [tuple(p) for p in copies]
     assert np.array_equal(x.batch.seq_lens, np.asarray(ora.st.lens, np.int32))
+    width = x.batch.block_tables.shape[1]
+    assert np.array_equal(x.batch.block_tables, opg.table_array(ora.st, width).astype(np.int32))
     run.write(x)
     ora.write(s, slots, copies)
     torch.cuda.synchronize()

@@ -183,3 +183,38 @@ def test_metadata_matches_oracle_full_size(cfg):
         prefix = st.tables[0][:64]
         assert all(mgr.alloc.refcount(b) == 64 + 16 * 3 for b in prefix)
         assert len(b.copy_pairs) == 3 * sum(1 for r in range(16) if int(w.ctx_lens[r]) % 16)
+
+
+def test_window_release_trace():
+    # the hand-worked trace of the oracle's pin, through the host manager:
+    # block size 4, window 6, first pops 0, 1, 2, ...
+    m = PagedKVManager(8, 4, window=6)
+    s = m.add_sequence(9)                      # blocks [0, 1, 2]
+    b = m.step([s], [1])                       # L=10: keys 4..9 visible -> block 0 released
+    assert m.blocks(s) == [-1, 1, 2] and b.block_tables.tolist() == [[-1, 1, 2]]
+    m.step([s], [3])                           # L=13: positions 12 take block 0 again; keys 7..12
+    assert m.blocks(s) == [-1, 1, 2, 0]
+    m.step([s], [1])                           # L=14: keys 8..13 -> block 1 released
+    assert m.blocks(s) == [-1, -1, 2, 0] and m.alloc.free_ids()[-1] == 1
+    with pytest.raises(ValueError):
+        m.slots(s, 0, 2)                       # released positions have no slots
+    m.finish(s)
+    assert m.alloc.num_free == 8
+
+
+@pytest.mark.parametrize("cfg,window", [(2, 1), (2, 16), (2, 100), (4, 17), (4, 2000), (3, 300), (5, 1000)])
+def test_window_metadata_matches_oracle(cfg, window):
+    w = synthetic.CONFIGS[cfg](**({"decode_steps": 20} if cfg == 2 else {}))
+    w.window = window
+    mgr, ids = build_manager(w)
+    st = opg.build_state(w)
+    for s in range(w.num_steps):
+        q_lens = w.step(s).q_lens
+        b = mgr.step(ids, q_lens)
+        slots, copies = opg.apply_step(st, q_lens, window)
+        assert np.array_equal(b.slot_mapping, slots.astype(np.int32)), f"step {s}"
+        assert [tuple(p) for p in b.copy_pairs.tolist()] == [tuple(p) for p in copies]
+        assert b.seq_lens.tolist() == st.lens
+        assert np.array_equal(b.block_tables, opg.table_array(st, b.block_tables.shape[1]).astype(np.int32))
+        assert mgr.alloc.free_ids() == st.pool.stack
+    assert any(-1 in mgr.blocks(i) for i in ids) == (window < max(st.lens))
