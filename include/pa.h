@@ -22,12 +22,16 @@
  * - KV pool layout (a reading: the pages store K and V either in one per-block
  *   slab, [manager] "Step 1: The Block", or as two tensors, [pytorch]
  *   "Allocate, append, and free KV-cache blocks"): two pools, K and V, each
- *       fp16  [num_blocks][num_kv_heads][block_size][head_dim]   (PA_KV_F16)
- *       int8  [num_blocks][num_kv_heads][block_size][head_dim]   (PA_KV_I8)
- *   so one (block, KV head) tile is one contiguous run of
- *   block_size * head_dim elements.  int8 pools carry per-block-per-head fp16
- *   scales k_scale, v_scale [num_blocks][num_kv_heads] ([engine] "INT8 KV
- *   cache design": symmetric, no zero point, one scale per block per head).
+ *       [num_blocks][num_layers][num_kv_heads][block_size][head_dim]
+ *   of fp16 (PA_KV_F16) or int8 codes (PA_KV_I8), so one (block, layer, KV
+ *   head) tile is one contiguous run of block_size * head_dim elements.  A
+ *   physical block holds its tokens for every layer ([pytorch] "Allocate,
+ *   append, and free KV-cache blocks" keeps the layer axis inside the block),
+ *   so one block table and one slot mapping serve all layers; num_layers = 1
+ *   is the single-layer pool [num_blocks][num_kv_heads][block_size][head_dim].
+ *   int8 pools carry per-block-per-layer-per-head fp16 scales k_scale,
+ *   v_scale [num_blocks][num_layers][num_kv_heads] ([engine] "INT8 KV cache
+ *   design": symmetric, no zero point, one scale per block per head).
  * - Supported shapes: block_size 16, head_dim 64 or 128, num_q_heads a
  *   multiple of num_kv_heads with a group size of 1, 2, 4 or 8,
  *   num_blocks * block_size < 2^31.  Anything else returns
@@ -60,13 +64,18 @@ typedef enum {
 
 typedef enum { PA_KV_F16 = 0, PA_KV_I8 = 1 } pa_kv_dtype;
 
-/* Shape of one KV pool pair (see the layout above). */
+/* Shape of one KV pool pair (see the layout above) and the layer a call
+ * addresses. */
 typedef struct {
   int32_t num_blocks;    /* physical blocks in each pool                  */
   int32_t block_size;    /* tokens per block (16)                         */
   int32_t num_kv_heads;
   int32_t head_dim;      /* 64 or 128                                     */
   int32_t kv_dtype;      /* pa_kv_dtype                                   */
+  int32_t num_layers;    /* layers per block; 0 is taken as 1             */
+  int32_t layer;         /* the layer pa_write_kv / pa_attend address,
+                            0 <= layer < num_layers (pa_copy_blocks copies
+                            every layer of a block and ignores it)        */
 } pa_cache_desc;
 
 /*
@@ -80,8 +89,9 @@ typedef struct {
  *                 A negative slot skips that token (padding).  Slots of one
  *                 call must be distinct.
  *   k_cache, v_cache  the pools (fp16 or int8 codes, per desc->kv_dtype).
- *   k_scale, v_scale  fp16 [num_blocks][num_kv_heads] for PA_KV_I8, else
- *                 ignored (may be NULL).
+ *   k_scale, v_scale  fp16 [num_blocks][num_layers][num_kv_heads] for
+ *                 PA_KV_I8, else ignored (may be NULL).
+ * Rows go to layer desc->layer of the pools; the other layers are untouched.
  *
  * fp16: token t's K/V of every head are copied bit-for-bit to offset
  * slot % block_size of block slot / block_size.
@@ -126,6 +136,17 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v,
  *                     step's queries see (seq_len - q_len - w + 1) are never
  *                     read, so the caller may have released those blocks.
  *                     Negative: PA_ERR_SHAPE.
+ *   reuse_plan        0 = plan the batch (one small kernel that turns the
+ *                     device lengths into work lists in the workspace);
+ *                     1 = use the plan an earlier pa_attend call left in
+ *                     this workspace.  The caller promises that the call is
+ *                     ordered after that one on the device and that the
+ *                     lengths (host and device), the table width, num_q_heads,
+ *                     num_kv_heads and the other options are the same: the
+ *                     case of the layers of one model step, which share the
+ *                     block tables and lengths ([engine] "07 Open items":
+ *                     build the step's block table and batch metadata once
+ *                     per step, not once per layer).
  */
 typedef struct {
   int32_t partition_tokens;
@@ -135,6 +156,7 @@ typedef struct {
   hipEvent_t mfma_begin;
   hipEvent_t mfma_end;
   int32_t window;
+  int32_t reuse_plan;
 } pa_attend_opts;
 
 /*
@@ -191,8 +213,8 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
                     const pa_attend_opts* opts, hipStream_t stream);
 
 /*
- * pa_copy_blocks - copy whole blocks (every KV head, every slot, and the
- * scales of int8 pools) from src to dst, for copy-on-write of a shared block
+ * pa_copy_blocks - copy whole blocks (every layer, every KV head, every slot,
+ * and the scales of int8 pools) from src to dst, for copy-on-write of a shared block
  * before its first divergent write ([pytorch] "Map the PyTorch design to vLLM
  * PagedAttention": shared blocks are copied only on the first divergent write;
  * [manager] "Architecture Overview": the diverging block is duplicated).

@@ -3,9 +3,11 @@
     python -m paged_kv_cache_47_amd.build [--debug]
 
 Every source under ``csrc/`` is compiled to an object (in parallel) and
-linked into ``paged_kv_cache_47_amd/libpa.so``.  Packed-fp32 instructions
-are disabled for every HIP compile; there is no fast-math (the int8 write
-relies on IEEE fp32 division).
+linked into ``paged_kv_cache_47_amd/libpa.so``: ``.hip`` files (kernels and
+the device-side C ABI) with hipcc, ``.cpp`` files (host bookkeeping, no GPU
+code) with the host C++ compiler.  Packed-fp32 instructions are disabled for
+every HIP compile; there is no fast-math (the int8 write relies on IEEE fp32
+division).
 """
 from __future__ import annotations
 
@@ -36,6 +38,16 @@ HIP_FLAGS = [
 FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
 
 
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
+
+def cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and shutil.which(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler found")
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -44,7 +56,7 @@ def hipcc() -> str:
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _run(cmd):
@@ -65,8 +77,11 @@ def build(debug: bool = False, verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        flags = [*HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra]
-        msg = _run([cc, *flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj])
+        if src.endswith(".cpp"):
+            cmd = [cxx(), *CXX_FLAGS, *extra]
+        else:
+            cmd = [cc, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra]
+        msg = _run([*cmd, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj])
         if verbose and msg:
             print(msg, file=sys.stderr)
         return obj

@@ -200,6 +200,7 @@ static pa_status check_desc(const pa_cache_desc* d) {
   if (d == nullptr) return PA_ERR_NULL;
   if (d->kv_dtype != PA_KV_F16 && d->kv_dtype != PA_KV_I8) return PA_ERR_DTYPE;
   if (d->num_blocks <= 0 || d->num_kv_heads <= 0 || d->block_size <= 0 || d->head_dim <= 0) return PA_ERR_SHAPE;
+  if (d->num_layers < 0 || d->layer < 0 || d->layer >= std::max(d->num_layers, 1)) return PA_ERR_SHAPE;
   if (d->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if ((int64_t)d->num_blocks * d->block_size >= ((int64_t)1 << 31)) return PA_ERR_SHAPE;
@@ -380,14 +381,17 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   pl.cap_vtok = (int32_t)P.n_vtok;
   pl.cap_vunit = (int32_t)P.n_vunit;
   pl.cap_munit = (int32_t)P.n_munit;
-  if (launch_plan(pl, stream) != hipSuccess) return PA_ERR_HIP;
+  if (!(opts && opts->reuse_plan) && launch_plan(pl, stream) != hipSuccess) return PA_ERR_HIP;
 
+  // the addressed layer's first tile of block 0; tiles of one block are num_layers * hkv apart
+  const int64_t tile0 = (int64_t)desc->layer * desc->num_kv_heads;
+  const int64_t tile_bytes = (int64_t)kBlockSize * desc->head_dim * (i8 ? 1 : 2);
   AttnArgs a;
   a.q = (const half_t*)q;
-  a.kc = k_cache;
-  a.vc = v_cache;
-  a.ks = (const half_t*)k_scale;
-  a.vs = (const half_t*)v_scale;
+  a.kc = (const char*)k_cache + tile0 * tile_bytes;
+  a.vc = (const char*)v_cache + tile0 * tile_bytes;
+  a.ks = i8 ? (const half_t*)k_scale + tile0 : nullptr;
+  a.vs = i8 ? (const half_t*)v_scale + tile0 : nullptr;
   a.block_tables = block_tables;
   a.seqs = pl.seqs;
   a.vtok = pl.vtok;
@@ -400,6 +404,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.num_blocks = desc->num_blocks;
   a.hq = num_q_heads;
   a.hkv = desc->num_kv_heads;
+  a.blk_tiles = std::max(desc->num_layers, 1) * desc->num_kv_heads;
   a.part = P.part > 0 ? P.part : INT32_MAX / 2;
   a.window = P.window;
   a.scale_log2 = scale * kLog2e;

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   int b = kbeg / kBlockSize + wave;
   auto load_tile = [&](int blk, Dw<ND>* kd, Dw<ND>* vd, int& ph) {
     ph = clamp_block(tbl[blk], a.num_blocks);
-    const int64_t off = ((int64_t)ph * a.hkv + h) * TILE;
+    const int64_t off = ((int64_t)ph * a.blk_tiles + h) * TILE;
     const uint32_t* kt = (const uint32_t*)((const char*)a.kc + off);
     const uint32_t* vt2 = (const uint32_t*)((const char*)a.vc + off);
 #pragma unroll
@@ -184,8 +184,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   auto process = [&](Dw<ND>* kr, Dw<ND>* vr, const int phys, const int blk) {
     float ksc = a.scale_log2, vsc = 1.f;
     if constexpr (I8) {
-      ksc *= scale_at(a.ks, (int64_t)phys * a.hkv + h);
-      vsc = scale_at(a.vs, (int64_t)phys * a.hkv + h);
+      ksc *= scale_at(a.ks, (int64_t)phys * a.blk_tiles + h);
+      vsc = scale_at(a.vs, (int64_t)phys * a.blk_tiles + h);
     }
     const int tok0 = blk * kBlockSize + grp;
     // wave-uniform: the last block of the range, or the block the window starts in

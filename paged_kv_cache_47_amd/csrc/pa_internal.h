@@ -50,6 +50,8 @@ struct AttnArgs {
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t hq, hkv;
+  int32_t blk_tiles;   // (layer, KV head) tiles per physical block: num_layers * hkv;
+                       // kc/vc/ks/vs point at the addressed layer's first tile of block 0
   int32_t part;        // keys per partition (a multiple of 16)
   int32_t window;      // sliding window in keys; 0 = none
   float scale_log2;    // scale * log2(e)

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int64_t sidx =
-            (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.kb[kb]), a.num_blocks) * a.hkv + h;
+            (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.kb[kb]), a.num_blocks) * a.blk_tiles + h;
         nks[kb] = (float)(a.ks + sidx)[vz];
       }
     }
@@ -158,7 +158,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
       const int c = (threadIdx.x + NTH * i) % NCH;   // threads past the chunks repeat the first ones
       const int key = c / CPR, ch = c % CPR;
       const int kg = min(max(kt + key, klo), L - 1);
-      const int64_t tile = (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.chunk[i]), a.num_blocks) * a.hkv + h;
+      const int64_t tile =
+          (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.chunk[i]), a.num_blocks) * a.blk_tiles + h;
       if constexpr (I8) nvc[i] = (float)(a.vs + tile)[vz];
       const uint32_t off = (uint32_t)((kg % kBlockSize) * D * EB + ch * 16);
       stk[i] = *(const uint4*)((const char*)a.kc + tile * kTileBytes + off);

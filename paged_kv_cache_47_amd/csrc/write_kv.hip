@@ -9,14 +9,27 @@
 
 namespace pa {
 
+// Pools hold every layer of a block: tile (block, layer, head) starts at
+// ((block * num_layers + layer) * hkv + head) * block_size * head_dim.  The
+// launchers offset the pool (and scale) pointers to the addressed layer's
+// first tile, so kernels index tiles as block * blk_tiles + head with
+// blk_tiles = num_layers * hkv.
+__host__ __device__ inline int64_t layer_tile0(const pa_cache_desc& d) {
+  return (int64_t)d.layer * d.num_kv_heads;
+}
+__host__ __device__ inline int32_t blk_tiles_of(const pa_cache_desc& d) {
+  return (d.num_layers > 0 ? d.num_layers : 1) * d.num_kv_heads;
+}
+
 // ---------------------------------------------------------------- fp16 ----
 // One thread moves 16 bytes (8 halves) of one token's K and V for one head.
 // Consecutive threads cover consecutive 16-byte chunks of a token row, so both
 // the read of k/v and the write into the block are contiguous per token-head.
 __global__ __launch_bounds__(256) void write_f16_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                         const int32_t* __restrict__ slots, int32_t T,
-                                                        int32_t hkv, int32_t chunks_per_row, int64_t num_slots,
-                                                        uint4* __restrict__ kc, uint4* __restrict__ vc) {
+                                                        int32_t hkv, int32_t blk_tiles, int32_t chunks_per_row,
+                                                        int64_t num_slots, uint4* __restrict__ kc,
+                                                        uint4* __restrict__ vc) {
   const int64_t per_token = (int64_t)hkv * chunks_per_row;
   const int64_t n = (int64_t)T * per_token;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
@@ -27,7 +40,7 @@ __global__ __launch_bounds__(256) void write_f16_kernel(const uint4* __restrict_
     const int32_t s = slots[t];
     if (s < 0 || s >= num_slots) continue;
     const int64_t blk = s / kBlockSize, off = s % kBlockSize;
-    const int64_t dst = ((blk * hkv + h) * kBlockSize + off) * chunks_per_row + c;
+    const int64_t dst = ((blk * blk_tiles + h) * kBlockSize + off) * chunks_per_row + c;
     kc[dst] = k[i];
     vc[dst] = v[i];
   }
@@ -39,8 +52,10 @@ hipError_t launch_write_f16(const pa_cache_desc& d, const void* k, const void* v
   const int64_t n = (int64_t)T * d.num_kv_heads * cpr;
   const int64_t blocks = (n + 255) / 256;
   const int grid = (int)(blocks < 65536 ? blocks : 65536);
-  write_f16_kernel<<<grid, 256, 0, s>>>((const uint4*)k, (const uint4*)v, slots, T, d.num_kv_heads, cpr,
-                                        (int64_t)d.num_blocks * kBlockSize, (uint4*)kc, (uint4*)vc);
+  const int64_t off = layer_tile0(d) * kBlockSize * cpr;   // in 16-byte chunks
+  write_f16_kernel<<<grid, 256, 0, s>>>((const uint4*)k, (const uint4*)v, slots, T, d.num_kv_heads, blk_tiles_of(d),
+                                        cpr, (int64_t)d.num_blocks * kBlockSize, (uint4*)kc + off,
+                                        (uint4*)vc + off);
   return hipGetLastError();
 }
 
@@ -56,13 +71,14 @@ hipError_t launch_write_f16(const pa_cache_desc& d, const void* k, const void* v
 // a CPU evaluation of the same formula bit for bit.
 template <int D>
 __device__ void replay_run_i8(const half_t* __restrict__ src, const int32_t s, const int t, const int n,
-                              const int h, const int hkv, int8_t* __restrict__ cache, half_t* __restrict__ scales) {
+                              const int h, const int hkv, const int blk_tiles, int8_t* __restrict__ cache,
+                              half_t* __restrict__ scales) {
   constexpr int EPL = D / 64;  // dims per lane: 2 (d128) or 1 (d64)
   const int lane = threadIdx.x;
   const int64_t blk = s / kBlockSize;
   const int o0 = s % kBlockSize;
-  int8_t* tile = cache + (blk * hkv + h) * (int64_t)kBlockSize * D;
-  const int64_t sidx = blk * hkv + h;
+  int8_t* tile = cache + (blk * blk_tiles + h) * (int64_t)kBlockSize * D;
+  const int64_t sidx = blk * blk_tiles + h;
 
   float c[kBlockSize][EPL];
   float sc = (float)scales[sidx];
@@ -114,7 +130,7 @@ constexpr int kI8Window = 8;
 template <int D>
 __global__ __launch_bounds__(64) void write_i8_kernel(const half_t* __restrict__ k, const half_t* __restrict__ v,
                                                       const int32_t* __restrict__ slots, int32_t T, int32_t hkv,
-                                                      int64_t num_slots, int8_t* __restrict__ kc,
+                                                      int32_t blk_tiles, int64_t num_slots, int8_t* __restrict__ kc,
                                                       int8_t* __restrict__ vc, half_t* __restrict__ ks,
                                                       half_t* __restrict__ vs) {
   const int h = blockIdx.y, which = blockIdx.z;
@@ -128,7 +144,7 @@ __global__ __launch_bounds__(64) void write_i8_kernel(const half_t* __restrict__
     if (t > 0 && (s % kBlockSize) != 0 && slots[t - 1] == s - 1) continue;  // inside a run started earlier
     int n = 1;
     while (t + n < T && ((s + n) % kBlockSize) != 0 && slots[t + n] == s + n) ++n;
-    replay_run_i8<D>(src, s, t, n, h, hkv, cache, scales);
+    replay_run_i8<D>(src, s, t, n, h, hkv, blk_tiles, cache, scales);
   }
 }
 
@@ -136,22 +152,27 @@ hipError_t launch_write_i8(const pa_cache_desc& d, const void* k, const void* v,
                            int32_t T, void* kc, void* vc, void* ks, void* vs, hipStream_t s) {
   dim3 grid((T + kI8Window - 1) / kI8Window, d.num_kv_heads, 2);
   const int64_t ns = (int64_t)d.num_blocks * kBlockSize;
+  const int64_t t0 = layer_tile0(d), off = t0 * kBlockSize * d.head_dim;
+  const int bt = blk_tiles_of(d);
   if (d.head_dim == 128)
-    write_i8_kernel<128><<<grid, 64, 0, s>>>((const half_t*)k, (const half_t*)v, slots, T, d.num_kv_heads, ns,
-                                             (int8_t*)kc, (int8_t*)vc, (half_t*)ks, (half_t*)vs);
+    write_i8_kernel<128><<<grid, 64, 0, s>>>((const half_t*)k, (const half_t*)v, slots, T, d.num_kv_heads, bt, ns,
+                                             (int8_t*)kc + off, (int8_t*)vc + off, (half_t*)ks + t0,
+                                             (half_t*)vs + t0);
   else
-    write_i8_kernel<64><<<grid, 64, 0, s>>>((const half_t*)k, (const half_t*)v, slots, T, d.num_kv_heads, ns,
-                                            (int8_t*)kc, (int8_t*)vc, (half_t*)ks, (half_t*)vs);
+    write_i8_kernel<64><<<grid, 64, 0, s>>>((const half_t*)k, (const half_t*)v, slots, T, d.num_kv_heads, bt, ns,
+                                            (int8_t*)kc + off, (int8_t*)vc + off, (half_t*)ks + t0,
+                                            (half_t*)vs + t0);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------- block copies ----
 // blockIdx.x = pair; threads stride over the 16-byte chunks of the K and V
-// tiles of every head of the source block, then copy the int8 scales.
+// tiles of every layer and head of the source block, then copy the int8
+// scales (one per layer and head).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kc, uint4* __restrict__ vc,
                                                           half_t* __restrict__ ks, half_t* __restrict__ vs,
                                                           const int32_t* __restrict__ pairs, int32_t num_blocks,
-                                                          int32_t chunks_per_block, int32_t hkv) {
+                                                          int32_t chunks_per_block, int32_t blk_tiles) {
   const int32_t src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
   if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
   const int64_t so = (int64_t)src * chunks_per_block, d = (int64_t)dst * chunks_per_block;
@@ -160,9 +181,9 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kc
     vc[d + i] = vc[so + i];
   }
   if (ks != nullptr) {
-    for (int i = threadIdx.x; i < hkv; i += blockDim.x) {
-      ks[(int64_t)dst * hkv + i] = ks[(int64_t)src * hkv + i];
-      vs[(int64_t)dst * hkv + i] = vs[(int64_t)src * hkv + i];
+    for (int i = threadIdx.x; i < blk_tiles; i += blockDim.x) {
+      ks[(int64_t)dst * blk_tiles + i] = ks[(int64_t)src * blk_tiles + i];
+      vs[(int64_t)dst * blk_tiles + i] = vs[(int64_t)src * blk_tiles + i];
     }
   }
 }
@@ -170,10 +191,10 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ kc
 hipError_t launch_copy(const pa_cache_desc& d, void* kc, void* vc, void* ks, void* vs, const int32_t* pairs,
                        int32_t n, hipStream_t s) {
   const int eb = d.kv_dtype == PA_KV_I8 ? 1 : 2;
-  const int chunks = d.num_kv_heads * kBlockSize * d.head_dim * eb / 16;
+  const int chunks = blk_tiles_of(d) * kBlockSize * d.head_dim * eb / 16;
   const bool i8 = d.kv_dtype == PA_KV_I8;
   copy_blocks_kernel<<<n, 256, 0, s>>>((uint4*)kc, (uint4*)vc, i8 ? (half_t*)ks : nullptr, i8 ? (half_t*)vs : nullptr,
-                                       pairs, d.num_blocks, chunks, d.num_kv_heads);
+                                       pairs, d.num_blocks, chunks, blk_tiles_of(d));
   return hipGetLastError();
 }
 

@@ -10,14 +10,12 @@ and the current HIP stream); host length arrays are numpy int32.
 from __future__ import annotations
 
 import ctypes
-import os
 from typing import Optional
 
 import numpy as np
 import torch
 
-_HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+from ._lib import LIB_PATH, LibraryMissing, cdll
 
 PA_KV_F16 = 0
 PA_KV_I8 = 1
@@ -27,17 +25,21 @@ class PagedAttentionError(RuntimeError):
     pass
 
 
+class LibraryNotBuilt(PagedAttentionError, LibraryMissing):
+    pass
+
+
 class CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32)]
+                ("kv_dtype", ctypes.c_int32), ("num_layers", ctypes.c_int32), ("layer", ctypes.c_int32)]
 
 
 class AttendOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("mfma_min_rows", ctypes.c_int32),
                 ("vector_begin", ctypes.c_void_p), ("vector_end", ctypes.c_void_p),
                 ("mfma_begin", ctypes.c_void_p), ("mfma_end", ctypes.c_void_p),
-                ("window", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("reuse_plan", ctypes.c_int32)]
 
 
 _lib = None
@@ -48,10 +50,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(path):
-        raise PagedAttentionError(
-            f"{path} is missing: build it with `python -m paged_kv_cache_47_amd.build` (there is no fallback)")
-    lib = ctypes.CDLL(path)
+    try:
+        lib = cdll(path)
+    except LibraryMissing as e:
+        raise LibraryNotBuilt(str(e)) from None
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pdesc, popts = ctypes.POINTER(CacheDesc), ctypes.POINTER(AttendOpts)
     pi32 = ctypes.POINTER(ctypes.c_int32)
@@ -98,18 +100,30 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
-    """Descriptor of a pool shaped [num_blocks, num_kv_heads, block_size, head_dim]."""
-    if k_cache.dim() != 4:
-        raise ValueError("pools are [num_blocks, num_kv_heads, block_size, head_dim]")
+def cache_desc(k_cache: torch.Tensor, layer: int = 0) -> CacheDesc:
+    """Descriptor of a pool shaped [num_blocks, num_kv_heads, block_size, head_dim]
+    (one layer) or [num_blocks, num_layers, num_kv_heads, block_size, head_dim],
+    addressing ``layer``."""
+    if k_cache.dim() not in (4, 5):
+        raise ValueError("pools are [num_blocks, (num_layers,) num_kv_heads, block_size, head_dim]")
     if k_cache.dtype == torch.float16:
         kind = PA_KV_F16
     elif k_cache.dtype == torch.int8:
         kind = PA_KV_I8
     else:
         raise TypeError(f"pool dtype {k_cache.dtype} is neither float16 nor int8")
-    nb, hkv, bs, d = k_cache.shape
-    return CacheDesc(nb, bs, hkv, d, kind)
+    if k_cache.dim() == 4:
+        nb, hkv, bs, d = k_cache.shape
+        nl = 1
+    else:
+        nb, nl, hkv, bs, d = k_cache.shape
+    if not 0 <= int(layer) < nl:
+        raise ValueError(f"layer {layer} outside the pool's {nl} layers")
+    return CacheDesc(nb, bs, hkv, d, kind, nl, int(layer))
+
+
+def _scale_dims(k_cache: torch.Tensor) -> int:
+    return 2 if k_cache.dim() == 4 else 3
 
 
 def _host_i32(a) -> np.ndarray:
@@ -120,32 +134,38 @@ def _hp(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def _opts(partition_tokens: int = 0, mfma_min_rows: int = 0, events=None, window: int = 0) -> AttendOpts:
+def _opts(partition_tokens: int = 0, mfma_min_rows: int = 0, events=None, window: int = 0,
+          reuse_plan: bool = False) -> AttendOpts:
     ev = list(events) if events is not None else [None] * 4
     return AttendOpts(int(partition_tokens), int(mfma_min_rows), *[None if e is None else int(e) for e in ev],
-                      int(window))
+                      int(window), int(bool(reuse_plan)))
 
 
-def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, stream=None) -> None:
-    """Write new K/V rows ``k, v [T, Hkv, D]`` (fp16) into the pools through ``slot_mapping [T]``."""
+def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, stream=None,
+                layer: int = 0) -> None:
+    """Write new K/V rows ``k, v [T, Hkv, D]`` (fp16) into layer ``layer`` of the
+    pools through ``slot_mapping [T]``."""
     lib = load_library()
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, layer)
     _need(k, "k", torch.float16, 3)
     _need(v, "v", torch.float16, 3)
     _need(slot_mapping, "slot_mapping", torch.int32, 1)
-    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(v_cache, "v_cache", k_cache.dtype, k_cache.dim())
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
     T = k.shape[0]
     if tuple(k.shape) != (T, desc.num_kv_heads, desc.head_dim) or v.shape != k.shape or slot_mapping.shape[0] != T:
         raise ValueError("k, v must be [T, num_kv_heads, head_dim] with one slot per row")
     if desc.kv_dtype == PA_KV_I8:
-        _need(k_scale, "k_scale", torch.float16, 2)
-        _need(v_scale, "v_scale", torch.float16, 2)
+        _need(k_scale, "k_scale", torch.float16, _scale_dims(k_cache))
+        _need(v_scale, "v_scale", torch.float16, _scale_dims(k_cache))
     _check(lib.pa_write_kv(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache),
                            _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _stream(stream)), "pa_write_kv")
 
 
 def pa_attend_workspace_bytes(k_cache, num_q_heads: int, h_seq_lens, h_q_lens,
                               partition_tokens: int = 0, mfma_min_rows: int = 0, window: int = 0) -> int:
+    """Workspace bytes pa_attend needs for this batch (the same for every layer)."""
     lib = load_library()
     desc = cache_desc(k_cache)
     hl, hq = _host_i32(h_seq_lens), _host_i32(h_q_lens)
@@ -159,18 +179,24 @@ def pa_attend_workspace_bytes(k_cache, num_q_heads: int, h_seq_lens, h_q_lens,
 
 def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
               out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
-              mfma_min_rows: int = 0, events=None, stream=None, window: int = 0) -> torch.Tensor:
+              mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
+              reuse_plan: bool = False) -> torch.Tensor:
     """Paged attention of the packed batch ``q [T, Hq, D]``; returns ``out [T, Hq, D]`` (fp16).
 
     ``window`` > 0: each query sees only the last ``window`` keys up to its own
-    position (sliding-window attention); 0 = all of them.
+    position (sliding-window attention); 0 = all of them.  ``layer``: the
+    layer of a multi-layer pool.  ``reuse_plan``: take the work lists an
+    earlier call (same lengths and options, e.g. the previous layer of the
+    step) left in ``workspace`` instead of planning again.
 
     ``events``: optional (vector_begin, vector_end, mfma_begin, mfma_end) raw
     hipEvent_t handles (ints or None) recorded around the two attention kernels."""
     lib = load_library()
-    desc = cache_desc(k_cache)
+    desc = cache_desc(k_cache, layer)
     _need(q, "q", torch.float16, 3)
-    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(v_cache, "v_cache", k_cache.dtype, k_cache.dim())
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     _need(q_lens, "q_lens", torch.int32, 1)
@@ -181,17 +207,19 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
     if q.shape[2] != desc.head_dim or int(hq.sum()) != q.shape[0]:
         raise ValueError("q must be [sum(q_lens), num_q_heads, head_dim]")
     if desc.kv_dtype == PA_KV_I8:
-        _need(k_scale, "k_scale", torch.float16, 2)
-        _need(v_scale, "v_scale", torch.float16, 2)
+        _need(k_scale, "k_scale", torch.float16, _scale_dims(k_cache))
+        _need(v_scale, "v_scale", torch.float16, _scale_dims(k_cache))
     if out is None:
         out = torch.empty_like(q)
     else:
         _need(out, "out", torch.float16, 3)
         if out.shape != q.shape:
             raise ValueError("out must match q")
-    opts = _opts(partition_tokens, mfma_min_rows, events, window)
+    opts = _opts(partition_tokens, mfma_min_rows, events, window, reuse_plan)
     need = lib.pa_attend_workspace_bytes(ctypes.byref(desc), q.shape[1], S, _hp(hl), _hp(hq), ctypes.byref(opts))
     if workspace is None:
+        if reuse_plan:
+            raise ValueError("reuse_plan needs the workspace of the call that planned")
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
     _check(lib.pa_attend(ctypes.byref(desc), _ptr(q), q.shape[1], _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                          _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(q_lens), S,
@@ -201,15 +229,17 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
 
 
 def pa_copy_blocks(k_cache, v_cache, src_dst, k_scale=None, v_scale=None, stream=None) -> None:
-    """Copy whole blocks for copy-on-write: ``src_dst [n, 2]`` int32 (src, dst) pairs."""
+    """Copy whole blocks (every layer and head) for copy-on-write: ``src_dst [n, 2]`` int32 (src, dst) pairs."""
     lib = load_library()
     desc = cache_desc(k_cache)
-    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(v_cache, "v_cache", k_cache.dtype, k_cache.dim())
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
     _need(src_dst, "src_dst", torch.int32, 2)
     if src_dst.shape[1] != 2:
         raise ValueError("src_dst must be [n, 2]")
     if desc.kv_dtype == PA_KV_I8:
-        _need(k_scale, "k_scale", torch.float16, 2)
-        _need(v_scale, "v_scale", torch.float16, 2)
+        _need(k_scale, "k_scale", torch.float16, _scale_dims(k_cache))
+        _need(v_scale, "v_scale", torch.float16, _scale_dims(k_cache))
     _check(lib.pa_copy_blocks(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                               _ptr(src_dst), src_dst.shape[0], _stream(stream)), "pa_copy_blocks")

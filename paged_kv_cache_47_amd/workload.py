@@ -8,6 +8,10 @@ each) and beam requests are then forked; int8 pools get their cached context
 written token by token through ``pa_write_kv``.  A step reserves the new
 positions (growing tables, copy-on-write of shared blocks), then runs
 ``pa_copy_blocks`` -> ``pa_write_kv`` -> ``pa_attend`` on the current stream.
+With several layers the pools hold every layer of a block; one step's
+metadata serves all layers, and each layer's write and attention follow
+each other (as in a model), the attention of layers after the first reusing
+the first layer's plan.
 """
 from __future__ import annotations
 
@@ -62,6 +66,7 @@ class DeviceRun:
         self.k_cache = torch.from_numpy(w.pool_k).to(self.device)
         self.v_cache = torch.from_numpy(w.pool_v).to(self.device)
         self.i8 = w.kv_dtype == "i8"
+        self.layers = int(w.num_layers)
         self.k_scale = torch.from_numpy(w.pool_k_scale).to(self.device) if self.i8 else None
         self.v_scale = torch.from_numpy(w.pool_v_scale).to(self.device) if self.i8 else None
         if w.context is not None:
@@ -102,13 +107,17 @@ class DeviceRun:
     def _write_context(self, batch_tokens: int) -> None:
         pend_k, pend_v, pend_s, n = [], [], [], 0
 
+        ax = 0 if self.layers == 1 else 1   # token axis of the context draws
+
         def flush():
             nonlocal pend_k, pend_v, pend_s, n
             if n:
-                k = torch.from_numpy(np.concatenate(pend_k)).to(self.device)
-                v = torch.from_numpy(np.concatenate(pend_v)).to(self.device)
+                k = torch.from_numpy(np.concatenate(pend_k, axis=ax)).to(self.device)
+                v = torch.from_numpy(np.concatenate(pend_v, axis=ax)).to(self.device)
                 s = torch.from_numpy(np.concatenate(pend_s)).to(self.device)
-                pa.pa_write_kv(k, v, s, self.k_cache, self.v_cache, self.k_scale, self.v_scale)
+                for layer in range(self.layers):
+                    kl, vl = (k, v) if self.layers == 1 else (k[layer], v[layer])
+                    pa.pa_write_kv(kl, vl, s, self.k_cache, self.v_cache, self.k_scale, self.v_scale, layer=layer)
             pend_k, pend_v, pend_s, n = [], [], [], 0
 
         for i, sid in enumerate(self.ids):
@@ -126,7 +135,8 @@ class DeviceRun:
 
     def activations(self, s: int) -> tuple:
         """Step ``s``'s new K, new V and queries on the device (what a model
-        would hand over), drawn and copied outside any timed region."""
+        would hand over; a leading layer axis with several layers), drawn and
+        copied outside any timed region."""
         st = self.w.step(s)
         d = self.device
         return tuple(torch.from_numpy(np.ascontiguousarray(a)).to(d) for a in (st.new_k, st.new_v, st.q))
@@ -146,12 +156,27 @@ class DeviceRun:
         sm, cp, bt, sl, ql = self._upload_i32([b.slot_mapping, b.copy_pairs, b.block_tables, b.seq_lens, b.q_lens])
         return StepInputs(b, sm, cp, bt, sl, ql, nk, nv, q)
 
-    def write(self, x: StepInputs) -> None:
+    def layer_acts(self, x: StepInputs, layer: int) -> tuple:
+        if self.layers == 1:
+            return x.new_k, x.new_v, x.q
+        return x.new_k[layer], x.new_v[layer], x.q[layer]
+
+    def copy(self, x: StepInputs) -> None:
+        """The step's copy-on-write block copies (every layer of each block)."""
         if x.copy_pairs.shape[0]:
             pa.pa_copy_blocks(self.k_cache, self.v_cache, x.copy_pairs, self.k_scale, self.v_scale)
-        pa.pa_write_kv(x.new_k, x.new_v, x.slot_mapping, self.k_cache, self.v_cache, self.k_scale, self.v_scale)
 
-    def attend(self, x: StepInputs, out=None, workspace=None, **opts) -> torch.Tensor:
+    def write_layer(self, x: StepInputs, layer: int) -> None:
+        nk, nv, _ = self.layer_acts(x, layer)
+        pa.pa_write_kv(nk, nv, x.slot_mapping, self.k_cache, self.v_cache, self.k_scale, self.v_scale, layer=layer)
+
+    def write(self, x: StepInputs) -> None:
+        """Copies, then every layer's KV write."""
+        self.copy(x)
+        for layer in range(self.layers):
+            self.write_layer(x, layer)
+
+    def attend(self, x: StepInputs, out=None, workspace=None, layer: int = 0, **opts) -> torch.Tensor:
         if workspace is None:
             need = pa.pa_attend_workspace_bytes(self.k_cache, self.w.num_q_heads, x.batch.seq_lens,
                                                 x.batch.q_lens, opts.get("partition_tokens", 0),
@@ -159,10 +184,20 @@ class DeviceRun:
             if self._ws is None or self._ws.numel() < need:
                 self._ws = torch.empty(2 * need, dtype=torch.uint8, device=self.device)
             workspace = self._ws
-        return pa.pa_attend(x.q, self.k_cache, self.v_cache, x.block_tables, x.seq_lens, x.q_lens,
-                            x.batch.seq_lens, x.batch.q_lens, self.w.scale, out=out, workspace=workspace,
-                            k_scale=self.k_scale, v_scale=self.v_scale, window=self.w.window, **opts)
+        return pa.pa_attend(self.layer_acts(x, layer)[2], self.k_cache, self.v_cache, x.block_tables, x.seq_lens,
+                            x.q_lens, x.batch.seq_lens, x.batch.q_lens, self.w.scale, out=out, workspace=workspace,
+                            k_scale=self.k_scale, v_scale=self.v_scale, window=self.w.window, layer=layer, **opts)
 
-    def run(self, x: StepInputs, **opts) -> torch.Tensor:
-        self.write(x)
-        return self.attend(x, **opts)
+    def run(self, x: StepInputs, **opts):
+        """One step: copies, then per layer its write and its attention (the
+        layers after the first reuse the first one's plan).  Returns the
+        output (one layer) or the list of per-layer outputs."""
+        if self.layers == 1:
+            self.write(x)
+            return self.attend(x, **opts)
+        self.copy(x)
+        outs = []
+        for layer in range(self.layers):
+            self.write_layer(x, layer)
+            outs.append(self.attend(x, layer=layer, reuse_plan=layer > 0, **opts))
+        return outs

@@ -32,7 +32,7 @@ BLOCK_SIZE = 16
 CHUNK = 1 << 20  # elements per independently seeded draw chunk
 
 # stream ids inside one workload's seed
-S_META, S_POOL_K, S_POOL_V, S_NEW_K, S_NEW_V, S_Q, S_KSCALE, S_VSCALE, S_CTX_K, S_CTX_V = range(10)
+S_META, S_POOL_K, S_POOL_V, S_NEW_K, S_NEW_V, S_Q, S_KSCALE, S_VSCALE, S_CTX_K, S_CTX_V, S_LAYERS = range(11)
 
 
 def _threads() -> int:
@@ -121,6 +121,9 @@ class Workload:
     context: Optional[Callable[[int], tuple]] = None
     # sliding-window attention over this many tokens (0 = full causal)
     window: int = 0
+    # layers per block: pools [NB, layers, Hkv, bs, D] and per-layer step
+    # activations [layers, T, H, D] when > 1 (one block table for all layers)
+    num_layers: int = 1
 
     _cache: dict = field(default_factory=dict, repr=False)
     _step_cache: dict = field(default_factory=dict, repr=False)
@@ -164,6 +167,13 @@ class Workload:
             return self._step_cache[s]
         return self.steps[s]
 
+    def layer_acts(self, s: int, layer: int) -> tuple:
+        """(new_k, new_v, q) of step ``s`` for one layer."""
+        st = self.step(s)
+        if self.num_layers == 1:
+            return st.new_k, st.new_v, st.q
+        return st.new_k[layer], st.new_v[layer], st.q[layer]
+
     @property
     def num_seqs(self) -> int:
         if self.beams is not None:
@@ -175,20 +185,39 @@ def _ceil_div(a, b):
     return -(-a // b)
 
 
-def _f16_pool(seed, nb, hkv, d):
+def _lk(layers):
+    """Shape prefix and key suffix of per-layer draws (none for one layer)."""
+    return ((), ()) if layers == 1 else ((layers,), (S_LAYERS,))
+
+
+def _f16_pool(seed, nb, hkv, d, layers=1):
+    _, key = _lk(layers)
+    shape = (nb, hkv, BLOCK_SIZE, d) if layers == 1 else (nb, layers, hkv, BLOCK_SIZE, d)
     return {
-        "k": lambda: normal_f16((seed, S_POOL_K), (nb, hkv, BLOCK_SIZE, d)),
-        "v": lambda: normal_f16((seed, S_POOL_V), (nb, hkv, BLOCK_SIZE, d)),
+        "k": lambda: normal_f16((seed, S_POOL_K, *key), shape),
+        "v": lambda: normal_f16((seed, S_POOL_V, *key), shape),
     }
 
 
-def _step(seed, tag, q_lens, hq, hkv, d):
+def _i8_pool(seed, nb, hkv, d, layers=1):
+    _, key = _lk(layers)
+    lead = (nb,) if layers == 1 else (nb, layers)
+    return {
+        "k": lambda: uniform_i8((seed, S_POOL_K, *key), (*lead, hkv, BLOCK_SIZE, d)),
+        "v": lambda: uniform_i8((seed, S_POOL_V, *key), (*lead, hkv, BLOCK_SIZE, d)),
+        "k_scale": lambda: uniform_scale_f16((seed, S_KSCALE, *key), (*lead, hkv)),
+        "v_scale": lambda: uniform_scale_f16((seed, S_VSCALE, *key), (*lead, hkv)),
+    }
+
+
+def _step(seed, tag, q_lens, hq, hkv, d, layers=1):
     t = int(np.sum(q_lens))
+    lead, key = _lk(layers)
     return StepDraw(
         q_lens=np.asarray(q_lens, np.int64),
-        new_k=normal_f16((seed, S_NEW_K, *tag), (t, hkv, d)),
-        new_v=normal_f16((seed, S_NEW_V, *tag), (t, hkv, d)),
-        q=normal_f16((seed, S_Q, *tag), (t, hq, d)),
+        new_k=normal_f16((seed, S_NEW_K, *tag, *key), (*lead, t, hkv, d)),
+        new_v=normal_f16((seed, S_NEW_V, *tag, *key), (*lead, t, hkv, d)),
+        q=normal_f16((seed, S_Q, *tag, *key), (*lead, t, hq, d)),
     )
 
 
@@ -211,10 +240,12 @@ def config1(seed: int = 47001) -> Workload:
 
 
 def config2(seed: int = 47002, num_seqs: int = 32, min_prompt: int = 32, max_prompt: int = 512,
-            decode_steps: int = 64) -> Workload:
+            decode_steps: int = 64, num_layers: int = 1) -> Workload:
     """GPT-2-small-shaped batch: 12/12 heads, d64; prompts U[32,512] prefilled
     (step 0, causal), then ``decode_steps`` steps of one token per sequence.
-    Plain free list (first pops 0, 1, 2, ...); blocks grow on demand."""
+    Plain free list (first pops 0, 1, 2, ...); blocks grow on demand.
+    ``num_layers`` > 1 (GPT-2 small has 12): a multi-layer pool and per-layer
+    activations over the same tables."""
     hq = hkv = 12
     d = 64
     rng = np.random.default_rng([seed, S_META])
@@ -223,15 +254,15 @@ def config2(seed: int = 47002, num_seqs: int = 32, min_prompt: int = 32, max_pro
 
     def steps(s):
         if s == 0:
-            return _step(seed, (0,), prompts, hq, hkv, d)
-        return _step(seed, (s,), np.ones(num_seqs, np.int64), hq, hkv, d)
+            return _step(seed, (0,), prompts, hq, hkv, d, num_layers)
+        return _step(seed, (s,), np.ones(num_seqs, np.int64), hq, hkv, d, num_layers)
 
     return Workload(
         name="gpt2-continuous-batch", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
         block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
         first_pops=None, ctx_lens=np.zeros(num_seqs, np.int64),
-        pool_draws=_f16_pool(seed, nb, hkv, d),
-        steps=steps, num_steps=1 + decode_steps,
+        pool_draws=_f16_pool(seed, nb, hkv, d, num_layers),
+        steps=steps, num_steps=1 + decode_steps, num_layers=num_layers,
     )
 
 
@@ -332,11 +363,14 @@ CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
 def custom(seed: int, kv_lens, q_lens, num_q_heads: int = 8, num_kv_heads: int = 2, head_dim: int = 128,
-           kv_dtype: str = "f16", extra_blocks: int = 3, permute: bool = True, window: int = 0) -> Workload:
+           kv_dtype: str = "f16", extra_blocks: int = 3, permute: bool = True, window: int = 0,
+           num_layers: int = 1) -> Workload:
     """A one-step workload with explicit post-write lengths ``kv_lens`` and
     query rows ``q_lens`` (the cached context is kv_len - q_len tokens).  For
     int8 pools the cached context is drawn as N(0,1) fp16 and written token
-    by token before the step; fp16 pools hold N(0,1) everywhere."""
+    by token before the step; fp16 pools hold N(0,1) everywhere.  With
+    ``num_layers`` > 1 every draw gets a leading layer axis (after the block
+    axis in the pools)."""
     hq, hkv, d = num_q_heads, num_kv_heads, head_dim
     post = np.asarray(kv_lens, np.int64)
     ql = np.asarray(q_lens, np.int64)
@@ -344,22 +378,20 @@ def custom(seed: int, kv_lens, q_lens, num_q_heads: int = 8, num_kv_heads: int =
     nb = int(np.sum(_ceil_div(post, BLOCK_SIZE))) + extra_blocks
     rng = np.random.default_rng([seed, S_META])
     perm = rng.permutation(nb) if permute else None
+    lead, key = _lk(num_layers)
     if kv_dtype == "i8":
-        draws = {
-            "k": lambda: uniform_i8((seed, S_POOL_K), (nb, hkv, BLOCK_SIZE, d)),
-            "v": lambda: uniform_i8((seed, S_POOL_V), (nb, hkv, BLOCK_SIZE, d)),
-            "k_scale": lambda: uniform_scale_f16((seed, S_KSCALE), (nb, hkv)),
-            "v_scale": lambda: uniform_scale_f16((seed, S_VSCALE), (nb, hkv)),
-        }
+        draws = _i8_pool(seed, nb, hkv, d, num_layers)
 
         def context(i):
             n = int(ctx[i])
-            return (normal_f16((seed, S_CTX_K, i), (n, hkv, d)), normal_f16((seed, S_CTX_V, i), (n, hkv, d)))
+            return (normal_f16((seed, S_CTX_K, i, *key), (*lead, n, hkv, d)),
+                    normal_f16((seed, S_CTX_V, i, *key), (*lead, n, hkv, d)))
     else:
-        draws = _f16_pool(seed, nb, hkv, d)
+        draws = _f16_pool(seed, nb, hkv, d, num_layers)
         context = None
     return Workload(
         name=f"custom-{seed}", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=BLOCK_SIZE,
         kv_dtype=kv_dtype, scale=1.0 / math.sqrt(d), num_blocks=nb, first_pops=perm, ctx_lens=ctx,
-        pool_draws=draws, steps=[_step(seed, (0,), ql, hq, hkv, d)], context=context, window=int(window),
+        pool_draws=draws, steps=[_step(seed, (0,), ql, hq, hkv, d, num_layers)], context=context,
+        window=int(window), num_layers=int(num_layers),
     )

@@ -52,8 +52,17 @@ class OracleSide:
                     c = int(w.ctx_lens[i])
                     if c:
                         ck, cv = w.context(i)
-                        okv.fill_context_i8(self.K, self.V, self.KS, self.VS, self.st.tables[i], ck, cv,
-                                            w.block_size)
+                        for layer in range(w.num_layers):
+                            K, V, KS, VS = self._layer(layer)
+                            lk, lv = (ck, cv) if w.num_layers == 1 else (ck[layer], cv[layer])
+                            okv.fill_context_i8(K, V, KS, VS, self.st.tables[i], lk, lv, w.block_size)
+
+    def _layer(self, layer: int):
+        """Views of one layer's pools and scales ([NB, Hkv, bs, D] / [NB, Hkv])."""
+        if self.w.num_layers == 1:
+            return self.K, self.V, self.KS, self.VS
+        pick = (lambda a: None if a is None else a[:, layer])
+        return pick(self.K), pick(self.V), pick(self.KS), pick(self.VS)
 
     def reserve(self, s: int):
         """Reserve step ``s``'s positions: (slot_mapping, copies)."""
@@ -61,19 +70,21 @@ class OracleSide:
 
     def write(self, s: int, slots, copies) -> None:
         w = self.w
-        step = w.step(s)
-        okv.copy_blocks([self.K, self.V, self.KS, self.VS], copies)
-        if w.kv_dtype == "i8":
-            self.K, self.V, self.KS, self.VS = okv.write_i8(self.K, self.V, self.KS, self.VS, step.new_k,
-                                                          step.new_v, slots, w.block_size)
-        else:
-            self.K, self.V = okv.write_f16(self.K, self.V, step.new_k, step.new_v, slots, w.block_size)
+        okv.copy_blocks([self.K, self.V, self.KS, self.VS], copies)   # whole blocks: every layer
+        for layer in range(w.num_layers):
+            nk, nv, _ = w.layer_acts(s, layer)
+            K, V, KS, VS = self._layer(layer)
+            if w.kv_dtype == "i8":
+                K[...], V[...], KS[...], VS[...] = okv.write_i8(K, V, KS, VS, nk, nv, slots, w.block_size)
+            else:
+                K[...], V[...] = okv.write_f16(K, V, nk, nv, slots, w.block_size)
 
-    def attend(self, s: int, seqs=None) -> np.ndarray:
+    def attend(self, s: int, seqs=None, layer: int = 0) -> np.ndarray:
         w = self.w
         step = w.step(s)
-        return oatt.paged_attention(step.q, self.K, self.V, self.st.tables, self.st.lens, step.q_lens, w.scale,
-                                    w.block_size, self.KS, self.VS, seqs=seqs, window=self.w.window)
+        K, V, KS, VS = self._layer(layer)
+        return oatt.paged_attention(w.layer_acts(s, layer)[2], K, V, self.st.tables, self.st.lens, step.q_lens,
+                                    w.scale, w.block_size, KS, VS, seqs=seqs, window=self.w.window)
 
     def row_ranges(self, s: int):
         q = np.asarray(self.w.step(s).q_lens)

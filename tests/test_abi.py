@@ -19,14 +19,16 @@ def _declared():
         if f.endswith(".h"):
             with open(os.path.join(ROOT, "include", f)) as fh:
                 src = fh.read()
-            names += re.findall(r"^\s*(?:pa_status|size_t|const char\*)\s+(pa_\w+)\s*\(", src, re.M)
+            names += re.findall(r"^\s*(?:pa_status|size_t|const char\*|int32_t|void|pa_mgr\*)\s+(pa_\w+)\s*\(",
+                                src, re.M)
     return names
 
 
 def test_exports_every_declared_symbol():
     lib = pa.load_library()
     names = _declared()
-    assert {"pa_write_kv", "pa_attend", "pa_attend_workspace_bytes", "pa_copy_blocks", "pa_status_str"} <= set(names)
+    assert {"pa_write_kv", "pa_attend", "pa_attend_workspace_bytes", "pa_copy_blocks", "pa_status_str",
+            "pa_mgr_create", "pa_mgr_step", "pa_mgr_destroy", "pa_host_status_str"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -120,3 +122,13 @@ def test_library_is_newer_than_its_sources():
             for f in os.listdir(d)]
     newest = max(os.path.getmtime(p) for p in srcs)
     assert os.path.getmtime(lib) >= newest, "libpa.so is older than its sources"
+
+
+def test_layer_validation():
+    d = _desc()
+    d.num_layers, d.layer = 3, 3
+    assert _attend(d, 4, [5], [1], 4) == 2            # layer outside the pool
+    d.num_layers, d.layer = -1, 0
+    assert _attend(d, 4, [5], [1], 4) == 2
+    d.num_layers, d.layer = 3, 2
+    assert _attend(d, 4, [5], [1], 4, ws_bytes=8) == 5   # a valid layer: validation reaches the workspace check

@@ -1,0 +1,131 @@
+"""Multi-layer pools on the GPU, through the C ABI, against the oracle.
+
+[pytorch] "Allocate, append, and free KV-cache blocks" keeps the layer axis
+inside each physical block ([num_blocks, num_layers, ...]), so one block
+table, one slot mapping and one set of lengths serve every layer of a step;
+[engine] "07 Open items" asks for that metadata to be built once per step
+rather than once per layer.  Covered: per-layer writes land in their own
+layer only (whole pools bit-exact), per-layer attention on both paths and
+with split-K, fp16 and int8 (per-layer scales), the plan of the first layer
+reused by the others (outputs bit-identical to planning each layer), block
+copies that carry every layer, and several decode steps.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import kv_write as okv
+from oracle import paging as opg
+from tests.oracle_side import OracleSide, assert_attn_close
+from tests.test_gpu_parity import SPLITS
+
+pytestmark = pytest.mark.gpu
+
+LENS = [1, 2, 15, 16, 17, 33, 100, 257, 700, 90]
+QLS = [1, 1, 1, 1, 2, 3, 16, 40, 1, 90]
+
+
+def _run(w):
+    from paged_kv_cache_47_amd.workload import DeviceRun
+    return DeviceRun(w)
+
+
+def _check_layers(run, ora, s, opts_list=({},)):
+    w = run.w
+    x = run.prepare(s)
+    slots, copies = ora.reserve(s)
+    assert np.array_equal(x.batch.slot_mapping, slots.astype(np.int32))
+    assert [tuple(p) for p in x.batch.copy_pairs.tolist()] == [tuple(p) for p in copies]
+    width = x.batch.block_tables.shape[1]
+    assert np.array_equal(x.batch.block_tables, opg.table_array(ora.st, width).astype(np.int32))
+    outs = run.run(x)              # per layer: write, attend (layers after the first reuse the plan)
+    outs = outs if isinstance(outs, list) else [outs]
+    ora.write(s, slots, copies)
+    torch.cuda.synchronize()
+    assert np.array_equal(run.k_cache.cpu().numpy(), ora.K)
+    assert np.array_equal(run.v_cache.cpu().numpy(), ora.V)
+    if w.kv_dtype == "i8":
+        assert np.array_equal(run.k_scale.cpu().numpy().view(np.uint16), ora.KS.view(np.uint16))
+        assert np.array_equal(run.v_scale.cpu().numpy().view(np.uint16), ora.VS.view(np.uint16))
+    for layer in range(w.num_layers):
+        ref = ora.attend(s, layer=layer)
+        assert_attn_close(outs[layer].cpu().numpy(), ref, w.kv_dtype == "i8", f"{w.name} step {s} layer {layer}")
+        for opts in opts_list:
+            out = run.attend(x, layer=layer, **opts)
+            torch.cuda.synchronize()
+            assert_attn_close(out.cpu().numpy(), ref, w.kv_dtype == "i8", f"layer {layer} {opts}")
+    return x, outs
+
+
+@pytest.mark.parametrize("dt,layers", [("f16", 3), ("i8", 2), ("f16", 1)])
+def test_layers_mixed_batch(dt, layers):
+    w = synthetic.custom(600 + layers, LENS, QLS, 8, 2, 128, dt, num_layers=layers)
+    _check_layers(_run(w), OracleSide(w), 0, SPLITS + ({"mfma_min_rows": 1}, {"mfma_min_rows": 2 ** 31 - 1}))
+
+
+def test_layers_gpt2_shape_prefill_then_decode():
+    w = synthetic.config2(num_seqs=5, min_prompt=20, max_prompt=130, decode_steps=4, num_layers=4)
+    run, ora = _run(w), OracleSide(w)
+    for s in range(5):
+        _check_layers(run, ora, s, ({"partition_tokens": 16},) if s else ())
+
+
+def test_reused_plan_gives_the_same_outputs():
+    w = synthetic.custom(610, LENS, QLS, 8, 2, 128, num_layers=3)
+    run = _run(w)
+    x = run.prepare(0)
+    run.write(x)
+    for opts in ({}, {"partition_tokens": 64}, {"mfma_min_rows": 1}):
+        ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+        planned = [run.attend(x, layer=l, workspace=ws, **opts).clone() for l in range(3)]
+        reused = [run.attend(x, layer=0, workspace=ws, **opts).clone()]
+        reused += [run.attend(x, layer=l, workspace=ws, reuse_plan=True, **opts).clone() for l in (1, 2)]
+        torch.cuda.synchronize()
+        for a, b in zip(planned, reused):
+            assert torch.equal(a, b), opts
+        assert not torch.equal(planned[0], planned[1])    # the layers do differ
+
+
+@pytest.mark.parametrize("dt", ["f16", "i8"])
+def test_copy_blocks_carry_every_layer(dt):
+    from paged_kv_cache_47_amd import pa
+    rng = np.random.default_rng(15)
+    nb, nl, hkv, d = 12, 3, 4, 64
+    if dt == "f16":
+        K = rng.standard_normal((nb, nl, hkv, 16, d)).astype(np.float16)
+        V = rng.standard_normal((nb, nl, hkv, 16, d)).astype(np.float16)
+        KS = VS = None
+    else:
+        K = rng.integers(-127, 128, (nb, nl, hkv, 16, d)).astype(np.int8)
+        V = rng.integers(-127, 128, (nb, nl, hkv, 16, d)).astype(np.int8)
+        KS = rng.uniform(0.01, 0.05, (nb, nl, hkv)).astype(np.float16)
+        VS = rng.uniform(0.01, 0.05, (nb, nl, hkv)).astype(np.float16)
+    pairs = [(0, 5), (3, 7), (3, 8), (11, 1)]
+    dev = [None if a is None else torch.from_numpy(a.copy()).cuda() for a in (K, V, KS, VS)]
+    pa.pa_copy_blocks(dev[0], dev[1], torch.tensor(pairs, dtype=torch.int32, device="cuda"), dev[2], dev[3])
+    okv.copy_blocks([K, V, KS, VS], pairs)
+    torch.cuda.synchronize()
+    for a, t in zip((K, V, KS, VS), dev):
+        if a is not None:
+            assert np.array_equal(t.cpu().numpy(), a)
+
+
+def test_write_touches_only_its_layer():
+    from paged_kv_cache_47_amd import pa
+    rng = np.random.default_rng(16)
+    nb, nl, hkv, d = 6, 4, 2, 128
+    K = rng.standard_normal((nb, nl, hkv, 16, d)).astype(np.float16)
+    V = rng.standard_normal((nb, nl, hkv, 16, d)).astype(np.float16)
+    nk = rng.standard_normal((3, hkv, d)).astype(np.float16)
+    nv = rng.standard_normal((3, hkv, d)).astype(np.float16)
+    slots = np.array([3, 40, 95], np.int32)
+    kc, vc = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda()
+    pa.pa_write_kv(torch.from_numpy(nk).cuda(), torch.from_numpy(nv).cuda(), torch.from_numpy(slots).cuda(), kc, vc,
+                   layer=2)
+    K[:, 2], V[:, 2] = okv.write_f16(K[:, 2], V[:, 2], nk, nv, slots, 16)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), K) and np.array_equal(vc.cpu().numpy(), V)
+    with pytest.raises(ValueError):
+        pa.pa_write_kv(torch.from_numpy(nk).cuda(), torch.from_numpy(nv).cuda(), torch.from_numpy(slots).cuda(),
+                       kc, vc, layer=4)

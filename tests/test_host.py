@@ -218,3 +218,97 @@ def test_window_metadata_matches_oracle(cfg, window):
         assert np.array_equal(b.block_tables, opg.table_array(st, b.block_tables.shape[1]).astype(np.int32))
         assert mgr.alloc.free_ids() == st.pool.stack
     assert any(-1 in mgr.blocks(i) for i in ids) == (window < max(st.lens))
+
+
+def _snapshot(m, ids):
+    return ([m.blocks(s) for s in ids], [m.seq_len(s) for s in ids], m.alloc.free_ids(),
+            m.alloc.refcounts().tolist())
+
+
+def test_step_is_atomic_when_the_pool_runs_out():
+    m = PagedKVManager(6, 4)
+    a = m.add_sequence(7)                     # 2 blocks
+    b = m.add_sequence(4)                     # 1 block
+    c = m.fork(a)                             # shares a's 2 blocks
+    before = _snapshot(m, [a, b, c])
+    # a: copy of the shared block 1 (pos 7) + a new block (pos 8); c: then sole owner of block 1,
+    # a new block for pos 8; b: 2 new blocks -> 5 > 3 free
+    with pytest.raises(KVCacheExhausted):
+        m.step([a, c, b], [2, 2, 5])
+    assert _snapshot(m, [a, b, c]) == before
+    with pytest.raises(ValueError):           # a sequence listed twice
+        m.step([a, a], [1, 1])
+    with pytest.raises(ValueError):           # a table narrower than the step needs
+        m.step([a], [2], width=2)
+    assert _snapshot(m, [a, b, c]) == before
+    x = m.step([a, c, b], [2, 2, 0])          # 2 + 1 + 0 blocks: fits exactly
+    assert m.alloc.num_free == 0 and x.copy_pairs.tolist() == [[1, 3]]
+
+
+def test_window_release_counts_toward_the_same_step():
+    # a block one sequence's window releases is free for the later sequences of that step
+    m = PagedKVManager(4, 4, window=2)
+    a = m.add_sequence(6)                     # blocks [0, 1]
+    b = m.add_sequence(8)                     # blocks [2, 3]: the pool is full
+    before = _snapshot(m, [a, b])
+    with pytest.raises(KVCacheExhausted):     # b first: it needs a block before anything is released
+        m.step([b, a], [1, 2])
+    assert _snapshot(m, [a, b]) == before
+    x = m.step([a, b], [2, 1])                # a: L=8, keys 5.. -> block 0 released; b takes it for pos 8
+    assert x.slot_mapping.tolist() == [6, 7, 0]
+    assert m.blocks(a) == [-1, 1] and m.blocks(b) == [-1, 3, 0]   # b: L=9, keys 7.. -> its block 2 released
+    assert m.alloc.free_ids() == [2]
+
+
+def _oracle_finish(st, i):
+    for b in st.tables[i]:
+        if b >= 0:
+            st.pool.release(b)
+    st.tables[i] = []
+
+
+@pytest.mark.parametrize("seed,window", [(1, 0), (2, 0), (3, 5), (4, 17), (5, 1)])
+def test_random_interleavings_match_the_oracle(seed, window):
+    rng = np.random.default_rng(seed)
+    nb, bs = 96, 4
+    perm = rng.permutation(nb)
+    m = PagedKVManager(nb, bs, first_pops=perm, window=window)
+    st = opg.RefState(nb, bs, first_pops=perm)
+    live = []
+    for _ in range(300):
+        op = rng.integers(0, 10)
+        if op < 2 and m.alloc.num_free >= 8:
+            n = int(rng.integers(0, 20))
+            live.append(m.add_sequence(n))
+            assert st.add(n) == live[-1]
+        elif op < 3 and live and not window:
+            src = live[int(rng.integers(len(live)))]
+            live.append(m.fork(src))
+            assert st.fork(src) == live[-1]
+        elif op < 4 and live:
+            sid = live.pop(int(rng.integers(len(live))))
+            m.finish(sid)
+            _oracle_finish(st, sid)
+        elif live:
+            k = int(rng.integers(1, len(live) + 1))
+            sids = [int(s) for s in rng.choice(live, size=k, replace=False)]
+            qls = [int(q) for q in rng.integers(0, 6, size=k)]
+            pool_before = list(st.pool.stack)
+            try:
+                b = m.step(sids, qls)
+            except KVCacheExhausted:
+                st.pool.stack = pool_before
+                assert m.alloc.free_ids() == st.pool.stack
+                continue
+            slots, copies = [], []
+            for s, q in zip(sids, qls):
+                sl, cp = st.append(s, q)
+                slots += sl
+                copies += cp
+                if window:
+                    opg.release_out_of_window(st, s, q, window)
+            assert b.slot_mapping.tolist() == slots
+            assert [tuple(p) for p in b.copy_pairs.tolist()] == copies
+        for s in live:
+            assert m.blocks(s) == st.tables[s] and m.seq_len(s) == st.lens[s]
+        assert m.alloc.free_ids() == st.pool.stack
