@@ -172,7 +172,12 @@ def cpu_baseline(w, step: int, budget_s: float):
     for s in range(step + 1):
         opg.apply_step(st, w.step(s).q_lens, w.window)
     sd = w.step(step)
+    q_all = w.layer_acts(step, 0)[2]                 # layer 0 of a multi-layer pool
     K, V = w.pool_k, w.pool_v
+    KS, VS = w.pool_k_scale, w.pool_v_scale
+    if w.num_layers > 1:
+        K, V = K[:, 0], V[:, 0]
+        KS, VS = (None, None) if KS is None else (KS[:, 0], VS[:, 0])
     bs = w.block_size
     eb = 1 if w.kv_dtype == "i8" else 2
     starts = np.concatenate([[0], np.cumsum(sd.q_lens)[:-1]])
@@ -181,10 +186,10 @@ def cpu_baseline(w, step: int, budget_s: float):
     for i in range(len(st.tables)):
         L, Q = st.lens[i], int(sd.q_lens[i])
         lo = oatt.window_start(L, Q, w.window)
-        Kc = oatt.gather(K, st.tables[i], L, bs, w.pool_k_scale, lo)
-        Vc = oatt.gather(V, st.tables[i], L, bs, w.pool_v_scale, lo)
+        Kc = oatt.gather(K, st.tables[i], L, bs, KS, lo)
+        Vc = oatt.gather(V, st.tables[i], L, bs, VS, lo)
         if Q:
-            oatt.attend(sd.q[starts[i]:starts[i] + Q], oatt.query_positions(L, Q), Kc, Vc, w.scale,
+            oatt.attend(q_all[starts[i]:starts[i] + Q], oatt.query_positions(L, Q), Kc, Vc, w.scale,
                         w.window, lo)
         done += 1
         kv_bytes += (L - lo) * w.num_kv_heads * w.head_dim * 2 * eb
@@ -197,7 +202,8 @@ def cpu_baseline(w, step: int, budget_s: float):
         "sample": f"first {done} of {len(st.tables)} sequences ({kv_bytes / 1e6:.1f} MB of KV), attention only "
                   f"(numpy fp64, BLAS threads={os.environ.get('OMP_NUM_THREADS', 'default')}), {dt:.1f} s"
                   + (" (on the pool as drawn: the int8 context replay is not part of the timed oracle work)"
-                     if w.kv_dtype == "i8" else ""),
+                     if w.kv_dtype == "i8" else "")
+                  + (" (layer 0 of the multi-layer pool)" if w.num_layers > 1 else ""),
         "seq_steps_per_s": round(done / dt, 3),
     }
 
@@ -325,17 +331,10 @@ def summarize_trace(stats_csv: str, out: str, cmd: str, title: str, alg_bytes: i
         f.write("\n".join(lines) + "\n")
 
 
-def end_to_end(args, w) -> dict:
-    """Workload 2 run as a server would: the prefill step, then every decode
-    step with its host bookkeeping (table growth, slot mapping), the copies of
-    its metadata and new rows to the device, the KV write and the attention.
-    Wall time over all steps (host included) and device time per step."""
+def _warm_clocks() -> None:
+    """About 0.2 s of unrelated device work: set-up leaves the GPU idle long
+    enough to drop its clocks."""
     import torch
-    from paged_kv_cache_47_amd.workload import DeviceRun
-    run = DeviceRun(w)
-    acts = [run.activations(s) for s in range(w.num_steps)]   # the model's outputs, already on the device
-    # the set-up above leaves the GPU idle long enough to drop its clocks: bring them back with ~0.2 s
-    # of unrelated device work before timing
     a_ = torch.randn(4096, 4096, device="cuda", dtype=torch.float16)
     t_warm = time.perf_counter()
     while time.perf_counter() - t_warm < 0.2:
@@ -344,34 +343,81 @@ def end_to_end(args, w) -> dict:
         torch.cuda.synchronize()
     del a_
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.num_steps)]
-    for a_, b_ in ev:
-        a_.record()
-        b_.record()
-    torch.cuda.synchronize()
-    x = run.prepare(0, acts=acts[0])
-    ev[0][0].record()
-    run.run(x)
-    ev[0][1].record()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(1, w.num_steps):
-        x = run.prepare(s, acts=acts[s])
-        ev[s][0].record()
+
+
+def end_to_end(args, w) -> dict:
+    """Workload 2 run as a server would: the prefill step, then every decode
+    step with its host bookkeeping (table growth, slot mapping), the copy of
+    its metadata to the device, the KV writes and the attention of every
+    layer.  Three ways to issue a decode step, each from a fresh pool:
+
+    * eager: ``DeviceRun.prepare`` + ``run`` (the manager's step into numpy
+      arrays, one packed metadata upload, the library calls marshalled anew);
+    * prepared: ``StaticSteps`` (the native step straight into pinned memory,
+      one copy to fixed device buffers, prepared library calls);
+    * graph: the same, with the step's calls captured once in a HIP graph
+      shaped for the largest length the run reaches, and replayed.
+
+    Wall time over the decode steps (host included) and device time per step
+    (events around each step's device work)."""
+    import torch
+    from paged_kv_cache_47_amd.workload import DeviceRun, StaticSteps
+    out = {"layers": w.num_layers, "decode_steps": w.num_steps - 1}
+    for mode in ("eager", "prepared", "graph"):
+        run = DeviceRun(w)
+        acts = [run.activations(s) for s in range(w.num_steps)]   # the model's outputs, already on the device
+        x = run.prepare(0, acts=acts[0])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         run.run(x)
-        ev[s][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dev = [a_.elapsed_time(b_) for a_, b_ in ev]
-    seqs = len(run.ids)
-    dec = w.num_steps - 1
-    return {"prefill_ms": round(dev[0], 5), "decode_steps": dec, "seq_steps": seqs * dec,
-            "wall_s_decode_steps": round(wall, 5),
-            "seq_steps_per_s_wall": round(seqs * dec / wall, 1),
-            "seq_steps_per_s_device": round(seqs * dec / (sum(dev[1:]) * 1e-3), 1),
-            "note": "wall: host bookkeeping + metadata H2D + write + attend of every decode step "
-                    "(new K/V and queries already on the device); "
-                    "device: the write + attend events of each decode step; prefill: the first step's events"}
+        e1.record()
+        torch.cuda.synchronize()
+        prefill_ms = e0.elapsed_time(e1)
+        width = -(-(int(x.batch.seq_lens.max()) + w.num_steps - 1) // w.block_size)
+        st = None
+        if mode != "eager":
+            st = StaticSteps(run, width, partition_tokens=256)
+            if mode == "graph":
+                st.capture()
+        _warm_clocks()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(w.num_steps)]
+        for a_, b_ in ev:
+            a_.record()
+            b_.record()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(1, w.num_steps):
+            if mode == "eager":
+                x = run.prepare(s, acts=acts[s])
+                ev[s][0].record()
+                run.run(x)
+            else:
+                st.set_activations(acts=acts[s])
+                st.host_step(exact_lengths=mode == "prepared")
+                ev[s][0].record()
+                st.launch() if mode == "prepared" else st.replay()
+            ev[s][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        dev = [a_.elapsed_time(b_) for a_, b_ in ev[1:]]
+        seqs = len(run.ids)
+        dec = w.num_steps - 1
+        out[mode] = {"seq_steps_per_s_wall": round(seqs * dec / wall, 1),
+                     "seq_steps_per_s_device": round(seqs * dec / (sum(dev) * 1e-3), 1),
+                     "wall_ms_per_step": round(wall / dec * 1e3, 4),
+                     "device_ms_per_step": round(float(np.mean(dev)), 5)}
+        if mode == "eager":
+            out["prefill_ms"] = round(prefill_ms, 5)
+        del st, run, acts, x
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    out["seq_steps"] = len(w.ctx_lens) * (w.num_steps - 1)
+    out["note"] = ("a seq-step is one new token of one sequence through the KV write and attention of every "
+                   "layer; wall: host bookkeeping + metadata copy + device work of every decode step, with the new "
+                   "K/V and queries already on the device (copied into the fixed buffers in the prepared and "
+                   "graph modes); device: events around each step's device work")
+    return out
 
 
 def main(argv=None) -> int:
@@ -388,6 +434,9 @@ def main(argv=None) -> int:
                          "(default: for working sets under 512 MB, workloads 1, 2 and 4)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window attention over this many keys (0: full causal attention)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="workload 2 only: layers per block (GPT-2 small has 12); a step writes and attends "
+                         "every layer over one set of metadata")
     ap.add_argument("--no-share", action="store_true",
                     help="workload 4 control: every sequence owns its own copy of the prefix (no sharing, no forks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -437,7 +486,15 @@ def main(argv=None) -> int:
     from paged_kv_cache_47_amd.workload import DeviceRun
 
     torch.cuda.set_device(0)
-    w = synthetic.config4(share=False) if (args.workload == 4 and args.no_share) else synthetic.CONFIGS[args.workload]()
+    if args.layers != 1 and args.workload != 2:
+        print("--layers applies to workload 2 only", file=sys.stderr)
+        return 2
+    if args.workload == 4 and args.no_share:
+        w = synthetic.config4(share=False)
+    elif args.workload == 2:
+        w = synthetic.config2(num_layers=args.layers)
+    else:
+        w = synthetic.CONFIGS[args.workload]()
     w.window = args.window
     run = DeviceRun(w)
     step_index = 0
@@ -450,7 +507,7 @@ def main(argv=None) -> int:
     L = x.batch.seq_lens.astype(np.int64)
     Q = x.batch.q_lens.astype(np.int64)
     vec_bytes, mfma_flops, kv_bytes = work_split(w, L, Q)
-    out = torch.empty_like(x.q)
+    kv_bytes *= w.num_layers                     # the step attends every layer
     need = pa.pa_attend_workspace_bytes(run.k_cache, w.num_q_heads, x.batch.seq_lens, x.batch.q_lens,
                                         partition_tokens=args.partition_tokens, window=w.window)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
@@ -459,12 +516,29 @@ def main(argv=None) -> int:
     evs.record_all(torch.cuda.current_stream().cuda_stream)   # first records are slow: do them untimed
     torch.cuda.synchronize()
 
+    # every step's library calls, marshalled once before anything is timed: copies (if any), then per
+    # layer the KV write and the attention (layers after the first reuse the first one's plan); the
+    # timed variant records the kernel events around the first layer's attention kernels
+    kc, vc, ks, vs = run.k_cache, run.v_cache, run.k_scale, run.v_scale
+    outs = [torch.empty_like(run.layer_acts(x, l)[2]) for l in range(w.num_layers)]
+
+    def step_calls(i, timed_kernel):
+        calls = [pa.prepare_copy_blocks(kc, vc, x.copy_pairs, ks, vs)] if x.copy_pairs.shape[0] else []
+        for layer in range(w.num_layers):
+            nk, nv, q = run.layer_acts(x, layer)
+            ev = tuple(evs.handle(4 * i + j) for j in range(4)) if (timed_kernel and layer == 0) else None
+            calls.append(pa.prepare_write_kv(nk, nv, x.slot_mapping, kc, vc, ks, vs, layer=layer))
+            calls.append(pa.prepare_attend(q, kc, vc, x.block_tables, x.seq_lens, x.q_lens, x.batch.seq_lens,
+                                           x.batch.q_lens, w.scale, out=outs[layer], workspace=ws, k_scale=ks,
+                                           v_scale=vs, partition_tokens=args.partition_tokens, events=ev,
+                                           window=w.window, layer=layer, reuse_plan=layer > 0))
+        return calls
+
+    prepared = {(i, tk): step_calls(i, tk) for i in range(n) for tk in (True, False)}
+
     def step(i, timed_kernel=True):
-        run.write(x)
-        ev = tuple(evs.handle(4 * i + j) for j in range(4)) if timed_kernel else None
-        pa.pa_attend(x.q, run.k_cache, run.v_cache, x.block_tables, x.seq_lens, x.q_lens, x.batch.seq_lens,
-                     x.batch.q_lens, w.scale, out=out, workspace=ws, k_scale=run.k_scale, v_scale=run.v_scale,
-                     partition_tokens=args.partition_tokens, events=ev, window=w.window)
+        for c in prepared[(i, timed_kernel)]:
+            c()
 
     # the region's own events, created and recorded once before anything is timed
     t0 = torch.cuda.Event(enable_timing=True)
@@ -558,10 +632,12 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload] + (" [control: every sequence owns its prefix copy]"
                                                           if args.workload == 4 and args.no_share else "")
-                   + (f" [sliding window of {args.window} keys]" if args.window else ""),
+                   + (f" [sliding window of {args.window} keys]" if args.window else "")
+                   + (f" [{w.num_layers} layers per block: every step writes and attends each]"
+                      if w.num_layers > 1 else ""),
                    "num_seqs": S, "kv_tokens": int(L.sum()),
                    "query_rows": int(Q.sum()), "num_blocks": w.num_blocks,
-                   "partition_tokens": args.partition_tokens, "window": args.window},
+                   "partition_tokens": args.partition_tokens, "window": args.window, "layers": w.num_layers},
         "pct_of_peak": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "seq_steps_per_s": round(S / (ms * 1e-3), 1),
         "ms_per_step_without_kernel_events": round(ms_plain, 5),

@@ -56,12 +56,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise LibraryNotBuilt(str(e)) from None
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pdesc, popts = ctypes.POINTER(CacheDesc), ctypes.POINTER(AttendOpts)
-    pi32 = ctypes.POINTER(ctypes.c_int32)
     lib.pa_write_kv.argtypes = [pdesc, vp, vp, vp, i32, vp, vp, vp, vp, vp]
     lib.pa_write_kv.restype = ctypes.c_int
-    lib.pa_attend_workspace_bytes.argtypes = [pdesc, i32, i32, pi32, pi32, popts]
+    lib.pa_attend_workspace_bytes.argtypes = [pdesc, i32, i32, vp, vp, popts]
     lib.pa_attend_workspace_bytes.restype = sz
-    lib.pa_attend.argtypes = [pdesc, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, pi32, pi32,
+    lib.pa_attend.argtypes = [pdesc, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp,
                               ctypes.c_float, vp, vp, sz, popts, vp]
     lib.pa_attend.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [pdesc, vp, vp, vp, vp, vp, i32, vp]
@@ -141,10 +140,30 @@ def _opts(partition_tokens: int = 0, mfma_min_rows: int = 0, events=None, window
                       int(window), int(bool(reuse_plan)))
 
 
-def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, stream=None,
-                layer: int = 0) -> None:
-    """Write new K/V rows ``k, v [T, Hkv, D]`` (fp16) into layer ``layer`` of the
-    pools through ``slot_mapping [T]``."""
+class PreparedCall:
+    """One library call whose arguments were checked and marshalled once;
+    calling it issues the same call again (same pointers, sizes, options and
+    stream).  The tensors and host arrays it refers to must stay alive and at
+    the same addresses; their contents may change between calls."""
+    __slots__ = ("fn", "args", "what", "keep")
+
+    def __init__(self, fn, args, what, keep=()):
+        self.fn, self.args, self.what, self.keep = fn, args, what, keep
+
+    def __call__(self) -> None:
+        st = self.fn(*self.args)
+        if st:
+            _check(st, self.what)
+
+
+def _host_addr(a: np.ndarray) -> int:
+    return a.__array_interface__["data"][0]
+
+
+def prepare_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, stream=None,
+                     layer: int = 0) -> PreparedCall:
+    """``pa_write_kv`` of new K/V rows ``k, v [T, Hkv, D]`` (fp16) into layer
+    ``layer`` of the pools through ``slot_mapping [T]``, as a prepared call."""
     lib = load_library()
     desc = cache_desc(k_cache, layer)
     _need(k, "k", torch.float16, 3)
@@ -159,8 +178,16 @@ def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None
     if desc.kv_dtype == PA_KV_I8:
         _need(k_scale, "k_scale", torch.float16, _scale_dims(k_cache))
         _need(v_scale, "v_scale", torch.float16, _scale_dims(k_cache))
-    _check(lib.pa_write_kv(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache),
-                           _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _stream(stream)), "pa_write_kv")
+    args = (ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache),
+            _ptr(k_scale), _ptr(v_scale), _stream(stream))
+    return PreparedCall(lib.pa_write_kv, args, "pa_write_kv", (desc,))
+
+
+def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, stream=None,
+                layer: int = 0) -> None:
+    """Write new K/V rows ``k, v [T, Hkv, D]`` (fp16) into layer ``layer`` of the
+    pools through ``slot_mapping [T]``."""
+    prepare_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream, layer)()
 
 
 def pa_attend_workspace_bytes(k_cache, num_q_heads: int, h_seq_lens, h_q_lens,
@@ -170,27 +197,22 @@ def pa_attend_workspace_bytes(k_cache, num_q_heads: int, h_seq_lens, h_q_lens,
     desc = cache_desc(k_cache)
     hl, hq = _host_i32(h_seq_lens), _host_i32(h_q_lens)
     opts = _opts(partition_tokens, mfma_min_rows, window=window)
-    n = lib.pa_attend_workspace_bytes(ctypes.byref(desc), int(num_q_heads), len(hl), _hp(hl), _hp(hq),
-                                      ctypes.byref(opts))
+    n = lib.pa_attend_workspace_bytes(ctypes.byref(desc), int(num_q_heads), len(hl), _host_addr(hl),
+                                      _host_addr(hq), ctypes.byref(opts))
     if n == 0:
         raise PagedAttentionError("pa_attend_workspace_bytes: invalid arguments")
     return int(n)
 
 
-def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
-              out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
-              mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
-              reuse_plan: bool = False) -> torch.Tensor:
-    """Paged attention of the packed batch ``q [T, Hq, D]``; returns ``out [T, Hq, D]`` (fp16).
-
-    ``window`` > 0: each query sees only the last ``window`` keys up to its own
-    position (sliding-window attention); 0 = all of them.  ``layer``: the
-    layer of a multi-layer pool.  ``reuse_plan``: take the work lists an
-    earlier call (same lengths and options, e.g. the previous layer of the
-    step) left in ``workspace`` instead of planning again.
-
-    ``events``: optional (vector_begin, vector_end, mfma_begin, mfma_end) raw
-    hipEvent_t handles (ints or None) recorded around the two attention kernels."""
+def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
+                   out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
+                   mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
+                   reuse_plan: bool = False) -> PreparedCall:
+    """``pa_attend`` as a prepared call (arguments as for ``pa_attend``; the
+    output tensor is the call's ``keep[0]``).  ``h_seq_lens`` and ``h_q_lens``
+    are passed by address: when they are int32 numpy arrays they are used in
+    place, so a caller may update them between calls (the device lengths
+    must match them at each call)."""
     lib = load_library()
     desc = cache_desc(k_cache, layer)
     _need(q, "q", torch.float16, 3)
@@ -216,20 +238,42 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
         if out.shape != q.shape:
             raise ValueError("out must match q")
     opts = _opts(partition_tokens, mfma_min_rows, events, window, reuse_plan)
-    need = lib.pa_attend_workspace_bytes(ctypes.byref(desc), q.shape[1], S, _hp(hl), _hp(hq), ctypes.byref(opts))
     if workspace is None:
         if reuse_plan:
             raise ValueError("reuse_plan needs the workspace of the call that planned")
+        need = lib.pa_attend_workspace_bytes(ctypes.byref(desc), q.shape[1], S, _host_addr(hl), _host_addr(hq),
+                                             ctypes.byref(opts))
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
-    _check(lib.pa_attend(ctypes.byref(desc), _ptr(q), q.shape[1], _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
-                         _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(q_lens), S,
-                         _hp(hl), _hp(hq), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
-                         workspace.numel(), ctypes.byref(opts), _stream(stream)), "pa_attend")
-    return out
+    args = (ctypes.byref(desc), _ptr(q), q.shape[1], _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+            _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(q_lens), S, _host_addr(hl),
+            _host_addr(hq), ctypes.c_float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
+            ctypes.byref(opts), _stream(stream))
+    return PreparedCall(lib.pa_attend, args, "pa_attend", (out, desc, opts, hl, hq, workspace))
 
 
-def pa_copy_blocks(k_cache, v_cache, src_dst, k_scale=None, v_scale=None, stream=None) -> None:
-    """Copy whole blocks (every layer and head) for copy-on-write: ``src_dst [n, 2]`` int32 (src, dst) pairs."""
+def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
+              out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
+              mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
+              reuse_plan: bool = False) -> torch.Tensor:
+    """Paged attention of the packed batch ``q [T, Hq, D]``; returns ``out [T, Hq, D]`` (fp16).
+
+    ``window`` > 0: each query sees only the last ``window`` keys up to its own
+    position (sliding-window attention); 0 = all of them.  ``layer``: the
+    layer of a multi-layer pool.  ``reuse_plan``: take the work lists an
+    earlier call (same lengths and options, e.g. the previous layer of the
+    step) left in ``workspace`` instead of planning again.
+
+    ``events``: optional (vector_begin, vector_end, mfma_begin, mfma_end) raw
+    hipEvent_t handles (ints or None) recorded around the two attention kernels."""
+    call = prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale, out,
+                          workspace, k_scale, v_scale, partition_tokens, mfma_min_rows, events, stream, window,
+                          layer, reuse_plan)
+    call()
+    return call.keep[0]
+
+
+def prepare_copy_blocks(k_cache, v_cache, src_dst, k_scale=None, v_scale=None, stream=None) -> PreparedCall:
+    """``pa_copy_blocks`` as a prepared call."""
     lib = load_library()
     desc = cache_desc(k_cache)
     _need(v_cache, "v_cache", k_cache.dtype, k_cache.dim())
@@ -241,5 +285,11 @@ def pa_copy_blocks(k_cache, v_cache, src_dst, k_scale=None, v_scale=None, stream
     if desc.kv_dtype == PA_KV_I8:
         _need(k_scale, "k_scale", torch.float16, _scale_dims(k_cache))
         _need(v_scale, "v_scale", torch.float16, _scale_dims(k_cache))
-    _check(lib.pa_copy_blocks(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
-                              _ptr(src_dst), src_dst.shape[0], _stream(stream)), "pa_copy_blocks")
+    args = (ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(src_dst),
+            src_dst.shape[0], _stream(stream))
+    return PreparedCall(lib.pa_copy_blocks, args, "pa_copy_blocks", (desc,))
+
+
+def pa_copy_blocks(k_cache, v_cache, src_dst, k_scale=None, v_scale=None, stream=None) -> None:
+    """Copy whole blocks (every layer and head) for copy-on-write: ``src_dst [n, 2]`` int32 (src, dst) pairs."""
+    prepare_copy_blocks(k_cache, v_cache, src_dst, k_scale, v_scale, stream)()

@@ -15,6 +15,7 @@ the first layer's plan.
 """
 from __future__ import annotations
 
+import ctypes
 from dataclasses import dataclass
 from typing import List, Optional
 
@@ -201,3 +202,141 @@ class DeviceRun:
             self.write_layer(x, layer)
             outs.append(self.attend(x, layer=layer, reuse_plan=layer > 0, **opts))
         return outs
+
+
+class StaticSteps:
+    """Fixed-shape steps of a ``DeviceRun`` issued from buffers at fixed
+    device addresses, so that a whole step (block copies, then every layer's
+    KV write and attention) is a list of prepared library calls, which can
+    also be captured once in a HIP graph and replayed.
+
+    Every step reserves ``q_len`` new positions for each of the run's
+    sequences.  The native manager writes the step's metadata straight into
+    a pinned host buffer (two of them, used in turn) laid out like the
+    device buffer, and one asynchronous copy moves it over.  The attention
+    launches are shaped for an upper bound on the lengths (``width`` blocks
+    per sequence), so the same launches serve every step up to that bound;
+    the plan kernel builds the work lists from the true device lengths.
+    Copy-on-write pairs are padded to one per sequence (a step copies at most
+    one block per sequence: only the block holding its first new position
+    can already exist) with (-1, -1), which the copy kernel skips.
+    """
+
+    def __init__(self, run: DeviceRun, width: int, q_len: int = 1, partition_tokens: int = 256,
+                 copies: bool = False):
+        from . import host
+        w = run.w
+        self.run, self.w = run, w
+        self.S = S = len(run.ids)
+        self.T = T = S * int(q_len)
+        self.W = W = int(width)
+        self.copies = bool(copies)
+        self.partition_tokens = int(partition_tokens)
+        o = self.off = {"ql": 0, "sl": S, "slots": 2 * S, "cp": 2 * S + T, "tab": 4 * S + T}
+        n = o["tab"] + S * W
+        self.pinned = [torch.empty(n, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.host = [p.numpy() for p in self.pinned]
+        self.base = [p.data_ptr() for p in self.pinned]
+        for h in self.host:
+            h[:S] = q_len
+        self.done = [None, None]
+        self.turn = 0
+        dev = self.dev = torch.zeros(n, dtype=torch.int32, device=run.device)
+        self.q_lens = dev[0:S]
+        self.seq_lens = dev[S:2 * S]
+        self.slots = dev[2 * S:2 * S + T]
+        self.pairs = dev[o["cp"]:o["cp"] + 2 * S].view(S, 2)
+        self.tables = dev[o["tab"]:].view(S, W)
+        # host lengths handed to the attention calls: the upper bound until a step says otherwise
+        self.h_len = np.full(S, W * w.block_size, np.int32)
+        self.h_ql = np.full(S, q_len, np.int32)
+        L, hq, hkv, d = run.layers, w.num_q_heads, w.num_kv_heads, w.head_dim
+        f16 = dict(dtype=torch.float16, device=run.device)
+        self.new_k = torch.zeros((L, T, hkv, d), **f16)
+        self.new_v = torch.zeros((L, T, hkv, d), **f16)
+        self.q = torch.zeros((L, T, hq, d), **f16)
+        self.out = torch.zeros((L, T, hq, d), **f16)
+        need = pa.pa_attend_workspace_bytes(run.k_cache, hq, self.h_len, self.h_ql, self.partition_tokens, 0,
+                                            w.window)
+        self.ws = torch.empty(need, dtype=torch.uint8, device=run.device)
+        self._lib = host._native()
+        self._ok = host._ok
+        self.mgr = run.mgr._h.ptr
+        self.sids = np.asarray(run.ids, np.int32)
+        self.sids_ptr = self.sids.__array_interface__["data"][0]
+        self.nc = ctypes.c_int32()
+        self.nc_ptr = ctypes.addressof(self.nc)
+        self.calls = self._calls()
+        self.graph = None
+
+    def _calls(self) -> list:
+        """The step's library calls, on the current stream."""
+        run, w = self.run, self.w
+        kc, vc, ks, vs = run.k_cache, run.v_cache, run.k_scale, run.v_scale
+        calls = []
+        if self.copies:
+            calls.append(pa.prepare_copy_blocks(kc, vc, self.pairs, ks, vs))
+        for layer in range(run.layers):
+            calls.append(pa.prepare_write_kv(self.new_k[layer], self.new_v[layer], self.slots, kc, vc, ks, vs,
+                                             layer=layer))
+            calls.append(pa.prepare_attend(self.q[layer], kc, vc, self.tables, self.seq_lens, self.q_lens,
+                                           self.h_len, self.h_ql, w.scale, out=self.out[layer], workspace=self.ws,
+                                           k_scale=ks, v_scale=vs, partition_tokens=self.partition_tokens,
+                                           window=w.window, layer=layer, reuse_plan=layer > 0))
+        return calls
+
+    def set_activations(self, s: int = None, acts=None) -> None:
+        """Copy step ``s``'s activations (or ``acts`` = (new_k, new_v, q) device
+        tensors with a leading layer axis when there are several layers) into
+        the fixed buffers."""
+        if acts is None:
+            acts = self.run.activations(s)
+        for dst, src in zip((self.new_k, self.new_v, self.q), acts):
+            dst.copy_(src.view(dst.shape), non_blocking=True)
+
+    def host_step(self, exact_lengths: bool = True) -> None:
+        """Bookkeeping of the next step (native, into pinned memory) and the
+        asynchronous copy of its metadata to the device on the current
+        stream.  ``exact_lengths``: hand the step's true lengths to the
+        prepared attention calls (a captured graph keeps the upper bound)."""
+        t = self.turn = self.turn ^ 1
+        if self.done[t] is not None:
+            self.done[t].synchronize()           # the copy that last read this buffer has finished
+        b, o, S = self.base[t], self.off, self.S
+        self._ok(self._lib.pa_mgr_step(self.mgr, self.sids_ptr, b + 4 * o["ql"], S, self.W, b + 4 * o["slots"],
+                                       b + 4 * o["cp"], S, self.nc_ptr, b + 4 * o["tab"], b + 4 * o["sl"]),
+                 "step")
+        h = self.host[t]
+        if self.copies:
+            h[o["cp"] + 2 * self.nc.value:o["cp"] + 2 * S] = -1
+        elif self.nc.value:
+            raise RuntimeError("a step made copy-on-write pairs but these steps were set up without copies")
+        self.dev.copy_(self.pinned[t], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.done[t] = ev
+        if exact_lengths:
+            self.h_len[:] = h[S:2 * S]
+
+    def lengths(self) -> np.ndarray:
+        """The last step's lengths (host copy)."""
+        return self.host[self.turn][self.S:2 * self.S].copy()
+
+    def launch(self) -> None:
+        """Issue the step's calls (copies, then per layer write and attention)."""
+        for c in self.calls:
+            c()
+
+    def capture(self) -> None:
+        """Capture the step's calls once in a HIP graph, shaped for the upper
+        bound on the lengths."""
+        self.h_len[:] = self.W * self.w.block_size
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls = self._calls()                # bound to the capture stream
+            for c in calls:
+                c()
+        self.graph = g
+
+    def replay(self) -> None:
+        self.graph.replay()

@@ -285,14 +285,17 @@ def config3(seed: int = 47003, num_seqs: int = 256, max_len: int = 4096, min_len
 
 
 def config4(seed: int = 47004, num_requests: int = 64, prefix: int = 1024, min_suffix: int = 16,
-            max_suffix: int = 256, beam_requests: int = 16, beam_width: int = 4, share: bool = True) -> Workload:
+            max_suffix: int = 256, beam_requests: int = 16, beam_width: int = 4, share: bool = True,
+            decode_steps: int = 1) -> Workload:
     """Shared prefix + beam copy-on-write: every request's table starts with
     the same ``prefix``-token chain; suffixes U[16,256]; requests
     0..beam_requests-1 are forked into ``beam_width`` sequences; one decode
     token per sequence.  Free list is a seeded permutation.
 
     ``share=False`` is the control with the same sequences and lengths but
-    nothing shared: every sequence (each beam too) owns all of its blocks."""
+    nothing shared: every sequence (each beam too) owns all of its blocks.
+    ``decode_steps`` > 1 adds further one-token steps (step s drawn under its
+    own tag; step 0 is the same either way)."""
     hq, hkv, d = 32, 8, 128
     rng = np.random.default_rng([seed, S_META])
     suffix = rng.integers(min_suffix, max_suffix + 1, num_requests).astype(np.int64)
@@ -302,6 +305,13 @@ def config4(seed: int = 47004, num_requests: int = 64, prefix: int = 1024, min_s
     nb = int(math.ceil(1.1 * need))
     perm = rng.permutation(nb)
     nseq = int(np.sum(beams))
+
+    def steps(s):
+        return _step(seed, (s,), np.ones(nseq, np.int64), hq, hkv, d)
+
+    if decode_steps > 1:
+        nb += nseq * _ceil_div(decode_steps, BLOCK_SIZE)
+        perm = rng.permutation(nb)
     if not share:
         lens = np.repeat(prefix + suffix, beams)
         nb = int(math.ceil(1.1 * int(np.sum(_ceil_div(lens + 1, BLOCK_SIZE)))))
@@ -317,7 +327,7 @@ def config4(seed: int = 47004, num_requests: int = 64, prefix: int = 1024, min_s
         block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
         first_pops=perm, ctx_lens=prefix + suffix,
         pool_draws=_f16_pool(seed, nb, hkv, d),
-        steps=[_step(seed, (0,), np.ones(nseq, np.int64), hq, hkv, d)],
+        steps=steps if decode_steps > 1 else [steps(0)], num_steps=int(decode_steps),
         shared_prefix=prefix, beams=beams,
     )
 
