@@ -93,6 +93,25 @@ __device__ int tile_cost_bucket(const PlanArgs& a, int2 mu) {
   return min((kmax - k0) / kMfmaBN, kCostBuckets - 1);
 }
 
+// Vector-path units go out longest first too (a unit's cost: its keys, in
+// 64-key buckets), so a long row's partitions do not start last and set the
+// kernel's tail; the decode kernel's workgroup x takes unit vorder[x].  The
+// units keep their own indices (partials are stored by unit), so the merge
+// does not depend on the order.
+__device__ void order_vector_units(const PlanArgs& a, int n) {
+  __shared__ int slot[kCostBuckets];
+  __shared__ int4 scan_lds[kPlanWaves];
+  slot[threadIdx.x] = 0;
+  __syncthreads();   // also makes this workgroup's writes of vcost visible to all its threads
+  for (int u = threadIdx.x; u < n; u += kPlanThreads) atomicAdd(&slot[kCostBuckets - 1 - a.vcost[u]], 1);
+  __syncthreads();
+  int4 tot;
+  const int first = block_exclusive_scan4(make_int4(slot[threadIdx.x], 0, 0, 0), scan_lds, tot).x;
+  slot[threadIdx.x] = first;
+  __syncthreads();
+  for (int u = threadIdx.x; u < n; u += kPlanThreads) a.vorder[atomicAdd(&slot[kCostBuckets - 1 - a.vcost[u]], 1)] = u;
+}
+
 __device__ void order_row_tiles(const PlanArgs& a, int n) {
   __shared__ int slot[kCostBuckets];
   __shared__ int4 scan_lds[kPlanWaves];
@@ -159,8 +178,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
           vt.parts = parts;
           a.vtok[k] = vt;
         }
-        for (int p = 0; p < parts; ++p)
-          if (u + p < a.cap_vunit) a.vunit[u + p] = make_int2(fits ? k : -1, p);
+        const int keys = vector_keys(L - Q + t, a.window);
+        for (int p = 0; p < parts; ++p) {
+          if (u + p < a.cap_vunit) {
+            a.vunit[u + p] = make_int2(fits ? k : -1, p);
+            const int ck = a.part > 0 ? min(a.part, keys - p * a.part) : keys;
+            a.vcost[u + p] = fits ? min(ck / 64, kCostBuckets - 1) : 0;
+          }
+        }
         u += parts;
       }
     }
@@ -175,9 +200,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     vt.t = vt.u0 = vt.parts = 0;
     a.vtok[k] = vt;
   }
-  for (int u = base_vu + threadIdx.x; u < a.cap_vunit; u += kPlanThreads) a.vunit[u] = make_int2(-1, 0);
+  for (int u = base_vu + threadIdx.x; u < a.cap_vunit; u += kPlanThreads) {
+    a.vunit[u] = make_int2(-1, 0);
+    a.vcost[u] = 0;
+  }
   for (int u = base_mu + threadIdx.x; u < a.cap_munit; u += kPlanThreads) a.munit[u] = make_int2(-1, 0);
   order_row_tiles(a, min(base_mu, a.cap_munit));
+  __syncthreads();   // the two orderings share nothing but reuse the scan's LDS pattern
+  order_vector_units(a, a.cap_vunit);
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
@@ -190,7 +220,8 @@ struct HostPlan {
   int32_t part = 0, min_rows = 16, total_q = 0, window = 0;
   int64_t n_vtok = 0, n_vunit = 0, n_munit = 0;
   int32_t max_parts = 0;
-  size_t off_seqs = 0, off_vtok = 0, off_vunit = 0, off_munit = 0, off_munit_tmp = 0, off_lse = 0, off_po = 0;
+  size_t off_seqs = 0, off_vtok = 0, off_vunit = 0, off_vorder = 0, off_vcost = 0, off_munit = 0, off_munit_tmp = 0,
+         off_lse = 0, off_po = 0;
   size_t bytes = 0;
 };
 
@@ -215,13 +246,17 @@ static pa_status check_heads(const pa_cache_desc* d, int32_t hq) {
 }
 
 // Keys per split-K partition when the caller leaves it to the library: aim
-// for about 16 workgroups per compute unit over the whole vector path, with
-// partitions of 256 .. 4096 keys.
-static int32_t auto_part(int64_t total_keys, int32_t hkv) {
+// for about 16 workgroups per compute unit over the whole vector path, but
+// give every partition at least 768 KB of K and V (1536 keys of fp16 at head
+// dim 128): below that the partial outputs and the merge kernel cost more
+// than the extra parallelism gains (measured on batches of 1k-key rows and
+// on 32-sequence decode steps); at most 4096 keys.
+static int32_t auto_part(int64_t total_keys, int32_t hkv, int32_t head_dim, int32_t elem_bytes) {
   const int64_t target_units = 256 * 16;
-  int64_t p = total_keys * hkv / target_units;
+  const int64_t min_keys = (int64_t)(768 << 10) / (2 * head_dim * elem_bytes);
+  int64_t p = std::max(total_keys * hkv / target_units, min_keys);
   p = (p + 255) / 256 * 256;
-  return (int32_t)std::min<int64_t>(4096, std::max<int64_t>(256, p));
+  return (int32_t)std::min<int64_t>(4096, p);
 }
 
 static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs, const int32_t* hL,
@@ -247,7 +282,9 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   }
   if (total_q >= INT32_MAX / 2) return PA_ERR_SHAPE;
   P.total_q = (int32_t)total_q;
-  P.part = req_part > 0 ? req_part : (req_part < 0 ? 0 : auto_part(vec_keys, d->num_kv_heads));
+  P.part = req_part > 0 ? req_part
+                       : (req_part < 0 ? 0 : auto_part(vec_keys, d->num_kv_heads, d->head_dim,
+                                                       d->kv_dtype == PA_KV_I8 ? 1 : 2));
   for (int i = 0; i < num_seqs; ++i) {
     const int L = hL[i], Q = hQ[i];
     if (Q > 0 && (int64_t)Q * g >= P.min_rows) {
@@ -269,6 +306,10 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   off = align_up(off + sizeof(VTok) * (size_t)std::max<int64_t>(P.n_vtok, 1), 256);
   P.off_vunit = off;
   off = align_up(off + sizeof(int2) * (size_t)std::max<int64_t>(P.n_vunit, 1), 256);
+  P.off_vorder = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)std::max<int64_t>(P.n_vunit, 1), 256);
+  P.off_vcost = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)std::max<int64_t>(P.n_vunit, 1), 256);
   P.off_munit = off;
   off = align_up(off + sizeof(int2) * (size_t)std::max<int64_t>(P.n_munit, 1), 256);
   P.off_munit_tmp = off;
@@ -369,6 +410,8 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   pl.seqs = (SeqInfo*)(ws + P.off_seqs);
   pl.vtok = (VTok*)(ws + P.off_vtok);
   pl.vunit = (int2*)(ws + P.off_vunit);
+  pl.vorder = (int32_t*)(ws + P.off_vorder);
+  pl.vcost = (int32_t*)(ws + P.off_vcost);
   pl.munit = (int2*)(ws + P.off_munit);
   pl.munit_tmp = (int2*)(ws + P.off_munit_tmp);
   pl.num_seqs = num_seqs;
@@ -396,6 +439,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.seqs = pl.seqs;
   a.vtok = pl.vtok;
   a.vunit = pl.vunit;
+  a.vorder = pl.vorder;
   a.munit = pl.munit;
   a.plse = P.max_parts > 1 ? (float*)(ws + P.off_lse) : nullptr;
   a.po = P.max_parts > 1 ? (float*)(ws + P.off_po) : nullptr;

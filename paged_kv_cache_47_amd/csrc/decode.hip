@@ -128,7 +128,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   __shared__ float sm[NW][G], sl[NW][G];
   __shared__ float so[NW][G][D];
 
-  const int u = blockIdx.x, h = blockIdx.y;
+  const int u = a.vorder[blockIdx.x], h = blockIdx.y;   // units go out longest first
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps block indices scalar
   const int2 un = a.vunit[u];

@@ -43,6 +43,7 @@ struct AttnArgs {
   const SeqInfo* seqs;
   const VTok* vtok;
   const int2* vunit;   // {vtok index, partition}
+  const int32_t* vorder;  // dispatch order of the vector units: workgroup x takes unit vorder[x]
   const int2* munit;   // {sequence, row tile}
   float* po;           // [n_vunit][Hq][D] normalised partial outputs
   float* plse;         // [n_vunit][Hq] base-2 log-sum-exp of each partial
@@ -68,6 +69,8 @@ struct PlanArgs {
   SeqInfo* seqs;
   VTok* vtok;
   int2* vunit;
+  int32_t* vorder;     // vector units, longest first (a permutation of 0 .. cap_vunit-1)
+  int32_t* vcost;      // cost bucket of each vector unit (scratch for the ordering)
   int2* munit;
   int2* munit_tmp;     // row tiles in sequence order, before the longest-first ordering
   int32_t num_seqs;

@@ -222,7 +222,7 @@ class StaticSteps:
     can already exist) with (-1, -1), which the copy kernel skips.
     """
 
-    def __init__(self, run: DeviceRun, width: int, q_len: int = 1, partition_tokens: int = 256,
+    def __init__(self, run: DeviceRun, width: int, q_len: int = 1, partition_tokens: int = 0,
                  copies: bool = False):
         from . import host
         w = run.w
