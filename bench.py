@@ -437,6 +437,8 @@ def main(argv=None) -> int:
     ap.add_argument("--layers", type=int, default=1,
                     help="workload 2 only: layers per block (GPT-2 small has 12); a step writes and attends "
                          "every layer over one set of metadata")
+    ap.add_argument("--kv-dtype", default="f16", choices=("f16", "bf16"),
+                    help="workloads 2 and 3: the pool type (bf16 pools take and return bf16 activations)")
     ap.add_argument("--no-share", action="store_true",
                     help="workload 4 control: every sequence owns its own copy of the prefix (no sharing, no forks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -489,10 +491,15 @@ def main(argv=None) -> int:
     if args.layers != 1 and args.workload != 2:
         print("--layers applies to workload 2 only", file=sys.stderr)
         return 2
+    if args.kv_dtype != "f16" and args.workload not in (2, 3):
+        print("--kv-dtype applies to workloads 2 and 3 only", file=sys.stderr)
+        return 2
     if args.workload == 4 and args.no_share:
         w = synthetic.config4(share=False)
     elif args.workload == 2:
-        w = synthetic.config2(num_layers=args.layers)
+        w = synthetic.config2(num_layers=args.layers, kv_dtype=args.kv_dtype)
+    elif args.workload == 3:
+        w = synthetic.config3(kv_dtype=args.kv_dtype)
     else:
         w = synthetic.CONFIGS[args.workload]()
     w.window = args.window
@@ -635,13 +642,14 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8" if w.kv_dtype == "i8" else "f16",
+        "dtype": w.kv_dtype,
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload] + (" [control: every sequence owns its prefix copy]"
                                                           if args.workload == 4 and args.no_share else "")
                    + (f" [sliding window of {args.window} keys]" if args.window else "")
                    + (f" [{w.num_layers} layers per block: every step writes and attends each]"
-                      if w.num_layers > 1 else ""),
+                      if w.num_layers > 1 else "")
+                   + (" [bf16 KV, queries and outputs]" if w.kv_dtype == "bf16" else ""),
                    "num_seqs": S, "kv_tokens": int(L.sum()),
                    "query_rows": int(Q.sum()), "num_blocks": w.num_blocks,
                    "partition_tokens": args.partition_tokens, "window": args.window, "layers": w.num_layers},

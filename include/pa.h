@@ -23,7 +23,8 @@
  *   slab, [manager] "Step 1: The Block", or as two tensors, [pytorch]
  *   "Allocate, append, and free KV-cache blocks"): two pools, K and V, each
  *       [num_blocks][num_layers][num_kv_heads][block_size][head_dim]
- *   of fp16 (PA_KV_F16) or int8 codes (PA_KV_I8), so one (block, layer, KV
+ *   of fp16 (PA_KV_F16), bf16 (PA_KV_BF16) or int8 codes (PA_KV_I8), so one
+ *   (block, layer, KV
  *   head) tile is one contiguous run of block_size * head_dim elements.  A
  *   physical block holds its tokens for every layer ([pytorch] "Allocate,
  *   append, and free KV-cache blocks" keeps the layer axis inside the block),
@@ -62,7 +63,11 @@ typedef enum {
   PA_ERR_HIP = 6           /* a HIP launch failed                              */
 } pa_status;
 
-typedef enum { PA_KV_F16 = 0, PA_KV_I8 = 1 } pa_kv_dtype;
+/* Element type of the pools.  The activations a call takes and returns (new
+ * K/V rows, queries, outputs) are bf16 for PA_KV_BF16 and fp16 otherwise
+ * ([pytorch] "Compute reference attention without hiding the layout" tests
+ * fp16 and bf16 caches, each against its own tolerance). */
+typedef enum { PA_KV_F16 = 0, PA_KV_I8 = 1, PA_KV_BF16 = 2 } pa_kv_dtype;
 
 /* Shape of one KV pool pair (see the layout above) and the layer a call
  * addresses. */
@@ -84,16 +89,17 @@ typedef struct {
  * flow", steps 2-3; "Map the PyTorch design to vLLM PagedAttention": slot
  * mappings are integer tensors handed over each step).
  *
- *   k, v          fp16 [num_tokens][num_kv_heads][head_dim], row-major.
+ *   k, v          [num_tokens][num_kv_heads][head_dim], row-major: fp16
+ *                 (bf16 for PA_KV_BF16 pools).
  *   slot_mapping  int32 [num_tokens]; slot = block_id * block_size + offset.
  *                 A negative slot skips that token (padding).  Slots of one
  *                 call must be distinct.
- *   k_cache, v_cache  the pools (fp16 or int8 codes, per desc->kv_dtype).
+ *   k_cache, v_cache  the pools (fp16, bf16 or int8 codes, per desc->kv_dtype).
  *   k_scale, v_scale  fp16 [num_blocks][num_layers][num_kv_heads] for
  *                 PA_KV_I8, else ignored (may be NULL).
  * Rows go to layer desc->layer of the pools; the other layers are untouched.
  *
- * fp16: token t's K/V of every head are copied bit-for-bit to offset
+ * fp16 and bf16: token t's K/V of every head are copied bit-for-bit to offset
  * slot % block_size of block slot / block_size.
  *
  * int8 ([engine] "INT8 KV cache design": on every token write the block's
@@ -178,7 +184,8 @@ size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
  * block_table, q_len_per_seq, kv_len_per_seq, block_size, and one packed
  * batch of prefill and decode rows).
  *
- *   q             fp16 [total_q][num_q_heads][head_dim], sequence-major:
+ *   q             [total_q][num_q_heads][head_dim], sequence-major (fp16;
+ *                 bf16 for PA_KV_BF16 pools):
  *                 sequence i's q_lens[i] rows follow sequence i-1's.
  *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entry b of row i is
  *                 the physical block of logical block b of sequence i.
@@ -189,7 +196,7 @@ size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
  *                 chosen from them, so they must equal the device arrays.
  *   scale         multiplier of q.k (normally head_dim ** -0.5); must be
  *                 positive and finite (PA_ERR_SHAPE otherwise).
- *   out           fp16 [total_q][num_q_heads][head_dim].
+ *   out           [total_q][num_q_heads][head_dim], the type of q.
  *   workspace     device scratch of at least pa_attend_workspace_bytes.
  *
  * Query row t (0-based) of sequence i sits at position

@@ -229,7 +229,7 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 static pa_status check_desc(const pa_cache_desc* d) {
   if (d == nullptr) return PA_ERR_NULL;
-  if (d->kv_dtype != PA_KV_F16 && d->kv_dtype != PA_KV_I8) return PA_ERR_DTYPE;
+  if (d->kv_dtype != PA_KV_F16 && d->kv_dtype != PA_KV_I8 && d->kv_dtype != PA_KV_BF16) return PA_ERR_DTYPE;
   if (d->num_blocks <= 0 || d->num_kv_heads <= 0 || d->block_size <= 0 || d->head_dim <= 0) return PA_ERR_SHAPE;
   if (d->num_layers < 0 || d->layer < 0 || d->layer >= std::max(d->num_layers, 1)) return PA_ERR_SHAPE;
   if (d->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
@@ -430,7 +430,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   const int64_t tile0 = (int64_t)desc->layer * desc->num_kv_heads;
   const int64_t tile_bytes = (int64_t)kBlockSize * desc->head_dim * (i8 ? 1 : 2);
   AttnArgs a;
-  a.q = (const half_t*)q;
+  a.q = q;
   a.kc = (const char*)k_cache + tile0 * tile_bytes;
   a.vc = (const char*)v_cache + tile0 * tile_bytes;
   a.ks = i8 ? (const half_t*)k_scale + tile0 : nullptr;
@@ -443,7 +443,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.munit = pl.munit;
   a.plse = P.max_parts > 1 ? (float*)(ws + P.off_lse) : nullptr;
   a.po = P.max_parts > 1 ? (float*)(ws + P.off_po) : nullptr;
-  a.out = (half_t*)out;
+  a.out = out;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = desc->num_blocks;
   a.hq = num_q_heads;
@@ -456,14 +456,15 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   auto mark = [&](hipEvent_t ev) { return ev == nullptr || hipEventRecord(ev, stream) == hipSuccess; };
   if (P.n_vunit > 0) {
     if (!mark(opts ? opts->vector_begin : nullptr)) return PA_ERR_HIP;
-    if (launch_decode(a, desc->head_dim, g, i8, (int)P.n_vunit, stream) != hipSuccess) return PA_ERR_HIP;
+    if (launch_decode(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_vunit, stream) != hipSuccess) return PA_ERR_HIP;
     if (!mark(opts ? opts->vector_end : nullptr)) return PA_ERR_HIP;
-    if (P.max_parts > 1 && launch_reduce(a, desc->head_dim, g, (int)P.n_vtok, stream) != hipSuccess)
+    if (P.max_parts > 1 && launch_reduce(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_vtok, stream) != hipSuccess)
       return PA_ERR_HIP;
   }
   if (P.n_munit > 0) {
     if (!mark(opts ? opts->mfma_begin : nullptr)) return PA_ERR_HIP;
-    if (launch_prefill(a, desc->head_dim, g, i8, (int)P.n_munit, stream) != hipSuccess) return PA_ERR_HIP;
+    if (launch_prefill(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_munit, stream) != hipSuccess)
+      return PA_ERR_HIP;
     if (!mark(opts ? opts->mfma_end : nullptr)) return PA_ERR_HIP;
   }
   return PA_OK;

@@ -40,9 +40,10 @@ __device__ __forceinline__ float dot2_first(half2_t a, half2_t b) {
   asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+__device__ __forceinline__ float dot2_first(bf162_t a, bf162_t b) { return dot2(a, b, 0.f); }
 
-template <bool I8, int N>
-__device__ __forceinline__ void v_token_pairs(const Dw<N>& r0, const Dw<N>& r1, half2_t* vp) {
+template <bool I8, int N, typename T2>
+__device__ __forceinline__ void v_token_pairs(const Dw<N>& r0, const Dw<N>& r1, T2* vp) {
   if constexpr (I8 && PA_I8_SDWA) {
 #pragma unroll
     for (int c = 0; c < N; ++c) {
@@ -66,8 +67,8 @@ __device__ __forceinline__ void v_token_pairs(const Dw<N>& r0, const Dw<N>& r1, 
   } else {
 #pragma unroll
     for (int c = 0; c < N; ++c) {
-      vp[2 * c + 0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(r1.v[c], r0.v[c], 0x05040100u));
-      vp[2 * c + 1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(r1.v[c], r0.v[c], 0x07060302u));
+      vp[2 * c + 0] = __builtin_bit_cast(T2, __builtin_amdgcn_perm(r1.v[c], r0.v[c], 0x05040100u));
+      vp[2 * c + 1] = __builtin_bit_cast(T2, __builtin_amdgcn_perm(r1.v[c], r0.v[c], 0x07060302u));
     }
   }
 }
@@ -109,8 +110,11 @@ __device__ __forceinline__ Dw<N> load_dw(const uint32_t* p) {
   return r;
 }
 
-template <int D, int G, bool I8, int NW, int VB>
+template <int D, int G, int KV, int NW, int VB>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
+  constexpr bool I8 = KV == kKvI8;
+  using act_t = typename Act<KV>::t;   // 16-bit type of queries, weights and outputs
+  using act2_t = typename Act<KV>::t2;
   constexpr int EB = I8 ? 1 : 2;       // bytes per element
   constexpr int ND = VB / 4;           // dwords per lane per load (VB = 8 or 16 bytes)
   constexpr int E = VB / EB;           // elements per lane per load
@@ -144,17 +148,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   const int64_t row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
   const int32_t* tbl = a.block_tables + (int64_t)vt.seq * a.max_blocks;
 
-  half2_t qh[G][E2];
+  act2_t qh[G][E2];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const uint4* qp = (const uint4*)(a.q + (row0 + g) * D + sub * E);
+    const uint4* qp = (const uint4*)((const act_t*)a.q + (row0 + g) * D + sub * E);
 #pragma unroll
     for (int c = 0; c < E / 8; ++c) {
       const uint4 w = qp[c];
-      qh[g][4 * c + 0] = __builtin_bit_cast(half2_t, w.x);
-      qh[g][4 * c + 1] = __builtin_bit_cast(half2_t, w.y);
-      qh[g][4 * c + 2] = __builtin_bit_cast(half2_t, w.z);
-      qh[g][4 * c + 3] = __builtin_bit_cast(half2_t, w.w);
+      qh[g][4 * c + 0] = __builtin_bit_cast(act2_t, w.x);
+      qh[g][4 * c + 1] = __builtin_bit_cast(act2_t, w.y);
+      qh[g][4 * c + 2] = __builtin_bit_cast(act2_t, w.z);
+      qh[g][4 * c + 3] = __builtin_bit_cast(act2_t, w.w);
     }
   }
 
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     float s[NL][G];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      half2_t kh[E2];
+      act2_t kh[E2];
       if constexpr (I8) {
 #pragma unroll
         for (int c = 0; c < ND; ++c) {
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < ND; ++c) kh[c] = __builtin_bit_cast(half2_t, kr[i].v[c]);
+        for (int c = 0; c < ND; ++c) kh[c] = __builtin_bit_cast(act2_t, kr[i].v[c]);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
         // zero addend, so no register has to be cleared first)
         float d = dot2_first(qh[g][0], kh[0]);
 #pragma unroll
-        for (int c = 1; c < E2; ++c) d = __builtin_amdgcn_fdot2(qh[g][c], kh[c], d, false);
+        for (int c = 1; c < E2; ++c) d = dot2(qh[g][c], kh[c], d);
         s[i][g] = d;
       }
     }
@@ -268,23 +272,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       // P.V on v_dot2_f32_f16 over token pairs: vp[e] = (V[tok 2j][e], V[tok 2j+1][e])
 #pragma unroll
       for (int j = 0; j < NL / 2; ++j) {
-        half2_t vp[E];
+        act2_t vp[E];
         v_token_pairs<I8, ND>(vr[2 * j], vr[2 * j + 1], vp);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float p0 = fast_exp2(fmaf(s[2 * j][g], ksc, -m[g]));
           const float p1 = fast_exp2(fmaf(s[2 * j + 1][g], ksc, -m[g]));
-          half2_t pp;
+          act2_t pp;
           if constexpr (I8) {
             l[g] += p0 + p1;
-            pp = (half2_t){(half_t)(p0 * vsc), (half_t)(p1 * vsc)};
+            pp = (act2_t){(act_t)(p0 * vsc), (act_t)(p1 * vsc)};
           } else {
-            pp = (half2_t){(half_t)p0, (half_t)p1};
+            pp = (act2_t){(act_t)p0, (act_t)p1};
             // sum the rounded weights the product uses, so the output stays a convex combination
-            l[g] = __builtin_amdgcn_fdot2(pp, (half2_t){(half_t)1.f, (half_t)1.f}, l[g], false);
+            l[g] = dot2(pp, (act2_t){(act_t)1.f, (act_t)1.f}, l[g]);
           }
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[g][e] = __builtin_amdgcn_fdot2(pp, vp[e], acc[g][e], false);
+          for (int e = 0; e < E; ++e) acc[g][e] = dot2(pp, vp[e], acc[g][e]);
         }
       }
     } else {
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       O += so[w][g][d] * f;
     }
     if (!split) {
-      a.out[(row0 + g) * D + d] = (half_t)(O / Ls);
+      ((act_t*)a.out)[(row0 + g) * D + d] = (act_t)(O / Ls);
     } else {
       const int64_t pr = (int64_t)u * a.hq + (int64_t)h * G + g;
       a.po[pr * D + d] = O / Ls;
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 
 // Merge the split-K partials of one (query row, KV head): its G query heads,
 // base-2 log-sum-exp: out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M).
-template <int D, int G>
+template <int D, int G, typename OUT>
 __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const VTok vt = a.vtok[blockIdx.x];
   if (vt.seq < 0 || vt.parts <= 1) return;
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
       S += wgt;
       O = fmaf(wgt, a.po[pr * D + d], O);
     }
-    a.out[(row0 + g) * D + d] = (half_t)(O / S);
+    ((OUT*)a.out)[(row0 + g) * D + d] = (OUT)(O / S);
   }
 }
 
@@ -424,42 +428,53 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
 #define PA_DECODE_VB_I8 16  // bytes per lane per load for int8 pools (8: twice the lanes per row)
 #endif
 
-template <int D, bool I8>
+template <int D, int KV>
 static hipError_t decode_g(const AttnArgs& a, int g, int n, hipStream_t s) {
   // 16-byte loads per lane; 8-byte int8 loads halve the per-lane registers
   // (4 waves/SIMD) but add reduction and softmax work, and measure slower
-  constexpr int kVB = I8 ? PA_DECODE_VB_I8 : 16;
+  constexpr int kVB = KV == kKvI8 ? PA_DECODE_VB_I8 : 16;
   dim3 grid(n, a.hkv);
   switch (g) {
-    case 1: decode_kernel<D, 1, I8, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
-    case 2: decode_kernel<D, 2, I8, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
-    case 4: decode_kernel<D, 4, I8, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
-    case 8: decode_kernel<D, 8, I8, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 1: decode_kernel<D, 1, KV, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 2: decode_kernel<D, 2, KV, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 4: decode_kernel<D, 4, KV, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    case 8: decode_kernel<D, 8, KV, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, bool i8, int n, hipStream_t s) {
-  if (head_dim == 128) return i8 ? decode_g<128, true>(a, group, n, s) : decode_g<128, false>(a, group, n, s);
-  return i8 ? decode_g<64, true>(a, group, n, s) : decode_g<64, false>(a, group, n, s);
 }
 
 template <int D>
+static hipError_t decode_d(const AttnArgs& a, int g, int kv, int n, hipStream_t s) {
+  switch (kv) {
+    case kKvF16: return decode_g<D, kKvF16>(a, g, n, s);
+    case kKvI8: return decode_g<D, kKvI8>(a, g, n, s);
+    case kKvBF16: return decode_g<D, kKvBF16>(a, g, n, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, int kv, int n, hipStream_t s) {
+  return head_dim == 128 ? decode_d<128>(a, group, kv, n, s) : decode_d<64>(a, group, kv, n, s);
+}
+
+template <int D, typename OUT>
 static hipError_t reduce_g(const AttnArgs& a, int g, int n, hipStream_t s) {
   dim3 grid(n, a.hkv);
   switch (g) {
-    case 1: reduce_kernel<D, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: reduce_kernel<D, 2><<<grid, 256, 0, s>>>(a); break;
-    case 4: reduce_kernel<D, 4><<<grid, 256, 0, s>>>(a); break;
-    case 8: reduce_kernel<D, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: reduce_kernel<D, 1, OUT><<<grid, 256, 0, s>>>(a); break;
+    case 2: reduce_kernel<D, 2, OUT><<<grid, 256, 0, s>>>(a); break;
+    case 4: reduce_kernel<D, 4, OUT><<<grid, 256, 0, s>>>(a); break;
+    case 8: reduce_kernel<D, 8, OUT><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const AttnArgs& a, int head_dim, int group, int n_vtok, hipStream_t s) {
-  return head_dim == 128 ? reduce_g<128>(a, group, n_vtok, s) : reduce_g<64>(a, group, n_vtok, s);
+hipError_t launch_reduce(const AttnArgs& a, int head_dim, int group, int kv, int n_vtok, hipStream_t s) {
+  if (kv == kKvBF16)
+    return head_dim == 128 ? reduce_g<128, bf16_t>(a, group, n_vtok, s) : reduce_g<64, bf16_t>(a, group, n_vtok, s);
+  return head_dim == 128 ? reduce_g<128, half_t>(a, group, n_vtok, s) : reduce_g<64, half_t>(a, group, n_vtok, s);
 }
 
 }  // namespace pa

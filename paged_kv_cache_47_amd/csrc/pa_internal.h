@@ -12,8 +12,32 @@ typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16_t;
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf164_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Pool element kinds the kernels are built for (the pa_kv_dtype values).
+constexpr int kKvF16 = PA_KV_F16, kKvI8 = PA_KV_I8, kKvBF16 = PA_KV_BF16;
+
+// The 16-bit activation type of a pool kind (queries, new rows, outputs, the
+// softmax weights fed to the products): bf16 for bf16 pools, fp16 otherwise.
+template <int KV>
+struct Act {
+  using t = half_t;
+  using t2 = half2_t;
+  using t4 = half4_t;
+  using t8 = half8_t;
+};
+template <>
+struct Act<kKvBF16> {
+  using t = bf16_t;
+  using t2 = bf162_t;
+  using t4 = bf164_t;
+  using t8 = bf168_t;
+};
 
 constexpr int kBlockSize = 16;     // tokens per block (the only size built)
 constexpr int kWave = 64;
@@ -34,7 +58,7 @@ struct VTok {
 };
 
 struct AttnArgs {
-  const half_t* q;
+  const void* q;       // fp16, or bf16 for bf16 pools
   const void* kc;
   const void* vc;
   const half_t* ks;
@@ -47,7 +71,7 @@ struct AttnArgs {
   const int2* munit;   // {sequence, row tile}
   float* po;           // [n_vunit][Hq][D] normalised partial outputs
   float* plse;         // [n_vunit][Hq] base-2 log-sum-exp of each partial
-  half_t* out;
+  void* out;           // the type of q
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t hq, hkv;
@@ -85,9 +109,9 @@ struct PlanArgs {
 
 // Launchers (one translation unit each); all return hipGetLastError() after launch.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, bool i8, int n_vunit, hipStream_t s);
-hipError_t launch_reduce(const AttnArgs& a, int head_dim, int group, int n_vtok, hipStream_t s);
-hipError_t launch_prefill(const AttnArgs& a, int head_dim, int group, bool i8, int n_munit, hipStream_t s);
+hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, int kv, int n_vunit, hipStream_t s);
+hipError_t launch_reduce(const AttnArgs& a, int head_dim, int group, int kv, int n_vtok, hipStream_t s);
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, int group, int kv, int n_munit, hipStream_t s);
 hipError_t launch_write_f16(const pa_cache_desc& d, const void* k, const void* v, const int32_t* slots,
                             int32_t T, void* kc, void* vc, hipStream_t s);
 hipError_t launch_write_i8(const pa_cache_desc& d, const void* k, const void* v, const int32_t* slots,
@@ -99,6 +123,19 @@ hipError_t launch_copy(const pa_cache_desc& d, void* kc, void* vc, void* ks, voi
 // Device helpers
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Pair dot products with an fp32 accumulator, and the 16x16x32 matrix
+// product, for either 16-bit type.
+__device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+__device__ __forceinline__ float dot2(bf162_t a, bf162_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+__device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma16x16x32(bf168_t a, bf168_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {

@@ -14,7 +14,7 @@
 //
 // Sequences with q_len * G >= 16 rows take this path: kMfmaRows query rows
 // per workgroup (kMfmaWaves waves x 32), 64 keys per step, S^T = K Q^T and O^T = V^T P^T
-// on v_mfma_f32_16x16x32_f16.  Computing the transposes makes each lane own
+// on v_mfma_f32_16x16x32_f16 (_bf16 for bf16 pools).  Computing the transposes makes each lane own
 // one query row in both accumulators, and the P accumulator already sits in
 // the B-operand layout of the second product.  V is staged in LDS and read
 // with the gfx950 transposing LDS read.
@@ -42,8 +42,12 @@ namespace pa {
 // Lazy-rescale threshold of the MFMA path (log2 units): weights stay below 2^8.
 constexpr float kRescalePf = 8.0f;
 
-template <int D, int G, bool I8>
+template <int D, int G, int KV>
 __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kernel(AttnArgs a) {
+  constexpr bool I8 = KV == kKvI8;
+  using act_t = typename Act<KV>::t;     // 16-bit operand type of both products (int8 pools: fp16)
+  using act4_t = typename Act<KV>::t4;
+  using act8_t = typename Act<KV>::t8;
   constexpr int KS = D / 32;        // k-steps of 32 over the head dim
   constexpr int NT = D / 16;        // 16-wide output column tiles
   constexpr int BN = kMfmaBN;       // keys per step
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   int qpos[RB], qlo[RB];
   int64_t orow[RB];
   bool rvalid[RB];
-  half8_t qop[RB][KS];
+  act8_t qop[RB][KS];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int row = r0 + wave * 32 + rb * 16 + l16;
@@ -96,7 +100,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
     orow[rb] = ((int64_t)(si.q_start + tq) * a.hq + (int64_t)h * G + row % G) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qop[rb][ks] = rvalid[rb] ? *(const half8_t*)(a.q + orow[rb] + ks * 32 + 8 * grp) : (half8_t)(half_t)0.f;
+      qop[rb][ks] = rvalid[rb] ? *(const act8_t*)((const act_t*)a.q + orow[rb] + ks * 32 + 8 * grp)
+                               : (act8_t)(act_t)0.f;
   }
 
   float4_t o[RB][NT];
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   __syncthreads();
   typedef __attribute__((address_space(3))) short4_t lds_short4;
   int buf = 0;
-  const half8_t kOnes8 = (half8_t)(half_t)1.0f;
+  const act8_t kOnes8 = (act8_t)(act_t)1.0f;
 
   // One 64-key step: S = K Q^T for the four 16-key blocks (this lane: query
   // row l16 of each row block, keys 16*kb + 4*grp + e), the online-softmax
@@ -245,22 +250,23 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
     // S^T = K Q^T, k-step outer so the eight accumulators interleave, with the
     // next k-step's four K operands read from LDS while this one's products run
     float4_t s[RB][KB];
-    half8_t kq[2][KB];
+    act8_t kq[2][KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kq[0][kb] = *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + 8 * grp];
+    for (int kb = 0; kb < KB; ++kb)
+      kq[0][kb] = __builtin_bit_cast(act8_t, *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + 8 * grp]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-          kq[(ks + 1) & 1][kb] = *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + (ks + 1) * 32 + 8 * grp];
+          kq[(ks + 1) & 1][kb] = __builtin_bit_cast(
+              act8_t, *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + (ks + 1) * 32 + 8 * grp]);
       }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kq[ks & 1][kb], qop[rb][ks],
-                                                            ks == 0 ? (float4_t)0.f : s[rb][kb], 0, 0, 0);
+          s[rb][kb] = mfma16x16x32(kq[ks & 1][kb], qop[rb][ks], ks == 0 ? (float4_t)0.f : s[rb][kb]);
     }
     if (kt + BN - 1 > qmin || kt < wlo_last) {
 #pragma unroll
@@ -305,31 +311,31 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       // this half's V operands (transposing LDS reads) are requested before its weights are formed
-      half8_t vq[NT];
+      act8_t vq[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const half_t* p1 = &ldv[buf][(hh * 32 + 4 * grp + (l16 >> 2)) * LDV + nt * 16 + 4 * (l16 & 3)];
         const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
         const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1 + 16 * LDV));
         const half4_t h1 = __builtin_bit_cast(half4_t, v1), h2 = __builtin_bit_cast(half4_t, v2);
-        vq[nt] = (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w};
+        vq[nt] = __builtin_bit_cast(act8_t, (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w});
       }
-      half8_t p[RB];
+      act8_t p[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           // slot j of the k-step: keys 4*grp + [0..3] of the half's first and second 16-key block
           const int kb = 2 * hh + j / 4;
-          p[rb][j] = (half_t)fast_exp2(fmaf(s[rb][kb][j % 4], cks[kb], -m[rb]));
+          p[rb][j] = (act_t)fast_exp2(fmaf(s[rb][kb][j % 4], cks[kb], -m[rb]));
         }
         // row sums of exactly the weights the product uses: ones^T P^T on the matrix cores
-        lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kOnes8, p[rb], lsum[rb], 0, 0, 0);
+        lsum[rb] = mfma16x16x32(kOnes8, p[rb], lsum[rb]);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vq[nt], p[rb], o[rb][nt], 0, 0, 0);
+        for (int rb = 0; rb < RB; ++rb) o[rb][nt] = mfma16x16x32(vq[nt], p[rb], o[rb][nt]);
     }
     lstore(buf ^ 1);
     if (more) tn = tn2;
@@ -342,32 +348,41 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
     const float inv = (I8 ? 2.f : 1.f) / lsum[rb][0];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      half4_t r;
-      r.x = (half_t)(o[rb][nt][0] * inv);
-      r.y = (half_t)(o[rb][nt][1] * inv);
-      r.z = (half_t)(o[rb][nt][2] * inv);
-      r.w = (half_t)(o[rb][nt][3] * inv);
-      *(half4_t*)(a.out + orow[rb] + nt * 16 + 4 * grp) = r;
+      act4_t r;
+      r.x = (act_t)(o[rb][nt][0] * inv);
+      r.y = (act_t)(o[rb][nt][1] * inv);
+      r.z = (act_t)(o[rb][nt][2] * inv);
+      r.w = (act_t)(o[rb][nt][3] * inv);
+      *(act4_t*)((act_t*)a.out + orow[rb] + nt * 16 + 4 * grp) = r;
     }
   }
 }
 
-template <int D, bool I8>
+template <int D, int KV>
 static hipError_t prefill_g(const AttnArgs& a, int g, int n, hipStream_t s) {
   const dim3 grid(n * a.hkv);   // workgroup id = row tile * hkv + KV head
   switch (g) {
-    case 1: prefill_kernel<D, 1, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
-    case 2: prefill_kernel<D, 2, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
-    case 4: prefill_kernel<D, 4, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
-    case 8: prefill_kernel<D, 8, I8><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 1: prefill_kernel<D, 1, KV><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 2: prefill_kernel<D, 2, KV><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 4: prefill_kernel<D, 4, KV><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 8: prefill_kernel<D, 8, KV><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const AttnArgs& a, int head_dim, int group, bool i8, int n, hipStream_t s) {
-  if (head_dim == 128) return i8 ? prefill_g<128, true>(a, group, n, s) : prefill_g<128, false>(a, group, n, s);
-  return i8 ? prefill_g<64, true>(a, group, n, s) : prefill_g<64, false>(a, group, n, s);
+template <int D>
+static hipError_t prefill_d(const AttnArgs& a, int g, int kv, int n, hipStream_t s) {
+  switch (kv) {
+    case kKvF16: return prefill_g<D, kKvF16>(a, g, n, s);
+    case kKvI8: return prefill_g<D, kKvI8>(a, g, n, s);
+    case kKvBF16: return prefill_g<D, kKvBF16>(a, g, n, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, int group, int kv, int n, hipStream_t s) {
+  return head_dim == 128 ? prefill_d<128>(a, group, kv, n, s) : prefill_d<64>(a, group, kv, n, s);
 }
 
 }  // namespace pa

@@ -19,6 +19,7 @@ from ._lib import LIB_PATH, LibraryMissing, cdll
 
 PA_KV_F16 = 0
 PA_KV_I8 = 1
+PA_KV_BF16 = 2
 
 
 class PagedAttentionError(RuntimeError):
@@ -105,12 +106,9 @@ def cache_desc(k_cache: torch.Tensor, layer: int = 0) -> CacheDesc:
     addressing ``layer``."""
     if k_cache.dim() not in (4, 5):
         raise ValueError("pools are [num_blocks, (num_layers,) num_kv_heads, block_size, head_dim]")
-    if k_cache.dtype == torch.float16:
-        kind = PA_KV_F16
-    elif k_cache.dtype == torch.int8:
-        kind = PA_KV_I8
-    else:
-        raise TypeError(f"pool dtype {k_cache.dtype} is neither float16 nor int8")
+    kind = {torch.float16: PA_KV_F16, torch.int8: PA_KV_I8, torch.bfloat16: PA_KV_BF16}.get(k_cache.dtype)
+    if kind is None:
+        raise TypeError(f"pool dtype {k_cache.dtype} is not float16, bfloat16 or int8")
     if k_cache.dim() == 4:
         nb, hkv, bs, d = k_cache.shape
         nl = 1
@@ -123,6 +121,11 @@ def cache_desc(k_cache: torch.Tensor, layer: int = 0) -> CacheDesc:
 
 def _scale_dims(k_cache: torch.Tensor) -> int:
     return 2 if k_cache.dim() == 4 else 3
+
+
+def _act_dtype(desc: CacheDesc):
+    """Dtype of the activations (new rows, queries, outputs) for a pool."""
+    return torch.bfloat16 if desc.kv_dtype == PA_KV_BF16 else torch.float16
 
 
 def _host_i32(a) -> np.ndarray:
@@ -162,12 +165,13 @@ def _host_addr(a: np.ndarray) -> int:
 
 def prepare_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, stream=None,
                      layer: int = 0) -> PreparedCall:
-    """``pa_write_kv`` of new K/V rows ``k, v [T, Hkv, D]`` (fp16) into layer
-    ``layer`` of the pools through ``slot_mapping [T]``, as a prepared call."""
+    """``pa_write_kv`` of new K/V rows ``k, v [T, Hkv, D]`` (fp16; bf16 for bf16
+    pools) into layer ``layer`` of the pools through ``slot_mapping [T]``, as a
+    prepared call."""
     lib = load_library()
     desc = cache_desc(k_cache, layer)
-    _need(k, "k", torch.float16, 3)
-    _need(v, "v", torch.float16, 3)
+    _need(k, "k", _act_dtype(desc), 3)
+    _need(v, "v", _act_dtype(desc), 3)
     _need(slot_mapping, "slot_mapping", torch.int32, 1)
     _need(v_cache, "v_cache", k_cache.dtype, k_cache.dim())
     if v_cache.shape != k_cache.shape:
@@ -215,7 +219,7 @@ def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_le
     must match them at each call)."""
     lib = load_library()
     desc = cache_desc(k_cache, layer)
-    _need(q, "q", torch.float16, 3)
+    _need(q, "q", _act_dtype(desc), 3)
     _need(v_cache, "v_cache", k_cache.dtype, k_cache.dim())
     if v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache must have the same shape")
@@ -234,7 +238,7 @@ def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_le
     if out is None:
         out = torch.empty_like(q)
     else:
-        _need(out, "out", torch.float16, 3)
+        _need(out, "out", _act_dtype(desc), 3)
         if out.shape != q.shape:
             raise ValueError("out must match q")
     opts = _opts(partition_tokens, mfma_min_rows, events, window, reuse_plan)
@@ -255,7 +259,8 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
               out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
               mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
               reuse_plan: bool = False) -> torch.Tensor:
-    """Paged attention of the packed batch ``q [T, Hq, D]``; returns ``out [T, Hq, D]`` (fp16).
+    """Paged attention of the packed batch ``q [T, Hq, D]``; returns ``out [T, Hq, D]``
+    (fp16; bf16 for bf16 pools).
 
     ``window`` > 0: each query sees only the last ``window`` keys up to its own
     position (sliding-window attention); 0 = all of them.  ``layer``: the

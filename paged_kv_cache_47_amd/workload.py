@@ -64,8 +64,10 @@ class DeviceRun:
         self.w = w
         self.device = torch.device(device)
         self.mgr, self.ids = build_manager(w)
-        self.k_cache = torch.from_numpy(w.pool_k).to(self.device)
-        self.v_cache = torch.from_numpy(w.pool_v).to(self.device)
+        # bf16 values are drawn as float32 (exactly representable) and narrowed on the device
+        self.act_dtype = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float16
+        self.k_cache = self._dev(w.pool_k, w.kv_dtype == "bf16")
+        self.v_cache = self._dev(w.pool_v, w.kv_dtype == "bf16")
         self.i8 = w.kv_dtype == "i8"
         self.layers = int(w.num_layers)
         self.k_scale = torch.from_numpy(w.pool_k_scale).to(self.device) if self.i8 else None
@@ -76,6 +78,10 @@ class DeviceRun:
         self._copied = [None, None]   # event after the last copy out of each
         self._turn = 0
         self._ws = None               # attention workspace, grown as needed
+
+    def _dev(self, a, narrow: bool = True) -> torch.Tensor:
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
+        return t.to(torch.bfloat16) if (narrow and self.act_dtype == torch.bfloat16) else t
 
     def _upload_i32(self, arrays) -> list:
         """The step's int32 metadata arrays packed into one pinned host buffer
@@ -139,8 +145,7 @@ class DeviceRun:
         would hand over; a leading layer axis with several layers), drawn and
         copied outside any timed region."""
         st = self.w.step(s)
-        d = self.device
-        return tuple(torch.from_numpy(np.ascontiguousarray(a)).to(d) for a in (st.new_k, st.new_v, st.q))
+        return tuple(self._dev(a) for a in (st.new_k, st.new_v, st.q))
 
     def prepare(self, s: int = 0, width: Optional[int] = None, acts: Optional[tuple] = None) -> StepInputs:
         """Host bookkeeping of step ``s`` (table growth, slots, copy-on-write
@@ -148,12 +153,7 @@ class DeviceRun:
         are copied too unless ``acts`` (from ``activations``) is given."""
         st = self.w.step(s)
         b = self.mgr.step(self.ids, st.q_lens, width)
-        d = self.device
-
-        def dev(a):
-            return torch.from_numpy(np.ascontiguousarray(a)).to(d)
-
-        nk, nv, q = acts if acts is not None else (dev(st.new_k), dev(st.new_v), dev(st.q))
+        nk, nv, q = acts if acts is not None else (self._dev(st.new_k), self._dev(st.new_v), self._dev(st.q))
         sm, cp, bt, sl, ql = self._upload_i32([b.slot_mapping, b.copy_pairs, b.block_tables, b.seq_lens, b.q_lens])
         return StepInputs(b, sm, cp, bt, sl, ql, nk, nv, q)
 
@@ -251,7 +251,7 @@ class StaticSteps:
         self.h_len = np.full(S, W * w.block_size, np.int32)
         self.h_ql = np.full(S, q_len, np.int32)
         L, hq, hkv, d = run.layers, w.num_q_heads, w.num_kv_heads, w.head_dim
-        f16 = dict(dtype=torch.float16, device=run.device)
+        f16 = dict(dtype=run.act_dtype, device=run.device)
         self.new_k = torch.zeros((L, T, hkv, d), **f16)
         self.new_v = torch.zeros((L, T, hkv, d), **f16)
         self.q = torch.zeros((L, T, hq, d), **f16)

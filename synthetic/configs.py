@@ -69,6 +69,26 @@ def normal_f16(key, shape) -> np.ndarray:
     return _chunked(tuple(key), tuple(shape), np.float16, fill)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16 (ties to even), kept as
+    float32 (every bf16 value is exactly a float32); inputs are finite."""
+    b = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def normal_bf16(key, shape) -> np.ndarray:
+    """N(0,1) float32 draws rounded to bf16 (RNE), held as float32."""
+    def fill(rng, dst):
+        dst[:] = round_bf16(rng.standard_normal(dst.shape[0], dtype=np.float32))
+    return _chunked(tuple(key), tuple(shape), np.float32, fill)
+
+
+def normal_act(kv_dtype: str):
+    """The draw of 16-bit activations and pool values for a pool type."""
+    return normal_bf16 if kv_dtype == "bf16" else normal_f16
+
+
 def uniform_i8(key, shape) -> np.ndarray:
     """Uniform integers in [-127, 127] (filler for unused int8 pool slots)."""
     def fill(rng, dst):
@@ -101,7 +121,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    kv_dtype: str                 # "f16" or "i8"
+    kv_dtype: str                 # "f16", "bf16" (values held as float32) or "i8"
     scale: float
     num_blocks: int
     first_pops: Optional[np.ndarray]   # free-list order: successive pops return these ids
@@ -190,12 +210,13 @@ def _lk(layers):
     return ((), ()) if layers == 1 else ((layers,), (S_LAYERS,))
 
 
-def _f16_pool(seed, nb, hkv, d, layers=1):
+def _f16_pool(seed, nb, hkv, d, layers=1, kv_dtype="f16"):
     _, key = _lk(layers)
     shape = (nb, hkv, BLOCK_SIZE, d) if layers == 1 else (nb, layers, hkv, BLOCK_SIZE, d)
+    draw = normal_act(kv_dtype)
     return {
-        "k": lambda: normal_f16((seed, S_POOL_K, *key), shape),
-        "v": lambda: normal_f16((seed, S_POOL_V, *key), shape),
+        "k": lambda: draw((seed, S_POOL_K, *key), shape),
+        "v": lambda: draw((seed, S_POOL_V, *key), shape),
     }
 
 
@@ -210,14 +231,15 @@ def _i8_pool(seed, nb, hkv, d, layers=1):
     }
 
 
-def _step(seed, tag, q_lens, hq, hkv, d, layers=1):
+def _step(seed, tag, q_lens, hq, hkv, d, layers=1, kv_dtype="f16"):
     t = int(np.sum(q_lens))
     lead, key = _lk(layers)
+    draw = normal_act(kv_dtype)
     return StepDraw(
         q_lens=np.asarray(q_lens, np.int64),
-        new_k=normal_f16((seed, S_NEW_K, *tag, *key), (*lead, t, hkv, d)),
-        new_v=normal_f16((seed, S_NEW_V, *tag, *key), (*lead, t, hkv, d)),
-        q=normal_f16((seed, S_Q, *tag, *key), (*lead, t, hq, d)),
+        new_k=draw((seed, S_NEW_K, *tag, *key), (*lead, t, hkv, d)),
+        new_v=draw((seed, S_NEW_V, *tag, *key), (*lead, t, hkv, d)),
+        q=draw((seed, S_Q, *tag, *key), (*lead, t, hq, d)),
     )
 
 
@@ -240,7 +262,7 @@ def config1(seed: int = 47001) -> Workload:
 
 
 def config2(seed: int = 47002, num_seqs: int = 32, min_prompt: int = 32, max_prompt: int = 512,
-            decode_steps: int = 64, num_layers: int = 1) -> Workload:
+            decode_steps: int = 64, num_layers: int = 1, kv_dtype: str = "f16") -> Workload:
     """GPT-2-small-shaped batch: 12/12 heads, d64; prompts U[32,512] prefilled
     (step 0, causal), then ``decode_steps`` steps of one token per sequence.
     Plain free list (first pops 0, 1, 2, ...); blocks grow on demand.
@@ -254,20 +276,20 @@ def config2(seed: int = 47002, num_seqs: int = 32, min_prompt: int = 32, max_pro
 
     def steps(s):
         if s == 0:
-            return _step(seed, (0,), prompts, hq, hkv, d, num_layers)
-        return _step(seed, (s,), np.ones(num_seqs, np.int64), hq, hkv, d, num_layers)
+            return _step(seed, (0,), prompts, hq, hkv, d, num_layers, kv_dtype)
+        return _step(seed, (s,), np.ones(num_seqs, np.int64), hq, hkv, d, num_layers, kv_dtype)
 
     return Workload(
         name="gpt2-continuous-batch", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
-        block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
+        block_size=BLOCK_SIZE, kv_dtype=kv_dtype, scale=1.0 / math.sqrt(d), num_blocks=nb,
         first_pops=None, ctx_lens=np.zeros(num_seqs, np.int64),
-        pool_draws=_f16_pool(seed, nb, hkv, d, num_layers),
+        pool_draws=_f16_pool(seed, nb, hkv, d, num_layers, kv_dtype),
         steps=steps, num_steps=1 + decode_steps, num_layers=num_layers,
     )
 
 
 def config3(seed: int = 47003, num_seqs: int = 256, max_len: int = 4096, min_len: int = 1,
-            num_q_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128) -> Workload:
+            num_q_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128, kv_dtype: str = "f16") -> Workload:
     """GQA decode: 32/8 heads, d128; post-write lengths U[1,4096]; pool = the
     blocks needed plus 10%, free list a seeded permutation of the pool."""
     hq, hkv, d = num_q_heads, num_kv_heads, head_dim
@@ -277,10 +299,10 @@ def config3(seed: int = 47003, num_seqs: int = 256, max_len: int = 4096, min_len
     perm = rng.permutation(nb)
     return Workload(
         name="gqa-decode", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
-        block_size=BLOCK_SIZE, kv_dtype="f16", scale=1.0 / math.sqrt(d), num_blocks=nb,
+        block_size=BLOCK_SIZE, kv_dtype=kv_dtype, scale=1.0 / math.sqrt(d), num_blocks=nb,
         first_pops=perm, ctx_lens=post - 1,
-        pool_draws=_f16_pool(seed, nb, hkv, d),
-        steps=[_step(seed, (0,), np.ones(num_seqs, np.int64), hq, hkv, d)],
+        pool_draws=_f16_pool(seed, nb, hkv, d, kv_dtype=kv_dtype),
+        steps=[_step(seed, (0,), np.ones(num_seqs, np.int64), hq, hkv, d, kv_dtype=kv_dtype)],
     )
 
 
@@ -397,11 +419,11 @@ def custom(seed: int, kv_lens, q_lens, num_q_heads: int = 8, num_kv_heads: int =
             return (normal_f16((seed, S_CTX_K, i, *key), (*lead, n, hkv, d)),
                     normal_f16((seed, S_CTX_V, i, *key), (*lead, n, hkv, d)))
     else:
-        draws = _f16_pool(seed, nb, hkv, d, num_layers)
+        draws = _f16_pool(seed, nb, hkv, d, num_layers, kv_dtype)
         context = None
     return Workload(
         name=f"custom-{seed}", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=BLOCK_SIZE,
         kv_dtype=kv_dtype, scale=1.0 / math.sqrt(d), num_blocks=nb, first_pops=perm, ctx_lens=ctx,
-        pool_draws=draws, steps=[_step(seed, (0,), ql, hq, hkv, d, num_layers)], context=context,
+        pool_draws=draws, steps=[_step(seed, (0,), ql, hq, hkv, d, num_layers, kv_dtype)], context=context,
         window=int(window), num_layers=int(num_layers),
     )

@@ -17,7 +17,7 @@ import torch
 import synthetic
 from oracle import kv_write as okv
 from oracle import paging as opg
-from tests.oracle_side import OracleSide, assert_attn_close
+from tests.oracle_side import OracleSide, assert_attn_close, dev_np, same_bits
 from tests.test_gpu_parity import SPLITS
 
 pytestmark = pytest.mark.gpu
@@ -43,22 +43,22 @@ def _check_layers(run, ora, s, opts_list=({},)):
     outs = outs if isinstance(outs, list) else [outs]
     ora.write(s, slots, copies)
     torch.cuda.synchronize()
-    assert np.array_equal(run.k_cache.cpu().numpy(), ora.K)
-    assert np.array_equal(run.v_cache.cpu().numpy(), ora.V)
+    assert same_bits(dev_np(run.k_cache), ora.K)
+    assert same_bits(dev_np(run.v_cache), ora.V)
     if w.kv_dtype == "i8":
         assert np.array_equal(run.k_scale.cpu().numpy().view(np.uint16), ora.KS.view(np.uint16))
         assert np.array_equal(run.v_scale.cpu().numpy().view(np.uint16), ora.VS.view(np.uint16))
     for layer in range(w.num_layers):
         ref = ora.attend(s, layer=layer)
-        assert_attn_close(outs[layer].cpu().numpy(), ref, w.kv_dtype == "i8", f"{w.name} step {s} layer {layer}")
+        assert_attn_close(dev_np(outs[layer]), ref, w.kv_dtype, f"{w.name} step {s} layer {layer}")
         for opts in opts_list:
             out = run.attend(x, layer=layer, **opts)
             torch.cuda.synchronize()
-            assert_attn_close(out.cpu().numpy(), ref, w.kv_dtype == "i8", f"layer {layer} {opts}")
+            assert_attn_close(dev_np(out), ref, w.kv_dtype, f"layer {layer} {opts}")
     return x, outs
 
 
-@pytest.mark.parametrize("dt,layers", [("f16", 3), ("i8", 2), ("f16", 1)])
+@pytest.mark.parametrize("dt,layers", [("f16", 3), ("i8", 2), ("f16", 1), ("bf16", 2)])
 def test_layers_mixed_batch(dt, layers):
     w = synthetic.custom(600 + layers, LENS, QLS, 8, 2, 128, dt, num_layers=layers)
     _check_layers(_run(w), OracleSide(w), 0, SPLITS + ({"mfma_min_rows": 1}, {"mfma_min_rows": 2 ** 31 - 1}))

@@ -11,7 +11,7 @@ import torch
 
 import synthetic
 from oracle import paging as opg
-from tests.oracle_side import OracleSide, assert_attn_close
+from tests.oracle_side import OracleSide, assert_attn_close, dev_np, same_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +34,8 @@ def _check_step(run, ora, s, opts_list=({},), check_pool=True):
     ora.write(s, slots, copies)
     torch.cuda.synchronize()
     if check_pool:
-        assert np.array_equal(run.k_cache.cpu().numpy(), ora.K)
-        assert np.array_equal(run.v_cache.cpu().numpy(), ora.V)
+        assert same_bits(dev_np(run.k_cache), ora.K)
+        assert same_bits(dev_np(run.v_cache), ora.V)
         if w.kv_dtype == "i8":
             assert np.array_equal(run.k_scale.cpu().numpy().view(np.uint16), ora.KS.view(np.uint16))
             assert np.array_equal(run.v_scale.cpu().numpy().view(np.uint16), ora.VS.view(np.uint16))
@@ -43,7 +43,7 @@ def _check_step(run, ora, s, opts_list=({},), check_pool=True):
     for opts in opts_list:
         out = run.attend(x, **opts)
         torch.cuda.synchronize()
-        assert_attn_close(out.cpu().numpy(), ref, w.kv_dtype == "i8", f"{w.name} step {s} {opts}")
+        assert_attn_close(dev_np(out), ref, w.kv_dtype, f"{w.name} step {s} {opts}")
     return x
 
 
