@@ -76,6 +76,7 @@ void pa_mgr_destroy(pa_mgr* m);
 
 /* ---- allocator ---------------------------------------------------------- */
 int32_t pa_mgr_num_blocks(const pa_mgr* m);
+int32_t pa_mgr_block_size(const pa_mgr* m);
 int32_t pa_mgr_num_free(const pa_mgr* m);
 /* Pop n blocks (all or none) into out[n]; each starts with one reference. */
 int32_t pa_mgr_allocate(pa_mgr* m, int32_t n, int32_t* out);

@@ -215,6 +215,7 @@ pa_mgr* pa_mgr_create(int32_t num_blocks, int32_t block_size, const int32_t* fir
 void pa_mgr_destroy(pa_mgr* m) { delete m; }
 
 int32_t pa_mgr_num_blocks(const pa_mgr* m) { return m ? m->nb : PA_HOST_ERR_ARG; }
+int32_t pa_mgr_block_size(const pa_mgr* m) { return m ? m->bs : PA_HOST_ERR_ARG; }
 int32_t pa_mgr_num_free(const pa_mgr* m) { return m ? (int32_t)m->stack.size() : PA_HOST_ERR_ARG; }
 
 int32_t pa_mgr_allocate(pa_mgr* m, int32_t n, int32_t* out) {
