@@ -49,6 +49,8 @@ WORKLOADS = {
        "copy-on-write + write + attend, 32/8 heads, head_dim 128, fp16",
     5: "packed-int8: 8 chunks x 512 rows (context U[0,8192]) + 192 decode seqs (kv_len U[1,32768]), "
        "32/8 heads, head_dim 128, int8 KV with per-block-per-head fp16 scales",
+    6: "gpt2-churn: 256 requests (prompts U[32,512], 64 new tokens each) through the continuous-batching "
+       "scheduler over a 1152-block pool, <= 4096 rows and 64 sequences per step, 12/12 heads, head_dim 64",
 }
 
 
@@ -420,6 +422,68 @@ def end_to_end(args, w) -> dict:
     return out
 
 
+def serve_bench(args) -> dict:
+    """Workload 6: the whole request stream through the native scheduler and
+    the library, every step's bookkeeping, metadata copy, writes and
+    attention in the timed region (the activations a model would produce are
+    slices of buffers already on the device).  One untimed pass first."""
+    import torch
+    import synthetic
+    from paged_kv_cache_47_amd.workload import ServeRun
+    rs = synthetic.config6(num_layers=args.layers, kv_dtype=args.kv_dtype)
+    dt = torch.bfloat16 if rs.kv_dtype == "bf16" else torch.float16
+    lead = () if rs.num_layers == 1 else (rs.num_layers,)
+    g = torch.Generator(device="cuda").manual_seed(rs.seed)
+    big = [torch.randn((*lead, rs.max_batch_tokens, h, rs.head_dim), generator=g, device="cuda").to(dt)
+           for h in (rs.num_kv_heads, rs.num_kv_heads, rs.num_q_heads)]
+
+    def acts(step, rows):
+        return tuple(b[..., :rows, :, :] if rs.num_layers == 1 else b[:, :rows] for b in big)
+
+    def one_pass(timed):
+        run = ServeRun(rs, acts=acts)
+        ev, rows, prefill_rows = [], 0, 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while not run.done():
+            if timed:
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record()
+            st, _ = run.step()
+            if timed:
+                b_.record()
+                ev.append((a_, b_))
+            rows += int(st.q_lens.sum())
+            prefill_rows += int(st.q_lens[st.q_lens > 1].sum())
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return run, wall, ev, rows, prefill_rows
+
+    one_pass(False)
+    _warm_clocks()
+    run, wall, ev, rows, prefill_rows = one_pass(True)
+    steps = len(ev)
+    dev_ms = sum(a_.elapsed_time(b_) for a_, b_ in ev)
+    gen = run.sched.counts()["generated"]
+    return {
+        "metric": "continuous batching under churn: generated tokens (seq-steps) per second",
+        "value": round(gen / wall, 1), "unit": "seq-steps/s", "n_gpus": 1, "steps": steps, "warmup": 1,
+        "ms_per_step": round(wall / steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": rs.kv_dtype, "data": "synthetic",
+        "config": {"workload": WORKLOADS[6] + (f" [{rs.num_layers} layers per block]" if rs.num_layers > 1 else ""),
+                   "requests": int(len(rs.prompts)), "new_tokens": int(rs.new_tokens[0]),
+                   "num_blocks": rs.num_blocks, "max_batch_tokens": rs.max_batch_tokens, "max_seqs": rs.max_seqs,
+                   "lookahead": rs.lookahead, "max_skips": rs.max_skips, "layers": rs.num_layers},
+        "generated_tokens": int(gen), "rows": rows, "prefill_rows": prefill_rows,
+        "wall_s": round(wall, 4), "device_ms_per_step": round(dev_ms / steps, 5),
+        "seq_steps_per_s_device": round(gen / (dev_ms * 1e-3), 1),
+        "roofline": None,
+        "note": "wall: the whole stream, host scheduling + metadata copy + writes + attention of every step; "
+                "device: events around each step's work; no roofline line: the steps mix prefill (MFMA) and "
+                "decode (vector) kernels of varying size (workloads 2, 3 and 5 rate each kernel)",
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -481,6 +545,11 @@ def main(argv=None) -> int:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
+    if args.workload == 6:
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps(serve_bench(args)), flush=True)
+        return 0
 
     import torch
     import synthetic
@@ -488,11 +557,11 @@ def main(argv=None) -> int:
     from paged_kv_cache_47_amd.workload import DeviceRun
 
     torch.cuda.set_device(0)
-    if args.layers != 1 and args.workload != 2:
-        print("--layers applies to workload 2 only", file=sys.stderr)
+    if args.layers != 1 and args.workload not in (2, 6):
+        print("--layers applies to workloads 2 and 6 only", file=sys.stderr)
         return 2
-    if args.kv_dtype != "f16" and args.workload not in (2, 3):
-        print("--kv-dtype applies to workloads 2 and 3 only", file=sys.stderr)
+    if args.kv_dtype != "f16" and args.workload not in (2, 3, 6):
+        print("--kv-dtype applies to workloads 2, 3 and 6 only", file=sys.stderr)
         return 2
     if args.workload == 4 and args.no_share:
         w = synthetic.config4(share=False)

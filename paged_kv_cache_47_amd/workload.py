@@ -340,3 +340,97 @@ class StaticSteps:
 
     def replay(self) -> None:
         self.graph.replay()
+
+
+class ServeRun:
+    """A request stream (``synthetic.RequestStream``) through the native
+    continuous-batching scheduler and the library: each step the scheduler
+    releases finished requests, admits waiting ones and reserves the batch's
+    positions (decode rows of running requests, then prefill rows of the new
+    ones, packed); the step's metadata goes to the device in one copy; then
+    per layer the KV write and the attention (the layers after the first
+    reuse the first one's plan).  No sharing, so no block copies."""
+
+    def __init__(self, rs, device: str = "cuda", acts=None):
+        from .sched import Scheduler
+        self.rs = rs
+        self.device = torch.device(device)
+        self.sched = Scheduler(rs.num_blocks, rs.block_size, rs.max_batch_tokens, rs.max_seqs, rs.lookahead,
+                               rs.max_skips)
+        self.next_arrival = 0
+        self.step_index = 0
+        self.act_dtype = torch.bfloat16 if rs.kv_dtype == "bf16" else torch.float16
+        lead = () if rs.num_layers == 1 else (rs.num_layers,)
+        shape = (rs.num_blocks, *lead, rs.num_kv_heads, rs.block_size, rs.head_dim)
+        self.k_cache = torch.zeros(shape, dtype=self.act_dtype, device=self.device)
+        self.v_cache = torch.zeros(shape, dtype=self.act_dtype, device=self.device)
+        self.acts = acts          # None: draw each step's activations; else a callable (step, rows) -> tensors
+        self._pinned = [None, None]
+        self._copied = [None, None]
+        self._turn = 0
+        self._ws = None
+        self.width = 0
+        for _ in range(int(np.sum(rs.arrivals <= 0))):
+            self._arrive()
+
+    def _arrive(self) -> None:
+        i = self.next_arrival
+        self.sched.add(int(self.rs.prompts[i]), int(self.rs.new_tokens[i]))
+        self.next_arrival += 1
+
+    def done(self) -> bool:
+        return self.next_arrival == len(self.rs.prompts) and self.sched.done()
+
+    def _upload(self, arrays) -> list:
+        flat = [np.ascontiguousarray(a, dtype=np.int32).reshape(-1) for a in arrays]
+        n = max(1, sum(a.size for a in flat))
+        t = self._turn = self._turn ^ 1
+        if self._copied[t] is not None:
+            self._copied[t].synchronize()
+        if self._pinned[t] is None or self._pinned[t].numel() < n:
+            self._pinned[t] = torch.empty(2 * n, dtype=torch.int32, pin_memory=True)
+        host = self._pinned[t].numpy()
+        off = 0
+        for a in flat:
+            host[off:off + a.size] = a
+            off += a.size
+        dev = torch.empty(n, dtype=torch.int32, device=self.device)
+        dev.copy_(self._pinned[t][:n], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self._copied[t] = ev
+        out, off = [], 0
+        for a, f in zip(arrays, flat):
+            out.append(dev[off:off + f.size].view(np.shape(a)))
+            off += f.size
+        return out
+
+    def step(self):
+        """One scheduled step; returns (the schedule, the per-layer outputs,
+        or None for an empty batch)."""
+        rs = self.rs
+        while self.next_arrival < len(rs.prompts) and rs.arrivals[self.next_arrival] <= self.step_index:
+            self._arrive()
+        st = self.sched.step()
+        s = self.step_index
+        self.step_index += 1
+        if len(st.rids) == 0:
+            return st, None
+        T = int(st.q_lens.sum())
+        if self.acts is not None:
+            nk, nv, q = self.acts(s, T)
+        else:
+            nk, nv, q = (torch.from_numpy(np.ascontiguousarray(a)).to(self.device).to(self.act_dtype)
+                         for a in rs.acts(s, T))
+        sm, bt, sl, ql = self._upload([st.slot_mapping, st.block_tables, st.seq_lens, st.q_lens])
+        hl, hq = st.seq_lens.copy(), st.q_lens.copy()
+        need = pa.pa_attend_workspace_bytes(self.k_cache, rs.num_q_heads, hl, hq)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(2 * need, dtype=torch.uint8, device=self.device)
+        outs = []
+        for layer in range(rs.num_layers):
+            lk, lv, lq = (nk, nv, q) if rs.num_layers == 1 else (nk[layer], nv[layer], q[layer])
+            pa.pa_write_kv(lk, lv, sm, self.k_cache, self.v_cache, layer=layer)
+            outs.append(pa.pa_attend(lq, self.k_cache, self.v_cache, bt, sl, ql, hl, hq, rs.scale,
+                                     workspace=self._ws, layer=layer, reuse_plan=layer > 0))
+        return st, outs

@@ -7,6 +7,6 @@ quantisation); both the HIP path's harness and the CPU oracle take their
 inputs from here and each builds everything else on its own.
 """
 from .configs import (  # noqa: F401
-    Workload, StepDraw, normal_f16, config1, config2, config3, config4, config5,
-    CONFIGS, custom,
+    Workload, StepDraw, RequestStream, normal_f16, normal_bf16, round_bf16, config1, config2, config3, config4,
+    config5, config6, CONFIGS, custom,
 )

@@ -427,3 +427,59 @@ def custom(seed: int, kv_lens, q_lens, num_q_heads: int = 8, num_kv_heads: int =
         pool_draws=draws, steps=[_step(seed, (0,), ql, hq, hkv, d, num_layers, kv_dtype)], context=context,
         window=int(window), num_layers=int(num_layers),
     )
+
+
+@dataclass
+class RequestStream:
+    """Requests for the continuous-batching scheduler: arrival step, prompt
+    length and tokens to generate each, the attention shape, the pool and the
+    scheduler's limits.  Activations of step s are drawn under tag (s,)."""
+    name: str
+    seed: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    kv_dtype: str
+    scale: float
+    num_blocks: int
+    arrivals: np.ndarray          # step at which each request is queued
+    prompts: np.ndarray
+    new_tokens: np.ndarray
+    max_batch_tokens: int
+    max_seqs: int
+    lookahead: int
+    max_skips: int
+    num_layers: int = 1
+
+    def acts(self, s: int, rows: int) -> tuple:
+        """(new_k, new_v, q) of step ``s`` with ``rows`` packed rows (a leading
+        layer axis with several layers)."""
+        st = _step(self.seed, (s,), [rows], self.num_q_heads, self.num_kv_heads, self.head_dim, self.num_layers,
+                   self.kv_dtype)
+        return st.new_k, st.new_v, st.q
+
+
+def config6(seed: int = 47006, num_requests: int = 256, min_prompt: int = 32, max_prompt: int = 512,
+            new_tokens: int = 64, num_blocks: int = 1152, max_batch_tokens: int = 4096, max_seqs: int = 64,
+            lookahead: int = 4, max_skips: int = 8, arrive_per_step: int = 0, num_layers: int = 1,
+            kv_dtype: str = "f16") -> RequestStream:
+    """Continuous batching under churn, GPT-2-small-shaped (12/12 heads, d64):
+    ``num_requests`` requests with prompts U[32,512] each generating 64
+    tokens (every request of the engine page's workload generates 64), over
+    a 1152-block pool (the 32-request batch of workload 2), at most 4096 rows
+    and 64 sequences per step.  ``arrive_per_step`` = 0 queues every request
+    at once; k > 0 queues k per step."""
+    hq = hkv = 12
+    d = 64
+    rng = np.random.default_rng([seed, S_META])
+    prompts = rng.integers(min_prompt, max_prompt + 1, num_requests).astype(np.int64)
+    arrivals = (np.zeros(num_requests, np.int64) if arrive_per_step <= 0
+                else np.arange(num_requests, dtype=np.int64) // int(arrive_per_step))
+    return RequestStream(
+        name="gpt2-continuous-batching-churn", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        block_size=BLOCK_SIZE, kv_dtype=kv_dtype, scale=1.0 / math.sqrt(d), num_blocks=num_blocks,
+        arrivals=arrivals, prompts=prompts, new_tokens=np.full(num_requests, new_tokens, np.int64),
+        max_batch_tokens=max_batch_tokens, max_seqs=max_seqs, lookahead=lookahead, max_skips=max_skips,
+        num_layers=num_layers,
+    )
