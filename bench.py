@@ -430,7 +430,7 @@ def serve_bench(args) -> dict:
     import torch
     import synthetic
     from paged_kv_cache_47_amd.workload import ServeRun
-    rs = synthetic.config6(num_layers=args.layers, kv_dtype=args.kv_dtype)
+    rs = synthetic.config6(num_layers=args.layers, kv_dtype=args.kv_dtype, system_prompts=args.system_prompts)
     dt = torch.bfloat16 if rs.kv_dtype == "bf16" else torch.float16
     lead = () if rs.num_layers == 1 else (rs.num_layers,)
     g = torch.Generator(device="cuda").manual_seed(rs.seed)
@@ -470,11 +470,14 @@ def serve_bench(args) -> dict:
         "value": round(gen / wall, 1), "unit": "seq-steps/s", "n_gpus": 1, "steps": steps, "warmup": 1,
         "ms_per_step": round(wall / steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": rs.kv_dtype, "data": "synthetic",
-        "config": {"workload": WORKLOADS[6] + (f" [{rs.num_layers} layers per block]" if rs.num_layers > 1 else ""),
+        "config": {"workload": WORKLOADS[6] + (f" [{rs.num_layers} layers per block]" if rs.num_layers > 1 else "")
+                   + (f" [prompts = one of {args.system_prompts} shared system prompts of U[64,256] tokens + "
+                      "U[32,512] own tokens, through the prefix cache]" if args.system_prompts else ""),
                    "requests": int(len(rs.prompts)), "new_tokens": int(rs.new_tokens[0]),
                    "num_blocks": rs.num_blocks, "max_batch_tokens": rs.max_batch_tokens, "max_seqs": rs.max_seqs,
                    "lookahead": rs.lookahead, "max_skips": rs.max_skips, "layers": rs.num_layers},
         "generated_tokens": int(gen), "rows": rows, "prefill_rows": prefill_rows,
+        "prompt_tokens": int(rs.prompts.sum()), "prompt_tokens_from_cache": int(run.sched.cached_tokens),
         "wall_s": round(wall, 4), "device_ms_per_step": round(dev_ms / steps, 5),
         "seq_steps_per_s_device": round(gen / (dev_ms * 1e-3), 1),
         "roofline": None,
@@ -503,6 +506,9 @@ def main(argv=None) -> int:
                          "every layer over one set of metadata")
     ap.add_argument("--kv-dtype", default="f16", choices=("f16", "bf16"),
                     help="workloads 2 and 3: the pool type (bf16 pools take and return bf16 activations)")
+    ap.add_argument("--system-prompts", type=int, default=0,
+                    help="workload 6: requests start with one of this many shared system prompts, served from "
+                         "the prefix cache")
     ap.add_argument("--no-share", action="store_true",
                     help="workload 4 control: every sequence owns its own copy of the prefix (no sharing, no forks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

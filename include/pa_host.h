@@ -36,7 +36,7 @@
  * - Every call returns a pa_host_status; on any error nothing changed (calls
  *   are atomic), except pa_mgr_free_all, which stops at the first bad id.
  * - A block whose reference count drops to zero goes back on the free stack
- *   at once.
+ *   at once, unless it is published in the prefix cache (below).
  */
 #ifndef PA_HOST_H
 #define PA_HOST_H
@@ -118,6 +118,44 @@ int32_t pa_mgr_seq_len(const pa_mgr* m, int32_t sid);
 int32_t pa_mgr_seq_blocks(const pa_mgr* m, int32_t sid, int32_t* out, int32_t cap);
 /* Slots of the existing positions start .. start+n-1 of sid into out[n]. */
 int32_t pa_mgr_slots(const pa_mgr* m, int32_t sid, int32_t start, int32_t n, int32_t* out);
+
+/* ---- prefix cache --------------------------------------------------------- */
+/*
+ * [manager] "Architecture Overview" and "Step 4: The Prefix Tree (Radix
+ * Trie)": a tree
+ * whose edges are the token ids of one full block maps prompt prefixes to the
+ * blocks that hold them, so a request whose prompt starts with a known prefix
+ * reuses those blocks; "Step 2: The Block Pool": blocks whose reference count
+ * has dropped to zero are reclaimed least recently used first.  Here a published block whose count
+ * drops to zero is cached (neither free nor allocated, still in the tree);
+ * allocation takes the free stack first and, when it is empty, evicts the
+ * least recently released cached block together with its subtree (cached
+ * nodes go back on the stack, children before parents; nodes still in use
+ * only leave the tree).  Blocks never published are freed at once as before.
+ * Free-capacity checks (allocation, steps) count cached blocks as available.
+ */
+
+/*
+ * pa_mgr_add_sequence_prefix - a new sequence for a prompt of n tokens that
+ * starts with the longest chain of published full blocks matching its
+ * tokens (at most (n - 1) / block_size blocks: one prompt token is always
+ * left to compute).  The sequence holds those blocks (one more reference
+ * each; cached ones are revived) and has *cached_tokens = their tokens as its
+ * length; the rest of the prompt is reserved by later steps.
+ */
+int32_t pa_mgr_add_sequence_prefix(pa_mgr* m, const int32_t* tokens, int32_t n, int32_t* sid,
+                                   int32_t* cached_tokens);
+
+/*
+ * pa_mgr_publish - enter sid's full blocks that hold tokens[0 .. n-1] (after
+ * their K/V have been written, or ordered before any later read) into the
+ * tree, root first.  A path that already leads to another block, a block that
+ * is already a node elsewhere, or a released block ends the walk.
+ */
+int32_t pa_mgr_publish(pa_mgr* m, int32_t sid, const int32_t* tokens, int32_t n);
+
+/* Cached blocks (refcount 0, still in the tree). */
+int32_t pa_mgr_num_cached(const pa_mgr* m);
 
 /* ---- steps -------------------------------------------------------------- */
 /*

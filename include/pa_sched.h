@@ -60,6 +60,16 @@ void pa_sched_destroy(pa_sched* s);
  * lifetime blocks than the pool holds). */
 int32_t pa_sched_add(pa_sched* s, int32_t prompt_len, int32_t new_tokens, int32_t* rid);
 
+/* A request with token ids (prompt = tokens[0 .. n-1]): on admission its
+ * prompt is matched against the manager's prefix cache (pa_host.h), its first
+ * step reserves only the positions after the cached ones, and after that step
+ * its full prompt blocks are published.  Admission still reserves the whole
+ * lifetime (cached blocks count among the available ones). */
+int32_t pa_sched_add_tokens(pa_sched* s, const int32_t* tokens, int32_t n, int32_t new_tokens, int32_t* rid);
+
+/* Prompt tokens served from the prefix cache so far. */
+int64_t pa_sched_cached_tokens(const pa_sched* s);
+
 /* Widest block table any step can need: the largest lifetime in blocks of
  * the requests added so far (at least 1). */
 int32_t pa_sched_max_width(const pa_sched* s);

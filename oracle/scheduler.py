@@ -32,6 +32,10 @@ scheduler too):
   admitted, and only once it fits; then it leaves blocking mode.
 * the batch lists the running requests first (in admission order), then the
   requests admitted in this step (in admission order).
+* requests that carry token ids ([manager]'s prefix tree, ``oracle.prefix``)
+  are matched against the published blocks on admission: their first step
+  reserves only the positions after the cached prefix, and after it their
+  full prompt blocks are published.  Cached blocks count as available.
 """
 from __future__ import annotations
 
@@ -39,6 +43,7 @@ from dataclasses import dataclass, field
 from typing import List
 
 from . import paging as opg
+from .prefix import RefPrefixPool
 
 
 @dataclass
@@ -48,6 +53,8 @@ class Req:
     new: int
     sid: int = -1
     generated: int = 0
+    tokens: tuple = ()
+    first_rows: int = 0
     state: str = "waiting"     # waiting | running | finished
 
 
@@ -68,6 +75,8 @@ class RefScheduler:
     def __init__(self, num_blocks: int, block_size: int, max_batch_tokens: int, max_seqs: int,
                  lookahead: int, max_skips: int, first_pops=None):
         self.st = opg.RefState(num_blocks, block_size, first_pops)
+        self.st.pool = RefPrefixPool(num_blocks, first_pops)
+        self.cached_tokens = 0
         self.bs = block_size
         self.max_tokens, self.max_seqs = max_batch_tokens, max_seqs
         self.lookahead, self.max_skips = lookahead, max_skips
@@ -85,6 +94,11 @@ class RefScheduler:
         self.reqs.append(r)
         self.waiting.append(r.rid)
         return r.rid
+
+    def add_tokens(self, tokens, new: int) -> int:
+        rid = self.add(len(tokens), new)
+        self.reqs[rid].tokens = tuple(int(t) for t in tokens)
+        return rid
 
     def _owed(self) -> int:
         owed = 0
@@ -110,7 +124,7 @@ class RefScheduler:
         # 2. running requests decode one token each
         decode = list(self.running)
         # 3. admission
-        avail = self.st.pool.num_free - self._owed()
+        avail = self.st.pool.num_free + self.st.pool.num_cached - self._owed()
         tokens = self.max_tokens - len(decode)
         seqs = self.max_seqs - len(decode)
         admitted = []
@@ -144,6 +158,13 @@ class RefScheduler:
             self.waiting.remove(rid)
             r = self.reqs[rid]
             r.sid = self.st.add(0)
+            cached = []
+            if r.tokens:
+                cached = self.st.pool.match(r.tokens, self.bs)
+                self.st.tables[r.sid] = list(cached)
+                self.st.lens[r.sid] = len(cached) * self.bs
+            r.first_rows = r.prompt - len(cached) * self.bs
+            self.cached_tokens += len(cached) * self.bs
             r.state = "running"
             self.running.append(rid)
         # 4. the batch: running first, then the newly admitted
@@ -152,7 +173,7 @@ class RefScheduler:
             out.q_lens.append(1)
         for rid in admitted:
             out.rids.append(rid)
-            out.q_lens.append(self.reqs[rid].prompt)
+            out.q_lens.append(self.reqs[rid].first_rows)
         out.admitted = admitted
         out.blocking = self.blocking
         return out
@@ -168,6 +189,10 @@ class RefScheduler:
             assert not copies
             slots += s
             r.generated += 1
+        for rid in step.admitted:
+            r = self.reqs[rid]
+            if r.tokens:
+                self.st.pool.publish(self.st.tables[r.sid], self.st.lens[r.sid], r.tokens, self.bs)
         return slots
 
     def done(self) -> bool:

@@ -5,11 +5,19 @@
 // with reference-count changes kept in a scratch overlay), so a step that the
 // pool cannot supply is refused before anything changes; the real pass then
 // performs the same operations in the same order and cannot fail.
+//
+// Prefix cache: published full blocks are nodes of a tree whose edges are
+// the blocks' token ids (one block per edge), kept as a hash map from
+// (parent block, tokens) to block.  A published block whose reference count
+// drops to zero is cached instead of freed; when the free stack is empty, the
+// least recently released cached block is evicted together with its subtree
+// (cached nodes are freed, nodes still in use only leave the tree).
 #include "pa_host.h"
 
 #include <algorithm>
 #include <cstring>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 namespace {
@@ -23,6 +31,20 @@ struct Seq {
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
+struct PrefixKey {
+  int32_t parent;                // parent block, -1 for the root
+  std::vector<int32_t> tokens;   // the block's token ids
+  bool operator==(const PrefixKey& o) const { return parent == o.parent && tokens == o.tokens; }
+};
+
+struct PrefixKeyHash {
+  size_t operator()(const PrefixKey& k) const {
+    uint64_t h = 1469598103934665603ull ^ (uint32_t)k.parent;
+    for (int32_t t : k.tokens) h = (h ^ (uint32_t)t) * 1099511628211ull;
+    return (size_t)h;
+  }
+};
+
 }  // namespace
 
 struct pa_mgr {
@@ -30,6 +52,15 @@ struct pa_mgr {
   std::vector<int32_t> stack;    // free stack; its top is the back
   std::vector<int32_t> refs;     // reference count per block (0 = free)
   std::vector<Seq> seqs;
+  // prefix cache (sized on the first publish): tree nodes, their edges, and
+  // the least-recently-released list of cached blocks (refcount 0, in the tree)
+  std::unordered_map<PrefixKey, int32_t, PrefixKeyHash> index;
+  std::vector<uint8_t> indexed;
+  std::vector<int32_t> node_parent;
+  std::vector<std::vector<int32_t>> children;
+  std::vector<std::vector<int32_t>> node_tokens;
+  std::vector<int32_t> lru_prev, lru_next;
+  int32_t lru_head = -1, lru_tail = -1, cached = 0;
   // dry-run scratch: reference-count deltas of touched blocks, per-sequence stamps
   mutable std::vector<int32_t> delta;
   mutable std::vector<int32_t> touched;
@@ -39,14 +70,80 @@ struct pa_mgr {
   bool held(int32_t b) const { return b >= 0 && b < nb && refs[b] > 0; }
   bool valid_seq(int32_t s) const { return s >= 0 && s < (int32_t)seqs.size(); }
 
+  int64_t available() const { return (int64_t)stack.size() + cached; }
+
+  // the caller has checked available() >= 1
   int32_t pop() {
+    if (stack.empty()) evict(lru_head);
     const int32_t b = stack.back();
     stack.pop_back();
     refs[b] = 1;
     return b;
   }
   void drop(int32_t b) {   // b is held
-    if (--refs[b] == 0) stack.push_back(b);
+    if (--refs[b] == 0) {
+      if (!indexed.empty() && indexed[b]) {
+        lru_push(b);
+      } else {
+        stack.push_back(b);
+      }
+    }
+  }
+  // a cached block taken by a prefix match
+  void revive(int32_t b) {
+    if (refs[b] == 0) lru_remove(b);
+    ++refs[b];
+  }
+
+  void lru_push(int32_t b) {
+    lru_prev[b] = lru_tail;
+    lru_next[b] = -1;
+    if (lru_tail >= 0) lru_next[lru_tail] = b;
+    else lru_head = b;
+    lru_tail = b;
+    ++cached;
+  }
+  void lru_remove(int32_t b) {
+    if (lru_prev[b] >= 0) lru_next[lru_prev[b]] = lru_next[b];
+    else lru_head = lru_next[b];
+    if (lru_next[b] >= 0) lru_prev[lru_next[b]] = lru_prev[b];
+    else lru_tail = lru_prev[b];
+    --cached;
+  }
+  // Take node b and its subtree out of the tree: the subtree is listed
+  // breadth first and handled in reverse (deepest first, b last); cached
+  // nodes go back on the free stack, nodes in use only leave the tree (they
+  // are freed normally when released).
+  void evict(int32_t b) {
+    std::vector<int32_t> pre{b};
+    for (size_t i = 0; i < pre.size(); ++i)
+      for (int32_t c : children[pre[i]]) pre.push_back(c);
+    const int32_t parent = node_parent[b];
+    if (parent >= 0) {
+      auto& sib = children[parent];
+      sib.erase(std::find(sib.begin(), sib.end(), b));
+    }
+    for (auto it = pre.rbegin(); it != pre.rend(); ++it) {
+      const int32_t x = *it;
+      index.erase(PrefixKey{node_parent[x], node_tokens[x]});
+      children[x].clear();
+      node_tokens[x].clear();
+      node_parent[x] = -1;
+      indexed[x] = 0;
+      if (refs[x] == 0) {
+        lru_remove(x);
+        stack.push_back(x);
+      }
+    }
+  }
+  void enable_prefix() {
+    if (!indexed.empty()) return;
+    indexed.assign(nb, 0);
+    node_parent.assign(nb, -1);
+    children.assign(nb, {});
+    node_tokens.assign(nb, {});
+    lru_prev.assign(nb, -1);
+    lru_next.assign(nb, -1);
   }
 
   // ---- dry run ----------------------------------------------------------
@@ -106,7 +203,7 @@ struct pa_mgr {
       std::fill(seen.begin(), seen.end(), 0);
       epoch = 1;
     }
-    int64_t avail = (int64_t)stack.size();
+    int64_t avail = available();
     int32_t st = PA_HOST_OK;
     for (int32_t i = 0; i < num && st == PA_HOST_OK; ++i) {
       const int32_t s = sids[i], n = q_lens[i];
@@ -220,7 +317,7 @@ int32_t pa_mgr_num_free(const pa_mgr* m) { return m ? (int32_t)m->stack.size() :
 
 int32_t pa_mgr_allocate(pa_mgr* m, int32_t n, int32_t* out) {
   if (!m || n < 0 || (n > 0 && !out)) return PA_HOST_ERR_ARG;
-  if ((size_t)n > m->stack.size()) return PA_HOST_ERR_EXHAUSTED;
+  if (n > m->available()) return PA_HOST_ERR_EXHAUSTED;
   for (int32_t i = 0; i < n; ++i) out[i] = m->pop();
   return PA_HOST_OK;
 }
@@ -293,7 +390,7 @@ int32_t pa_mgr_add_sequence(pa_mgr* m, int32_t num_tokens, int32_t shared_from, 
     return PA_HOST_ERR_ARG;
   }
   const int32_t need = ceil_div((int64_t)num_tokens - (int64_t)nshared * m->bs, m->bs);
-  if ((size_t)need > m->stack.size()) return PA_HOST_ERR_EXHAUSTED;
+  if (need > m->available()) return PA_HOST_ERR_EXHAUSTED;
   try {
     Seq s;
     s.blocks.reserve(nshared + need);
@@ -307,6 +404,73 @@ int32_t pa_mgr_add_sequence(pa_mgr* m, int32_t num_tokens, int32_t shared_from, 
   for (int32_t i = 0; i < need; ++i) s.blocks.push_back(m->pop());
   for (int32_t j = 0; j < nshared; ++j) ++m->refs[s.blocks[j]];
   *sid = (int32_t)m->seqs.size() - 1;
+  return PA_HOST_OK;
+}
+
+int32_t pa_mgr_num_cached(const pa_mgr* m) { return m ? m->cached : PA_HOST_ERR_ARG; }
+
+int32_t pa_mgr_add_sequence_prefix(pa_mgr* m, const int32_t* tokens, int32_t n, int32_t* sid,
+                                   int32_t* cached_tokens) {
+  if (!m || !sid || !cached_tokens || n < 1 || !tokens) return PA_HOST_ERR_ARG;
+  std::vector<int32_t> matched;
+  if (!m->indexed.empty()) {
+    const int32_t maxb = (n - 1) / m->bs;   // at least one prompt token is left to compute
+    PrefixKey key{-1, {}};
+    for (int32_t j = 0; j < maxb; ++j) {
+      key.tokens.assign(tokens + (int64_t)j * m->bs, tokens + (int64_t)(j + 1) * m->bs);
+      auto it = m->index.find(key);
+      if (it == m->index.end()) break;
+      matched.push_back(it->second);
+      key.parent = it->second;
+    }
+  }
+  try {
+    Seq s;
+    s.blocks = matched;
+    s.len = (int32_t)matched.size() * m->bs;
+    m->seqs.push_back(std::move(s));
+  } catch (...) {
+    return PA_HOST_ERR_ARG;
+  }
+  for (int32_t b : matched) m->revive(b);
+  *sid = (int32_t)m->seqs.size() - 1;
+  *cached_tokens = (int32_t)matched.size() * m->bs;
+  return PA_HOST_OK;
+}
+
+int32_t pa_mgr_publish(pa_mgr* m, int32_t sid, const int32_t* tokens, int32_t n) {
+  if (!m || !m->valid_seq(sid) || n < 0 || (n > 0 && !tokens)) return PA_HOST_ERR_ARG;
+  const Seq& s = m->seqs[sid];
+  if (!s.live) return PA_HOST_ERR_ARG;
+  try {
+    m->enable_prefix();
+  } catch (...) {
+    return PA_HOST_ERR_ARG;
+  }
+  const int32_t nfull = std::min(n, s.len) / m->bs;
+  PrefixKey key{-1, {}};
+  for (int32_t j = 0; j < nfull; ++j) {
+    const int32_t b = s.blocks[j];
+    if (b < 0) break;                                // released by a sliding window
+    key.tokens.assign(tokens + (int64_t)j * m->bs, tokens + (int64_t)(j + 1) * m->bs);
+    auto it = m->index.find(key);
+    if (it != m->index.end()) {
+      if (it->second != b) break;                    // another block already holds this path
+      key.parent = b;
+      continue;
+    }
+    if (m->indexed[b]) break;                        // this block is a node on another path
+    try {
+      m->index.emplace(key, b);
+      if (key.parent >= 0) m->children[key.parent].push_back(b);
+    } catch (...) {
+      return PA_HOST_ERR_ARG;
+    }
+    m->indexed[b] = 1;
+    m->node_parent[b] = key.parent;
+    m->node_tokens[b] = key.tokens;
+    key.parent = b;
+  }
   return PA_HOST_OK;
 }
 

@@ -13,6 +13,8 @@ namespace {
 
 struct Req {
   int32_t prompt = 0, want = 0;   // P, N
+  int32_t tok0 = -1;              // first of its prompt tokens in the token store (-1: none)
+  int32_t first_rows = 0;         // rows of its first step: P minus the cached prefix
   int32_t sid = -1;
   int32_t generated = 0;
   int32_t state = 0;              // 0 waiting, 1 running, 2 finished
@@ -32,7 +34,8 @@ struct pa_sched {
   int32_t head_skips = 0;
   int32_t max_width = 1;
   int32_t n_finished = 0;
-  int64_t generated = 0;
+  int64_t generated = 0, cached_tokens = 0;
+  std::vector<int32_t> tokens;    // prompt tokens of the requests that carry them
   std::vector<int32_t> admitted, decode;   // per-step scratch
 
   int32_t lifetime(const Req& r) const { return blocks_for((int64_t)r.prompt + r.want - 1, bs); }
@@ -79,6 +82,25 @@ int32_t pa_sched_add(pa_sched* s, int32_t prompt_len, int32_t new_tokens, int32_
   return PA_HOST_OK;
 }
 
+int32_t pa_sched_add_tokens(pa_sched* s, const int32_t* tokens, int32_t n, int32_t new_tokens, int32_t* rid) {
+  if (!s || !tokens || n < 1) return PA_HOST_ERR_ARG;
+  const size_t at = s->tokens.size();
+  try {
+    s->tokens.insert(s->tokens.end(), tokens, tokens + n);
+  } catch (...) {
+    return PA_HOST_ERR_ARG;
+  }
+  const int32_t st = pa_sched_add(s, n, new_tokens, rid);
+  if (st != PA_HOST_OK) {
+    s->tokens.resize(at);
+    return st;
+  }
+  s->reqs[*rid].tok0 = (int32_t)at;
+  return PA_HOST_OK;
+}
+
+int64_t pa_sched_cached_tokens(const pa_sched* s) { return s ? s->cached_tokens : (int64_t)PA_HOST_ERR_ARG; }
+
 int32_t pa_sched_max_width(const pa_sched* s) { return s ? s->max_width : PA_HOST_ERR_ARG; }
 
 int32_t pa_sched_step(pa_sched* s, int32_t* rids, int32_t* sids, int32_t* q_lens, int32_t* num_rows,
@@ -114,7 +136,7 @@ int32_t pa_sched_step(pa_sched* s, int32_t* rids, int32_t* sids, int32_t* q_lens
   // 3. admission
   int64_t owed = 0;
   for (int32_t rid : s->running) owed += s->lifetime(s->reqs[rid]) - s->held(s->reqs[rid]);
-  int64_t avail = (int64_t)pa_mgr_num_free(s->m) - owed;
+  int64_t avail = (int64_t)pa_mgr_num_free(s->m) + pa_mgr_num_cached(s->m) - owed;
   int64_t tokens = (int64_t)s->max_tokens - (int64_t)s->decode.size();
   int64_t seqs = (int64_t)s->max_seqs - (int64_t)s->decode.size();
   s->admitted.clear();
@@ -148,10 +170,14 @@ int32_t pa_sched_step(pa_sched* s, int32_t* rids, int32_t* sids, int32_t* q_lens
   for (int32_t rid : s->admitted) {
     s->waiting.erase(std::find(s->waiting.begin(), s->waiting.end(), rid));
     Req& r = s->reqs[rid];
-    int32_t sid = -1;
-    const int32_t st = pa_mgr_add_sequence(s->m, 0, -1, 0, &sid);
-    if (st != PA_HOST_OK) return st;   // cannot happen: an empty sequence takes no block
+    int32_t sid = -1, cached = 0;
+    // cannot fail: an empty sequence takes no block, a prefix match only takes references
+    const int32_t st = r.tok0 >= 0 ? pa_mgr_add_sequence_prefix(s->m, &s->tokens[r.tok0], r.prompt, &sid, &cached)
+                                   : pa_mgr_add_sequence(s->m, 0, -1, 0, &sid);
+    if (st != PA_HOST_OK) return st;
     r.sid = sid;
+    r.first_rows = r.prompt - cached;
+    s->cached_tokens += cached;
     r.state = 1;
     s->running.push_back(rid);
   }
@@ -166,7 +192,7 @@ int32_t pa_sched_step(pa_sched* s, int32_t* rids, int32_t* sids, int32_t* q_lens
   for (int32_t rid : s->admitted) {
     rids[n] = rid;
     sids[n] = s->reqs[rid].sid;
-    q_lens[n] = s->reqs[rid].prompt;
+    q_lens[n] = s->reqs[rid].first_rows;
     ++n;
   }
   *num_rows = n;
@@ -178,6 +204,12 @@ int32_t pa_sched_step(pa_sched* s, int32_t* rids, int32_t* sids, int32_t* q_lens
   for (int32_t i = 0; i < n; ++i) {
     ++s->reqs[rids[i]].generated;
     ++s->generated;
+  }
+  // the new requests' prompts enter the prefix cache (their K/V are written by this step's
+  // device work, which every later step's reads follow)
+  for (int32_t rid : s->admitted) {
+    const Req& r = s->reqs[rid];
+    if (r.tok0 >= 0) pa_mgr_publish(s->m, r.sid, &s->tokens[r.tok0], r.prompt);
   }
   return PA_HOST_OK;
 }

@@ -30,8 +30,16 @@ Behaviour follows the pages:
   before position ``seq_len - q_len - w + 1``; once a sequence has reserved
   its positions for the step, every block holding only earlier positions is
   released (in table order) and its table entry becomes -1.
-A block whose refcount drops to zero goes straight back on the free stack.
-A step either reserves every listed sequence's positions or changes nothing.
+* [manager] "Step 4: The Prefix Tree (Radix Trie)" and "Step 2: The Block
+  Pool": published full blocks form a tree keyed by their token ids, so a
+  prompt starting with a known prefix reuses its blocks
+  (``add_sequence_prefix``, ``publish``); zero-refcount blocks are reclaimed
+  least recently used first.
+A block whose refcount drops to zero goes straight back on the free stack,
+unless it is published in the prefix cache: then it stays cached until an
+allocation finds the free stack empty and evicts the least recently released
+cached block (with its subtree).  A step either reserves every listed
+sequence's positions or changes nothing.
 """
 from __future__ import annotations
 
@@ -65,6 +73,9 @@ def _native():
         "pa_mgr_destroy": ([vp], None),
         "pa_mgr_num_blocks": ([vp], i32),
         "pa_mgr_num_free": ([vp], i32),
+        "pa_mgr_num_cached": ([vp], i32),
+        "pa_mgr_add_sequence_prefix": ([vp, vp, i32, vp, vp], i32),
+        "pa_mgr_publish": ([vp, i32, vp, i32], i32),
         "pa_mgr_allocate": ([vp, i32, vp], i32),
         "pa_mgr_refcount": ([vp, i32], i32),
         "pa_mgr_retain": ([vp, i32], i32),
@@ -151,10 +162,16 @@ class BlockAllocator:
 
     @property
     def num_free(self) -> int:
+        """Blocks on the free stack."""
         return self._lib.pa_mgr_num_free(self._h.ptr)
 
+    @property
+    def num_cached(self) -> int:
+        """Blocks held by nobody but kept in the prefix cache (reclaimable)."""
+        return self._lib.pa_mgr_num_cached(self._h.ptr)
+
     def can_allocate(self, num_blocks: int) -> bool:
-        return num_blocks <= self.num_free
+        return num_blocks <= self.num_free + self.num_cached
 
     def allocate(self) -> int:
         out = ctypes.c_int32()
@@ -264,6 +281,21 @@ class PagedKVManager:
             raise ValueError("shared prefix must be whole blocks of the source sequence")
         _ok(st, "add_sequence")
         return sid.value
+
+    def add_sequence_prefix(self, tokens: Sequence[int]) -> tuple:
+        """New sequence for a prompt: it starts with the longest chain of
+        published full blocks matching ``tokens`` (leaving at least one token);
+        returns (sequence id, cached tokens = its length)."""
+        t = _i32(tokens)
+        sid, cached = ctypes.c_int32(), ctypes.c_int32()
+        _ok(self._lib.pa_mgr_add_sequence_prefix(self._h.ptr, t.ctypes.data, len(t), ctypes.addressof(sid),
+                                                 ctypes.addressof(cached)), "add_sequence_prefix")
+        return sid.value, cached.value
+
+    def publish(self, sid: int, tokens: Sequence[int]) -> None:
+        """Enter the sequence's full blocks holding ``tokens`` into the prefix cache."""
+        t = _i32(tokens)
+        _ok(self._lib.pa_mgr_publish(self._h.ptr, int(sid), t.ctypes.data, len(t)), "publish")
 
     def fork(self, sid: int) -> int:
         child = ctypes.c_int32()

@@ -28,6 +28,8 @@ def _native():
         "pa_sched_create": ([vp, i32, i32, i32, i32], vp),
         "pa_sched_destroy": ([vp], None),
         "pa_sched_add": ([vp, i32, i32, vp], i32),
+        "pa_sched_add_tokens": ([vp, vp, i32, i32, vp], i32),
+        "pa_sched_cached_tokens": ([vp], ctypes.c_int64),
         "pa_sched_max_width": ([vp], i32),
         "pa_sched_step": ([vp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp], i32),
         "pa_sched_counts": ([vp, vp, vp, vp, vp, vp], i32),
@@ -78,6 +80,19 @@ class Scheduler:
         rid = ctypes.c_int32()
         _ok(self._lib.pa_sched_add(self.ptr, int(prompt_len), int(new_tokens), ctypes.addressof(rid)), "add")
         return rid.value
+
+    def add_tokens(self, tokens, new_tokens: int) -> int:
+        """Queue a request whose prompt is ``tokens`` (matched against and then
+        published into the prefix cache)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        rid = ctypes.c_int32()
+        _ok(self._lib.pa_sched_add_tokens(self.ptr, t.ctypes.data, len(t), int(new_tokens), ctypes.addressof(rid)),
+            "add")
+        return rid.value
+
+    @property
+    def cached_tokens(self) -> int:
+        return self._lib.pa_sched_cached_tokens(self.ptr)
 
     @property
     def max_width(self) -> int:

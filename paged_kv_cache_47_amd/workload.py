@@ -349,7 +349,10 @@ class ServeRun:
     positions (decode rows of running requests, then prefill rows of the new
     ones, packed); the step's metadata goes to the device in one copy; then
     per layer the KV write and the attention (the layers after the first
-    reuse the first one's plan).  No sharing, so no block copies."""
+    reuse the first one's plan).  Requests with token ids start from the
+    blocks the prefix cache holds for their prompt's prefix: their first step
+    writes and attends only the rest of the prompt.  Shared blocks are full
+    and never written again, so there are no block copies."""
 
     def __init__(self, rs, device: str = "cuda", acts=None):
         from .sched import Scheduler
@@ -375,7 +378,10 @@ class ServeRun:
 
     def _arrive(self) -> None:
         i = self.next_arrival
-        self.sched.add(int(self.rs.prompts[i]), int(self.rs.new_tokens[i]))
+        if self.rs.tokens is not None:
+            self.sched.add_tokens(self.rs.tokens[i], int(self.rs.new_tokens[i]))
+        else:
+            self.sched.add(int(self.rs.prompts[i]), int(self.rs.new_tokens[i]))
         self.next_arrival += 1
 
     def done(self) -> bool:

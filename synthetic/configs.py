@@ -451,6 +451,7 @@ class RequestStream:
     lookahead: int
     max_skips: int
     num_layers: int = 1
+    tokens: Optional[list] = None   # per request, its prompt's token ids (for the prefix cache)
 
     def acts(self, s: int, rows: int) -> tuple:
         """(new_k, new_v, q) of step ``s`` with ``rows`` packed rows (a leading
@@ -463,17 +464,31 @@ class RequestStream:
 def config6(seed: int = 47006, num_requests: int = 256, min_prompt: int = 32, max_prompt: int = 512,
             new_tokens: int = 64, num_blocks: int = 1152, max_batch_tokens: int = 4096, max_seqs: int = 64,
             lookahead: int = 4, max_skips: int = 8, arrive_per_step: int = 0, num_layers: int = 1,
-            kv_dtype: str = "f16") -> RequestStream:
+            kv_dtype: str = "f16", system_prompts: int = 0, min_system: int = 64,
+            max_system: int = 256) -> RequestStream:
     """Continuous batching under churn, GPT-2-small-shaped (12/12 heads, d64):
     ``num_requests`` requests with prompts U[32,512] each generating 64
     tokens (every request of the engine page's workload generates 64), over
     a 1152-block pool (the 32-request batch of workload 2), at most 4096 rows
     and 64 sequences per step.  ``arrive_per_step`` = 0 queues every request
-    at once; k > 0 queues k per step."""
+    at once; k > 0 queues k per step.  ``system_prompts`` = k > 0 gives every
+    request token ids: one of k shared system prompts (U[64,256] tokens) then
+    its own U[min_prompt, max_prompt] tokens, ids uniform over GPT-2's 50257,
+    so the prefix cache can serve the shared parts."""
     hq = hkv = 12
     d = 64
     rng = np.random.default_rng([seed, S_META])
     prompts = rng.integers(min_prompt, max_prompt + 1, num_requests).astype(np.int64)
+    tokens = None
+    if system_prompts > 0:
+        trng = np.random.default_rng([seed, S_META, 1])
+        systems = [trng.integers(0, 50257, int(trng.integers(min_system, max_system + 1))).astype(np.int32)
+                   for _ in range(system_prompts)]
+        pick = trng.integers(0, system_prompts, num_requests)
+        tokens = [np.concatenate([systems[int(pick[i])],
+                                  trng.integers(0, 50257, int(prompts[i])).astype(np.int32)])
+                  for i in range(num_requests)]
+        prompts = np.asarray([len(t) for t in tokens], np.int64)
     arrivals = (np.zeros(num_requests, np.int64) if arrive_per_step <= 0
                 else np.arange(num_requests, dtype=np.int64) // int(arrive_per_step))
     return RequestStream(
@@ -481,5 +496,5 @@ def config6(seed: int = 47006, num_requests: int = 256, min_prompt: int = 32, ma
         block_size=BLOCK_SIZE, kv_dtype=kv_dtype, scale=1.0 / math.sqrt(d), num_blocks=num_blocks,
         arrivals=arrivals, prompts=prompts, new_tokens=np.full(num_requests, new_tokens, np.int64),
         max_batch_tokens=max_batch_tokens, max_seqs=max_seqs, lookahead=lookahead, max_skips=max_skips,
-        num_layers=num_layers,
+        num_layers=num_layers, tokens=tokens,
     )
