@@ -521,7 +521,7 @@ def main(argv=None) -> int:
     ap.add_argument("--summarize-counters", nargs=3, metavar=("PMC_CSV", "OUT_MD", "COMMAND"),
                     help="write per-dispatch SQ/GRBM counter averages of --summary-kernel (semicolon-separated "
                          "prefixes) from a rocprofv3 --pmc run; no GPU is used")
-    ap.add_argument("--summary-kernel", default="void pa::decode_kernel<128, 4, false",
+    ap.add_argument("--summary-kernel", default="void pa::decode_kernel<128, 4, 0,",
                     help="kernel-name prefix the summaries rate")
     ap.add_argument("--summary-title", default="")
     ap.add_argument("--pmc-commands", nargs="*", default=[])

@@ -87,6 +87,14 @@ __device__ __forceinline__ float scale_at(const half_t* base, int64_t idx) {
   const uint16_t bits = (idx & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
   return (float)__builtin_bit_cast(half_t, bits);
 }
+// The aligned dword holding scale `idx`; `half_of` picks the scale out of it.
+// Split so that a load can be issued well before its value is first used.
+__device__ __forceinline__ uint32_t scale_word(const half_t* base, int64_t idx) {
+  return ((const uint32_t*)base)[idx >> 1];
+}
+__device__ __forceinline__ float half_of(uint32_t w, int hi) {
+  return (float)__builtin_bit_cast(half_t, (uint16_t)(hi ? w >> 16 : w & 0xffffu));
+}
 
 // ============================================================ vector path ===
 #ifndef PA_DECODE_NW
@@ -173,8 +181,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 
   const int bend = (kend + kBlockSize - 1) / kBlockSize;
   int b = kbeg / kBlockSize + wave;
-  auto load_tile = [&](int blk, Dw<ND>* kd, Dw<ND>* vd, int& ph) {
-    ph = clamp_block(tbl[blk], a.num_blocks);
+  // Physical block of a logical one (0 past the range, which is never loaded).
+  // The entry is read one iteration before its tile's loads are issued, so
+  // the scalar round trip overlaps the current block's work.
+  // (The raw entry is kept; the range check happens when it is used.)
+  auto table_at = [&](int blk) { return blk < bend ? tbl[blk] : 0; };
+  // Issue the loads of one tile (and, for int8, the words holding its two
+  // scales, read here rather than when the tile is processed for the same
+  // reason: `kq`/`vq` are those words, `qhi` which half is the scale).
+  auto load_tile = [&](int entry, Dw<ND>* kd, Dw<ND>* vd, uint32_t& kq, uint32_t& vq, int& qhi) {
+    const int ph = clamp_block(entry, a.num_blocks);
     const int64_t off = ((int64_t)ph * a.blk_tiles + h) * TILE;
     const uint32_t* kt = (const uint32_t*)((const char*)a.kc + off);
     const uint32_t* vt2 = (const uint32_t*)((const char*)a.vc + off);
@@ -182,14 +198,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     for (int i = 0; i < NL; ++i) kd[i] = load_dw<ND>(kt + (i * 64 + lane) * ND);
 #pragma unroll
     for (int i = 0; i < NL; ++i) vd[i] = load_dw<ND>(vt2 + (i * 64 + lane) * ND);
+    if constexpr (I8) {
+      const int64_t sidx = (int64_t)ph * a.blk_tiles + h;
+      kq = scale_word(a.ks, sidx);
+      vq = scale_word(a.vs, sidx);
+      qhi = (int)(sidx & 1);
+    }
   };
   // One block of this wave: scores, softmax bookkeeping, P.V.  `kr`/`vr` hold
-  // the block's K and V tile rows of this lane.
-  auto process = [&](Dw<ND>* kr, Dw<ND>* vr, const int phys, const int blk) {
+  // the block's K and V tile rows of this lane, `kq`/`vq` its int8 scales.
+  auto process = [&](Dw<ND>* kr, Dw<ND>* vr, const uint32_t kq, const uint32_t vq, const int qhi, const int blk) {
     float ksc = a.scale_log2, vsc = 1.f;
     if constexpr (I8) {
-      ksc *= scale_at(a.ks, (int64_t)phys * a.blk_tiles + h);
-      vsc = scale_at(a.vs, (int64_t)phys * a.blk_tiles + h);
+      ksc *= half_of(kq, qhi);
+      vsc = half_of(vq, qhi);
     }
     const int tok0 = blk * kBlockSize + grp;
     // wave-uniform: the last block of the range, or the block the window starts in
@@ -317,33 +339,43 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   if constexpr (PINGPONG) {
     // two tile buffers used in turn (no register copies between iterations)
     Dw<ND> ka[NL], va[NL], kb[NL], vb[NL];
-    int pha = 0, phb = 0;
-    if (b < bend) load_tile(b, ka, va, pha);
+    uint32_t kqa = 0, vqa = 0, kqb = 0, vqb = 0;
+    int qha = 0, qhb = 0;
+    int pn = table_at(b + NW);
+    if (b < bend) load_tile(table_at(b), ka, va, kqa, vqa, qha);
     while (b < bend) {
-      if (b + NW < bend) load_tile(b + NW, kb, vb, phb);
-      process(ka, va, pha, b);
+      if (b + NW < bend) load_tile(pn, kb, vb, kqb, vqb, qhb);
+      pn = table_at(b + 2 * NW);
+      process(ka, va, kqa, vqa, qha, b);
       b += NW;
       if (b >= bend) break;
-      if (b + NW < bend) load_tile(b + NW, ka, va, pha);
-      process(kb, vb, phb, b);
+      if (b + NW < bend) load_tile(pn, ka, va, kqa, vqa, qha);
+      pn = table_at(b + 2 * NW);
+      process(kb, vb, kqb, vqb, qhb, b);
       b += NW;
     }
   } else {
     // one loop body; the prefetched tile moves into the current one
     Dw<ND> kc[NL], vc[NL];
-    int phc = 0;
-    if (b < bend) load_tile(b, kc, vc, phc);
+    uint32_t kqc = 0, vqc = 0;
+    int qhc = 0;
+    int pn = table_at(b + NW);
+    if (b < bend) load_tile(table_at(b), kc, vc, kqc, vqc, qhc);
     while (b < bend) {
       Dw<ND> kn[NL], vn[NL];
-      int phn = 0;
-      if (b + NW < bend) load_tile(b + NW, kn, vn, phn);
-      process(kc, vc, phc, b);
+      uint32_t kqn = 0, vqn = 0;
+      int qhn = 0;
+      if (b + NW < bend) load_tile(pn, kn, vn, kqn, vqn, qhn);
+      pn = table_at(b + 2 * NW);
+      process(kc, vc, kqc, vqc, qhc, b);
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         kc[i] = kn[i];
         vc[i] = vn[i];
       }
-      phc = phn;
+      kqc = kqn;
+      vqc = vqn;
+      qhc = qhn;
       b += NW;
     }
   }

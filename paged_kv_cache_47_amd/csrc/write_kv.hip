@@ -69,6 +69,15 @@ hipError_t launch_write_f16(const pa_cache_desc& d, const void* k, const void* v
 //   code_j = clamp(rint(x_j / scale), -127, 127)   (zero if scale == 0).
 // fp32 division is IEEE (the build does not use fast-math) so the codes match
 // a CPU evaluation of the same formula bit for bit.
+//
+// Two exact shortcuts keep the per-token cost low:
+// * max|x_j| over the earlier rows is |scale| * max|code_j| (products of an
+//   fp16 scale and a 7-bit code are exact in fp32), so the wave tracks the
+//   largest code instead of re-reading every row;
+// * when the new scale equals the old one (positive and finite) and every
+//   earlier code is within +-127, requantising leaves every earlier code as
+//   it is: code_j * scale is exact and dividing it by the same scale gives
+//   code_j back exactly.  Only the new row is then quantised.
 template <int D>
 __device__ void replay_run_i8(const half_t* __restrict__ src, const int32_t s, const int t, const int n,
                               const int h, const int hkv, const int blk_tiles, int8_t* __restrict__ cache,
@@ -82,35 +91,56 @@ __device__ void replay_run_i8(const half_t* __restrict__ src, const int32_t s, c
 
   float c[kBlockSize][EPL];
   float sc = (float)scales[sidx];
+  float cm = 0.f;   // largest |code| of the rows before the current one (whole wave)
 #pragma unroll
   for (int j = 0; j < kBlockSize; ++j)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) c[j][e] = (j < o0) ? (float)tile[j * D + lane * EPL + e] : 0.f;
+    for (int e = 0; e < EPL; ++e) {
+      c[j][e] = (j < o0) ? (float)tile[j * D + lane * EPL + e] : 0.f;
+      cm = fmaxf(cm, fabsf(c[j][e]));
+    }
+  cm = wave_max(cm);
 
   for (int r = 0; r < n; ++r) {
     const int o = o0 + r;
     const half_t* row = src + ((int64_t)(t + r) * hkv + h) * D + lane * EPL;
-    float x[kBlockSize][EPL];
-    float amax = 0.f;
+    float xo[EPL];
+    float xm = 0.f;
 #pragma unroll
-    for (int j = 0; j < kBlockSize; ++j)
+    for (int e = 0; e < EPL; ++e) {
+      xo[e] = (float)row[e];
+      xm = fmaxf(xm, fabsf(xo[e]));
+    }
+    xm = wave_max(xm);
+    const float amax = fmaxf(cm * fabsf(sc), xm);
+    const float sn = (float)(half_t)(amax / 127.0f);
+    // wave-uniform: every value above is
+    const bool keep = sn == sc && sn > 0.f && sn <= 65504.f && cm <= 127.f;
+    float lm = cm;
+    if (!keep) {
+      lm = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float xv = (j < o) ? c[j][e] * sc : ((j == o) ? (float)row[e] : 0.f);
-        x[j][e] = xv;
-        amax = fmaxf(amax, fabsf(xv));
-      }
-    amax = wave_max(amax);
-    sc = (float)(half_t)(amax / 127.0f);
+      for (int j = 0; j < kBlockSize; ++j)
 #pragma unroll
-    for (int j = 0; j < kBlockSize; ++j)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        if (j <= o) {
-          float qv = (sc == 0.f) ? 0.f : __builtin_rintf(x[j][e] / sc);
-          c[j][e] = fminf(127.f, fmaxf(-127.f, qv));
+        for (int e = 0; e < EPL; ++e) {
+          if (j < o) {
+            const float qv = (sn == 0.f) ? 0.f : __builtin_rintf((c[j][e] * sc) / sn);
+            c[j][e] = fminf(127.f, fmaxf(-127.f, qv));
+            lm = fmaxf(lm, fabsf(c[j][e]));
+          }
         }
-      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float qv = (sn == 0.f) ? 0.f : __builtin_rintf(xo[e] / sn);
+      const float q = fminf(127.f, fmaxf(-127.f, qv));
+      lm = fmaxf(lm, fabsf(q));
+#pragma unroll
+      for (int j = 0; j < kBlockSize; ++j)
+        if (j == o) c[j][e] = q;
+    }
+    cm = wave_max(lm);
+    sc = sn;
   }
   const int olast = o0 + n - 1;
 #pragma unroll

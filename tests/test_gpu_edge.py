@@ -149,6 +149,57 @@ def test_int8_values_near_the_fp16_limit():
         assert np.all(err <= np.maximum(5e-2, 1e-2 * np.abs(ref))), (opts, float((err / np.maximum(np.abs(ref), 1)).max()))
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_int8_write_from_crafted_block_states(d):
+    # Appends to blocks whose earlier codes and scale are set by hand, against the oracle's
+    # per-token replay from the same state: a scale the new rows leave unchanged (only the new
+    # rows are quantised), a largest code below 127 (the scale moves), a stray -128 code, zero,
+    # negative and negative-zero scales, and a run that keeps the scale for some tokens only
+    from paged_kv_cache_47_amd import pa
+    rng = np.random.default_rng(41 + d)
+    nb, hkv, bs = 7, 2, 16
+    K = rng.integers(-127, 128, (nb, hkv, bs, d)).astype(np.int8)
+    V = rng.integers(-127, 128, (nb, hkv, bs, d)).astype(np.int8)
+    K[:, :, 0, 0] = 127
+    V[:, :, 0, 1] = -127
+    KS = np.full((nb, hkv), 0.02, np.float16)
+    VS = np.full((nb, hkv), 0.03, np.float16)
+    K[1] = np.clip(K[1], -100, 100)                    # largest code 100: the scale moves
+    V[1] = np.clip(V[1], -100, 100)
+    K[2, :, 1, 5] = -128                                # a code outside the written range
+    V[2, :, 2, 7] = -128
+    KS[3], VS[3] = 0, 0                                 # zero scale over nonzero codes
+    KS[4], VS[4] = -0.02, -0.03                         # negative scales
+    KS[5], VS[5] = np.float16(-0.0), np.float16(-0.0)
+    # (block, first offset, tokens); blocks 0 and 6 get rows within the old range, block 6 then larger ones
+    runs = [(0, 5, 3), (1, 8, 2), (2, 4, 1), (3, 6, 1), (4, 3, 2), (5, 2, 1), (6, 1, 6)]
+    slots, nk, nv = [], [], []
+    for b, o0, n in runs:
+        for i in range(n):
+            slots.append(b * bs + o0 + i)
+            big = b == 6 and i >= 3
+            nk.append((rng.standard_normal((hkv, d)) * (3.0 if big else 0.4)).clip(-2.5, 2.5) if not big
+                      else rng.standard_normal((hkv, d)) * 3.0)
+            nv.append((rng.standard_normal((hkv, d)) * 0.4).clip(-3.5, 3.5))
+    nk = np.asarray(nk).astype(np.float16)
+    nv = np.asarray(nv).astype(np.float16)
+    nk[9] = 0                                           # block 5: a zero row gives a zero scale
+    nv[9] = 0
+    slots = np.asarray(slots, np.int32)
+    dev = [torch.from_numpy(a.copy()).cuda() for a in (K, V, KS, VS)]
+    pa.pa_write_kv(torch.from_numpy(nk).cuda(), torch.from_numpy(nv).cuda(), torch.from_numpy(slots).cuda(),
+                   dev[0], dev[1], dev[2], dev[3])
+    eK, eV, eKS, eVS = okv.write_i8(K, V, KS, VS, nk, nv, slots, bs)
+    torch.cuda.synchronize()
+    gK, gV, gKS, gVS = (t.cpu().numpy() for t in dev)
+    assert np.array_equal(gK, eK) and np.array_equal(gV, eV)
+    assert np.array_equal(gKS.view(np.uint16), eKS.view(np.uint16))
+    assert np.array_equal(gVS.view(np.uint16), eVS.view(np.uint16))
+    # the cases are what they claim to be
+    assert eKS[0, 0] == KS[0, 0] and eKS[1, 0] != KS[1, 0] and eK[2, 0, 1, 5] == -127
+    assert eKS[4, 0] == -KS[4, 0] and eKS[5, 0] == 0 and eKS[6, 0] != KS[6, 0]
+
+
 def test_write_skips_negative_and_out_of_range_slots():
     from paged_kv_cache_47_amd import pa
     rng = np.random.default_rng(13)
