@@ -452,6 +452,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.part = P.part > 0 ? P.part : INT32_MAX / 2;
   a.window = P.window;
   a.scale_log2 = scale * kLog2e;
+  a.scale_count = (int64_t)desc->num_blocks * a.blk_tiles - tile0;
 
   auto mark = [&](hipEvent_t ev) { return ev == nullptr || hipEventRecord(ev, stream) == hipSuccess; };
   if (P.n_vunit > 0) {

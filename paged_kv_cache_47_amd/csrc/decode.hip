@@ -80,17 +80,16 @@ __device__ __forceinline__ void v_token_pairs(const Dw<N>& r0, const Dw<N>& r1, 
 constexpr float kRescaleF16 = 8.0f;
 constexpr float kRescaleI8 = 6.5f;
 
-// fp16 scale at a wave-uniform index, read as the aligned dword that holds it
-// (a scalar load; 16-bit loads would go through the vector memory path).
-__device__ __forceinline__ float scale_at(const half_t* base, int64_t idx) {
-  const uint32_t w = ((const uint32_t*)base)[idx >> 1];
-  const uint16_t bits = (idx & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu);
-  return (float)__builtin_bit_cast(half_t, bits);
+// fp16 scales are read with 16-bit buffer loads: any alignment, and the
+// descriptor's range check keeps every read inside the array.  The loads of a
+// tile's two scales are issued before its K and V loads (vector loads return
+// in order), so waiting for the scales never waits for the tile behind them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scale_rsrc(const half_t* base, int64_t count) {
+  const int64_t bytes = count > 0 ? 2 * count : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(bytes < INT32_MAX ? bytes : INT32_MAX), 0x00020000);
 }
-// The aligned dword holding scale `idx`; `half_of` picks the scale out of it.
-// Split so that a load can be issued well before its value is first used.
-__device__ __forceinline__ uint32_t scale_word(const half_t* base, int64_t idx) {
-  return ((const uint32_t*)base)[idx >> 1];
+__device__ __forceinline__ uint32_t scale_bits(__amdgpu_buffer_rsrc_t rs, int64_t idx) {
+  return __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(idx * 2), 0, 0);
 }
 __device__ __forceinline__ float half_of(uint32_t w, int hi) {
   return (float)__builtin_bit_cast(half_t, (uint16_t)(hi ? w >> 16 : w & 0xffffu));
@@ -181,16 +180,24 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 
   const int bend = (kend + kBlockSize - 1) / kBlockSize;
   int b = kbeg / kBlockSize + wave;
+  const __amdgpu_buffer_rsrc_t ks_rs = scale_rsrc(a.ks, I8 ? a.scale_count : 0);
+  const __amdgpu_buffer_rsrc_t vs_rs = scale_rsrc(a.vs, I8 ? a.scale_count : 0);
   // Physical block of a logical one (0 past the range, which is never loaded).
   // The entry is read one iteration before its tile's loads are issued, so
   // the scalar round trip overlaps the current block's work.
   // (The raw entry is kept; the range check happens when it is used.)
   auto table_at = [&](int blk) { return blk < bend ? tbl[blk] : 0; };
-  // Issue the loads of one tile (and, for int8, the words holding its two
-  // scales, read here rather than when the tile is processed for the same
-  // reason: `kq`/`vq` are those words, `qhi` which half is the scale).
+  // Issue the loads of one tile (and, for int8, first its two scales, read
+  // here rather than when the tile is processed for the same reason: `kq`/`vq`
+  // hold them in their low halves; `qhi` is always 0 for these loads).
   auto load_tile = [&](int entry, Dw<ND>* kd, Dw<ND>* vd, uint32_t& kq, uint32_t& vq, int& qhi) {
     const int ph = clamp_block(entry, a.num_blocks);
+    if constexpr (I8) {
+      const int64_t sidx = (int64_t)ph * a.blk_tiles + h;
+      kq = scale_bits(ks_rs, sidx);
+      vq = scale_bits(vs_rs, sidx);
+      qhi = 0;
+    }
     const int64_t off = ((int64_t)ph * a.blk_tiles + h) * TILE;
     const uint32_t* kt = (const uint32_t*)((const char*)a.kc + off);
     const uint32_t* vt2 = (const uint32_t*)((const char*)a.vc + off);
@@ -198,12 +205,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     for (int i = 0; i < NL; ++i) kd[i] = load_dw<ND>(kt + (i * 64 + lane) * ND);
 #pragma unroll
     for (int i = 0; i < NL; ++i) vd[i] = load_dw<ND>(vt2 + (i * 64 + lane) * ND);
-    if constexpr (I8) {
-      const int64_t sidx = (int64_t)ph * a.blk_tiles + h;
-      kq = scale_word(a.ks, sidx);
-      vq = scale_word(a.vs, sidx);
-      qhi = (int)(sidx & 1);
-    }
   };
   // One block of this wave: scores, softmax bookkeeping, P.V.  `kr`/`vr` hold
   // the block's K and V tile rows of this lane, `kq`/`vq` its int8 scales.

@@ -80,6 +80,7 @@ struct AttnArgs {
   int32_t part;        // keys per partition (a multiple of 16)
   int32_t window;      // sliding window in keys; 0 = none
   float scale_log2;    // scale * log2(e)
+  int64_t scale_count; // int8: scales from ks (or vs) to the end of its array (bounds of the scale reads)
 };
 
 // First key a query at position `pos` sees (0 without a window).

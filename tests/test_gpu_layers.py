@@ -64,6 +64,18 @@ def test_layers_mixed_batch(dt, layers):
     _check_layers(_run(w), OracleSide(w), 0, SPLITS + ({"mfma_min_rows": 1}, {"mfma_min_rows": 2 ** 31 - 1}))
 
 
+def test_int8_scales_at_odd_tile_offsets():
+    # one KV head and three layers: a block's scales sit at 3 * block + layer, so the layer-1 scales
+    # start 2 bytes into a 32-bit word, and with an odd block count and every block in use the
+    # layer-2 scale of the last block is the array's last half, at a 4-byte boundary
+    lens = [40, 1, 17, 300, 33, 129, 64, 20]
+    qls = [1, 1, 1, 20, 1, 3, 1, 1]
+    w = synthetic.custom(620, lens, qls, 4, 1, 64, "i8", extra_blocks=0, num_layers=3)
+    assert w.num_blocks % 2 == 1
+    _check_layers(_run(w), OracleSide(w), 0, ({"partition_tokens": 16}, {"mfma_min_rows": 2 ** 31 - 1},
+                                              {"mfma_min_rows": 1}))
+
+
 def test_layers_gpt2_shape_prefill_then_decode():
     w = synthetic.config2(num_seqs=5, min_prompt=20, max_prompt=130, decode_steps=4, num_layers=4)
     run, ora = _run(w), OracleSide(w)
