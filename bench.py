@@ -504,8 +504,9 @@ def main(argv=None) -> int:
     ap.add_argument("--layers", type=int, default=1,
                     help="workload 2 only: layers per block (GPT-2 small has 12); a step writes and attends "
                          "every layer over one set of metadata")
-    ap.add_argument("--kv-dtype", default="f16", choices=("f16", "bf16"),
-                    help="workloads 2 and 3: the pool type (bf16 pools take and return bf16 activations)")
+    ap.add_argument("--kv-dtype", default="f16", choices=("f16", "bf16", "i8"),
+                    help="workloads 2, 3 and 6: the pool type (bf16 pools take and return bf16 activations; "
+                         "i8, workload 6 only: int8 codes with per-block-per-head fp16 scales, fp16 activations)")
     ap.add_argument("--system-prompts", type=int, default=0,
                     help="workload 6: requests start with one of this many shared system prompts, served from "
                          "the prefix cache")
@@ -568,6 +569,9 @@ def main(argv=None) -> int:
         return 2
     if args.kv_dtype != "f16" and args.workload not in (2, 3, 6):
         print("--kv-dtype applies to workloads 2, 3 and 6 only", file=sys.stderr)
+        return 2
+    if args.kv_dtype == "i8" and args.workload != 6:
+        print("--kv-dtype i8 applies to workload 6 (workload 5 is the int8 kernel workload)", file=sys.stderr)
         return 2
     if args.workload == 4 and args.no_share:
         w = synthetic.config4(share=False)

@@ -365,8 +365,13 @@ class ServeRun:
         self.act_dtype = torch.bfloat16 if rs.kv_dtype == "bf16" else torch.float16
         lead = () if rs.num_layers == 1 else (rs.num_layers,)
         shape = (rs.num_blocks, *lead, rs.num_kv_heads, rs.block_size, rs.head_dim)
-        self.k_cache = torch.zeros(shape, dtype=self.act_dtype, device=self.device)
-        self.v_cache = torch.zeros(shape, dtype=self.act_dtype, device=self.device)
+        pool_dtype = torch.int8 if rs.kv_dtype == "i8" else self.act_dtype
+        self.k_cache = torch.zeros(shape, dtype=pool_dtype, device=self.device)
+        self.v_cache = torch.zeros(shape, dtype=pool_dtype, device=self.device)
+        self.k_scale = self.v_scale = None
+        if rs.kv_dtype == "i8":   # one fp16 scale per (block, layer, KV head)
+            self.k_scale = torch.zeros(shape[:-2], dtype=torch.float16, device=self.device)
+            self.v_scale = torch.zeros(shape[:-2], dtype=torch.float16, device=self.device)
         self.acts = acts          # None: draw each step's activations; else a callable (step, rows) -> tensors
         self._pinned = [None, None]
         self._copied = [None, None]
@@ -436,7 +441,8 @@ class ServeRun:
         outs = []
         for layer in range(rs.num_layers):
             lk, lv, lq = (nk, nv, q) if rs.num_layers == 1 else (nk[layer], nv[layer], q[layer])
-            pa.pa_write_kv(lk, lv, sm, self.k_cache, self.v_cache, layer=layer)
+            pa.pa_write_kv(lk, lv, sm, self.k_cache, self.v_cache, self.k_scale, self.v_scale, layer=layer)
             outs.append(pa.pa_attend(lq, self.k_cache, self.v_cache, bt, sl, ql, hl, hq, rs.scale,
-                                     workspace=self._ws, layer=layer, reuse_plan=layer > 0))
+                                     workspace=self._ws, k_scale=self.k_scale, v_scale=self.v_scale, layer=layer,
+                                     reuse_plan=layer > 0))
         return st, outs
