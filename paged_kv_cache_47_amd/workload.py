@@ -100,7 +100,10 @@ class DeviceRun:
         for a in flat:
             host[off:off + a.size] = a
             off += a.size
-        dev = torch.empty(n, dtype=torch.int32, device=self.device)
+        # one device buffer for every step: this copy is ordered after the previous step's kernels
+        if self._meta is None or self._meta.numel() < n:
+            self._meta = torch.empty(2 * n, dtype=torch.int32, device=self.device)
+        dev = self._meta[:n]
         dev.copy_(self._pinned[t][:n], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()
@@ -377,7 +380,19 @@ class ServeRun:
         self._copied = [None, None]
         self._turn = 0
         self._ws = None
+        self._meta = None         # device int32 buffer of the step's metadata, reused every step
         self.width = 0
+        # Per-step calls go straight to the library: the pools, their descriptors, the options and
+        # the stream are fixed for the run and checked once here; the step's own arguments are
+        # produced by the scheduler.  The steps run on the stream current at construction.
+        self._lib = pa.load_library()
+        self._descs = [pa.cache_desc(self.k_cache, layer) for layer in range(rs.num_layers)]
+        self._dptr = [ctypes.pointer(d) for d in self._descs]
+        self._opts = [pa._opts(reuse_plan=layer > 0) for layer in range(rs.num_layers)]
+        self._optr = [ctypes.pointer(o) for o in self._opts]
+        self._stream = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+        self._pools = tuple(None if t is None else t.data_ptr()
+                            for t in (self.k_cache, self.v_cache, self.k_scale, self.v_scale))
         for _ in range(int(np.sum(rs.arrivals <= 0))):
             self._arrive()
 
@@ -405,7 +420,10 @@ class ServeRun:
         for a in flat:
             host[off:off + a.size] = a
             off += a.size
-        dev = torch.empty(n, dtype=torch.int32, device=self.device)
+        # one device buffer for every step: this copy is ordered after the previous step's kernels
+        if self._meta is None or self._meta.numel() < n:
+            self._meta = torch.empty(2 * n, dtype=torch.int32, device=self.device)
+        dev = self._meta[:n]
         dev.copy_(self._pinned[t][:n], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()
@@ -434,15 +452,34 @@ class ServeRun:
             nk, nv, q = (torch.from_numpy(np.ascontiguousarray(a)).to(self.device).to(self.act_dtype)
                          for a in rs.acts(s, T))
         sm, bt, sl, ql = self._upload([st.slot_mapping, st.block_tables, st.seq_lens, st.q_lens])
-        hl, hq = st.seq_lens.copy(), st.q_lens.copy()
-        need = pa.pa_attend_workspace_bytes(self.k_cache, rs.num_q_heads, hl, hq)
+        hl, hq = np.ascontiguousarray(st.seq_lens, np.int32), np.ascontiguousarray(st.q_lens, np.int32)
+        S = len(hl)
+        ha, qa = hl.ctypes.data, hq.ctypes.data
+        lib, kc, vc, ks, vs = self._lib, *self._pools
+        need = lib.pa_attend_workspace_bytes(self._dptr[0], rs.num_q_heads, S, ha, qa, self._optr[0])
+        if need == 0:
+            raise pa.PagedAttentionError("pa_attend_workspace_bytes: invalid arguments")
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(2 * need, dtype=torch.uint8, device=self.device)
         outs = []
         for layer in range(rs.num_layers):
             lk, lv, lq = (nk, nv, q) if rs.num_layers == 1 else (nk[layer], nv[layer], q[layer])
-            pa.pa_write_kv(lk, lv, sm, self.k_cache, self.v_cache, self.k_scale, self.v_scale, layer=layer)
-            outs.append(pa.pa_attend(lq, self.k_cache, self.v_cache, bt, sl, ql, hl, hq, rs.scale,
-                                     workspace=self._ws, k_scale=self.k_scale, v_scale=self.v_scale, layer=layer,
-                                     reuse_plan=layer > 0))
+            # the library trusts these sizes: check them (and the type and layout) every step
+            if (tuple(lk.shape) != (T, rs.num_kv_heads, rs.head_dim) or lv.shape != lk.shape
+                    or tuple(lq.shape) != (T, rs.num_q_heads, rs.head_dim)):
+                raise ValueError(f"step {s}: activations must be [{T}, heads, {rs.head_dim}]")
+            if not (lk.dtype == lv.dtype == lq.dtype == self.act_dtype and lk.is_cuda and lv.is_cuda and lq.is_cuda
+                    and lk.is_contiguous() and lv.is_contiguous() and lq.is_contiguous()):
+                raise ValueError(f"step {s}: activations must be contiguous device {self.act_dtype} tensors")
+            out = torch.empty_like(lq)
+            r = lib.pa_write_kv(self._dptr[layer], lk.data_ptr(), lv.data_ptr(), sm.data_ptr(), T, kc, vc, ks, vs,
+                                self._stream)
+            if r == 0:
+                r = lib.pa_attend(self._dptr[layer], lq.data_ptr(), rs.num_q_heads, kc, vc, ks, vs, bt.data_ptr(),
+                                  bt.shape[1], sl.data_ptr(), ql.data_ptr(), S, ha, qa, ctypes.c_float(rs.scale),
+                                  out.data_ptr(), self._ws.data_ptr(), self._ws.numel(), self._optr[layer],
+                                  self._stream)
+            if r != 0:
+                pa._check(r, f"serve step {s} layer {layer}")
+            outs.append(out)
         return st, outs
