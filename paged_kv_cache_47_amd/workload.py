@@ -100,10 +100,7 @@ class DeviceRun:
         for a in flat:
             host[off:off + a.size] = a
             off += a.size
-        # one device buffer for every step: this copy is ordered after the previous step's kernels
-        if self._meta is None or self._meta.numel() < n:
-            self._meta = torch.empty(2 * n, dtype=torch.int32, device=self.device)
-        dev = self._meta[:n]
+        dev = torch.empty(n, dtype=torch.int32, device=self.device)
         dev.copy_(self._pinned[t][:n], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()
