@@ -35,7 +35,8 @@
  *   design": symmetric, no zero point, one scale per block per head).
  * - Supported shapes: block_size 16, head_dim 64 or 128, num_q_heads a
  *   multiple of num_kv_heads with a group size of 1, 2, 4 or 8,
- *   num_blocks * block_size < 2^31.  Anything else returns
+ *   num_blocks * block_size < 2^31, and for int8 pools scale arrays of
+ *   less than 2^31 bytes (pa_attend).  Anything else returns
  *   PA_ERR_UNSUPPORTED (or PA_ERR_SHAPE for inconsistent sizes).
  * - Device-side integer data (slots, block ids, lengths) are preconditions.
  *   Kernels never read or write outside the pools for out-of-range values:

@@ -396,6 +396,10 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   if (P.total_q == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !q_lens || !out || !workspace) return PA_ERR_NULL;
   if (desc->kv_dtype == PA_KV_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  // the decode kernel's scale reads are range-checked against a 31-bit byte count
+  if (desc->kv_dtype == PA_KV_I8 &&
+      (int64_t)desc->num_blocks * std::max(desc->num_layers, 1) * desc->num_kv_heads * 2 > INT32_MAX)
+    return PA_ERR_UNSUPPORTED;
   if (max_blocks_per_seq == 0) return PA_ERR_SHAPE;
   if (!(scale > 0.f) || scale > 3.0e38f) return PA_ERR_SHAPE;   // positive and finite
   if (workspace_bytes < P.bytes) return PA_ERR_WORKSPACE;

@@ -88,12 +88,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scale_rsrc(const half_t* base,
   const int64_t bytes = count > 0 ? 2 * count : 0;
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(bytes < INT32_MAX ? bytes : INT32_MAX), 0x00020000);
 }
-__device__ __forceinline__ uint32_t scale_bits(__amdgpu_buffer_rsrc_t rs, int64_t idx) {
+__device__ __forceinline__ uint16_t scale_bits(__amdgpu_buffer_rsrc_t rs, int64_t idx) {
   return __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(idx * 2), 0, 0);
 }
-__device__ __forceinline__ float half_of(uint32_t w, int hi) {
-  return (float)__builtin_bit_cast(half_t, (uint16_t)(hi ? w >> 16 : w & 0xffffu));
-}
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)__builtin_bit_cast(half_t, b); }
 
 // ============================================================ vector path ===
 #ifndef PA_DECODE_NW
@@ -187,16 +185,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   // the scalar round trip overlaps the current block's work.
   // (The raw entry is kept; the range check happens when it is used.)
   auto table_at = [&](int blk) { return blk < bend ? tbl[blk] : 0; };
-  // Issue the loads of one tile (and, for int8, first its two scales, read
-  // here rather than when the tile is processed for the same reason: `kq`/`vq`
-  // hold them in their low halves; `qhi` is always 0 for these loads).
-  auto load_tile = [&](int entry, Dw<ND>* kd, Dw<ND>* vd, uint32_t& kq, uint32_t& vq, int& qhi) {
+  // Issue the loads of one tile (for int8, first its two scales `kq`/`vq`,
+  // fetched with the tile rather than when it is processed so that their
+  // latency overlaps the current block's work too).
+  auto load_tile = [&](int entry, Dw<ND>* kd, Dw<ND>* vd, uint16_t& kq, uint16_t& vq) {
     const int ph = clamp_block(entry, a.num_blocks);
     if constexpr (I8) {
       const int64_t sidx = (int64_t)ph * a.blk_tiles + h;
       kq = scale_bits(ks_rs, sidx);
       vq = scale_bits(vs_rs, sidx);
-      qhi = 0;
     }
     const int64_t off = ((int64_t)ph * a.blk_tiles + h) * TILE;
     const uint32_t* kt = (const uint32_t*)((const char*)a.kc + off);
@@ -208,11 +205,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   };
   // One block of this wave: scores, softmax bookkeeping, P.V.  `kr`/`vr` hold
   // the block's K and V tile rows of this lane, `kq`/`vq` its int8 scales.
-  auto process = [&](Dw<ND>* kr, Dw<ND>* vr, const uint32_t kq, const uint32_t vq, const int qhi, const int blk) {
+  auto process = [&](Dw<ND>* kr, Dw<ND>* vr, const uint16_t kq, const uint16_t vq, const int blk) {
     float ksc = a.scale_log2, vsc = 1.f;
     if constexpr (I8) {
-      ksc *= half_of(kq, qhi);
-      vsc = half_of(vq, qhi);
+      ksc *= half_bits_to_float(kq);
+      vsc = half_bits_to_float(vq);
     }
     const int tok0 = blk * kBlockSize + grp;
     // wave-uniform: the last block of the range, or the block the window starts in
@@ -340,35 +337,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   if constexpr (PINGPONG) {
     // two tile buffers used in turn (no register copies between iterations)
     Dw<ND> ka[NL], va[NL], kb[NL], vb[NL];
-    uint32_t kqa = 0, vqa = 0, kqb = 0, vqb = 0;
-    int qha = 0, qhb = 0;
+    uint16_t kqa = 0, vqa = 0, kqb = 0, vqb = 0;
     int pn = table_at(b + NW);
-    if (b < bend) load_tile(table_at(b), ka, va, kqa, vqa, qha);
+    if (b < bend) load_tile(table_at(b), ka, va, kqa, vqa);
     while (b < bend) {
-      if (b + NW < bend) load_tile(pn, kb, vb, kqb, vqb, qhb);
+      if (b + NW < bend) load_tile(pn, kb, vb, kqb, vqb);
       pn = table_at(b + 2 * NW);
-      process(ka, va, kqa, vqa, qha, b);
+      process(ka, va, kqa, vqa, b);
       b += NW;
       if (b >= bend) break;
-      if (b + NW < bend) load_tile(pn, ka, va, kqa, vqa, qha);
+      if (b + NW < bend) load_tile(pn, ka, va, kqa, vqa);
       pn = table_at(b + 2 * NW);
-      process(kb, vb, kqb, vqb, qhb, b);
+      process(kb, vb, kqb, vqb, b);
       b += NW;
     }
   } else {
     // one loop body; the prefetched tile moves into the current one
     Dw<ND> kc[NL], vc[NL];
-    uint32_t kqc = 0, vqc = 0;
-    int qhc = 0;
+    uint16_t kqc = 0, vqc = 0;
     int pn = table_at(b + NW);
-    if (b < bend) load_tile(table_at(b), kc, vc, kqc, vqc, qhc);
+    if (b < bend) load_tile(table_at(b), kc, vc, kqc, vqc);
     while (b < bend) {
       Dw<ND> kn[NL], vn[NL];
-      uint32_t kqn = 0, vqn = 0;
-      int qhn = 0;
-      if (b + NW < bend) load_tile(pn, kn, vn, kqn, vqn, qhn);
+      uint16_t kqn = 0, vqn = 0;
+      if (b + NW < bend) load_tile(pn, kn, vn, kqn, vqn);
       pn = table_at(b + 2 * NW);
-      process(kc, vc, kqc, vqc, qhc, b);
+      process(kc, vc, kqc, vqc, b);
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         kc[i] = kn[i];
@@ -376,7 +370,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       }
       kqc = kqn;
       vqc = vqn;
-      qhc = qhn;
       b += NW;
     }
   }
