@@ -123,9 +123,11 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v,
 
 /*
  * Dispatch options of pa_attend (NULL = defaults; zero-initialise unused fields).
- *   partition_tokens  keys per split-K partition of the vector path:
- *                     0 = chosen from the batch, > 0 = this many (a multiple
- *                     of 16), < 0 = never split.
+ *   partition_tokens  largest split-K partition of the vector path, in
+ *                     keys: a row of n keys is split into ceil(n / p) equal
+ *                     partitions (rounded up to 16 keys; the last one takes
+ *                     what remains).  0 = p chosen from the batch, > 0 = p
+ *                     (a multiple of 16), < 0 = never split.
  *   mfma_min_rows     a sequence whose q_len * group rows reach this count
  *                     runs on the MFMA path, otherwise on the vector path:
  *                     0 = default (16), 1 = every sequence on MFMA,

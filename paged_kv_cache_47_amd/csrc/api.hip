@@ -182,7 +182,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         for (int p = 0; p < parts; ++p) {
           if (u + p < a.cap_vunit) {
             a.vunit[u + p] = make_int2(fits ? k : -1, p);
-            const int ck = a.part > 0 ? min(a.part, keys - p * a.part) : keys;
+            const int sz = parts > 1 ? (((keys + parts - 1) / parts + 15) & ~15) : keys;
+            const int ck = min(sz, keys - p * sz);
             a.vcost[u + p] = fits ? min(ck / 64, kCostBuckets - 1) : 0;
           }
         }
@@ -245,7 +246,8 @@ static pa_status check_heads(const pa_cache_desc* d, int32_t hq) {
   return PA_OK;
 }
 
-// Keys per split-K partition when the caller leaves it to the library: aim
+// Largest split-K partition when the caller leaves it to the library (a row
+// is then split into equal parts of at most this many keys): aim
 // for about 16 workgroups per compute unit over the whole vector path, but
 // give every partition at least 768 KB of K and V (1536 keys of fp16 at head
 // dim 128): below that the partial outputs and the merge kernel cost more

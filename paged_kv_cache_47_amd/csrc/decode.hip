@@ -147,8 +147,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   const SeqInfo si = a.seqs[vt.seq];
   const int nvis = si.kv_len - si.q_len + vt.t + 1;
   const int klo = window_lo(nvis - 1, a.window);        // first visible key
-  const int kbeg = (klo & ~(kBlockSize - 1)) + un.y * a.part;
-  const int kend = min(nvis, kbeg + a.part);
+  const int k0 = klo & ~(kBlockSize - 1);
+  // a split row's units are equal (rounded up to 16 keys), not full partitions and a remainder
+  const int sz = vt.parts > 1 ? (((nvis - k0 + vt.parts - 1) / vt.parts + 15) & ~15) : a.part;
+  const int kbeg = k0 + un.y * sz;
+  const int kend = min(nvis, kbeg + sz);
   const int grp = lane / LPT, sub = lane % LPT;
   const int64_t row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
   const int32_t* tbl = a.block_tables + (int64_t)vt.seq * a.max_blocks;

@@ -77,7 +77,7 @@ struct AttnArgs {
   int32_t hq, hkv;
   int32_t blk_tiles;   // (layer, KV head) tiles per physical block: num_layers * hkv;
                        // kc/vc/ks/vs point at the addressed layer's first tile of block 0
-  int32_t part;        // keys per partition (a multiple of 16)
+  int32_t part;        // largest partition in keys (a multiple of 16); a split row's units are equal
   int32_t window;      // sliding window in keys; 0 = none
   float scale_log2;    // scale * log2(e)
   int64_t scale_count; // int8: scales from ks (or vs) to the end of its array (bounds of the scale reads)
