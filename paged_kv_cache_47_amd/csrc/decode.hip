@@ -128,14 +128,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   constexpr int NL = kBlockSize / TPL; // loads per (block, head) tile
   constexpr int E2 = E / 2;            // fp16 pairs per lane per row
   constexpr int64_t TILE = (int64_t)kBlockSize * D * EB;
-#ifndef PA_DECODE_PINGPONG_I8
-#define PA_DECODE_PINGPONG_I8 0
-#endif
-  // two alternating tile buffers for fp16; int8 keeps one loop body (fewer live registers)
-  constexpr bool PINGPONG = I8 ? (PA_DECODE_PINGPONG_I8 != 0) : true;
+  // Two alternating tile buffers (no register copies between iterations).
+  // int8 with G >= 4 gets them by keeping Q in LDS (below); with smaller
+  // groups one loop body keeps more waves resident.
+  constexpr bool PINGPONG = I8 ? G >= 4 : true;
 
   __shared__ float sm[NW][G], sl[NW][G];
   __shared__ float so[NW][G][D];
+  // int8, G >= 4: the G query rows sit in LDS and each row's slice is read
+  // just before its dot products, so 8 rather than G * 8 registers of Q are
+  // live at a time, which makes room for the second tile buffer
+  constexpr bool QLDS = I8 && G >= 4;
+  __shared__ __attribute__((aligned(16))) act_t qs[QLDS ? G * D : 8];
 
   const int u = a.vorder[blockIdx.x], h = blockIdx.y;   // units go out longest first
   const int lane = threadIdx.x & 63;
@@ -156,17 +160,24 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   const int64_t row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
   const int32_t* tbl = a.block_tables + (int64_t)vt.seq * a.max_blocks;
 
-  act2_t qh[G][E2];
+  act2_t qh[QLDS ? 1 : G][E2];
+  if constexpr (QLDS) {
+    // the workgroup's G rows are contiguous: G * D / 8 chunks of 16 bytes
+    const uint4* qp = (const uint4*)((const act_t*)a.q + row0 * D);
+    for (int c = threadIdx.x; c < G * D / 8; c += NW * 64) ((uint4*)qs)[c] = qp[c];
+    __syncthreads();
+  } else {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4* qp = (const uint4*)((const act_t*)a.q + (row0 + g) * D + sub * E);
+    for (int g = 0; g < G; ++g) {
+      const uint4* qp = (const uint4*)((const act_t*)a.q + (row0 + g) * D + sub * E);
 #pragma unroll
-    for (int c = 0; c < E / 8; ++c) {
-      const uint4 w = qp[c];
-      qh[g][4 * c + 0] = __builtin_bit_cast(act2_t, w.x);
-      qh[g][4 * c + 1] = __builtin_bit_cast(act2_t, w.y);
-      qh[g][4 * c + 2] = __builtin_bit_cast(act2_t, w.z);
-      qh[g][4 * c + 3] = __builtin_bit_cast(act2_t, w.w);
+      for (int c = 0; c < E / 8; ++c) {
+        const uint4 w = qp[c];
+        qh[g][4 * c + 0] = __builtin_bit_cast(act2_t, w.x);
+        qh[g][4 * c + 1] = __builtin_bit_cast(act2_t, w.y);
+        qh[g][4 * c + 2] = __builtin_bit_cast(act2_t, w.z);
+        qh[g][4 * c + 3] = __builtin_bit_cast(act2_t, w.w);
+      }
     }
   }
 
@@ -228,6 +239,36 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     // raw dot products q.k of this lane group's NL tokens for the G rows;
     // the score (base 2) is d * ksc, ksc > 0
     float s[NL][G];
+    if constexpr (QLDS) {
+      // both token rows' K as fp16 first, then one query row at a time from LDS
+      act2_t kh[NL][E2];
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int c = 0; c < ND; ++c) {
+          kh[i][2 * c] = sdwa_pair<0, 1>(kr[i].v[c], kr[i].v[c]);
+          kh[i][2 * c + 1] = sdwa_pair<2, 3>(kr[i].v[c], kr[i].v[c]);
+        }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        act2_t qg[E2];
+#pragma unroll
+        for (int c = 0; c < E2 / 4; ++c) {
+          const uint4 w = ((const uint4*)(qs + g * D + sub * E))[c];
+          qg[4 * c + 0] = __builtin_bit_cast(act2_t, w.x);
+          qg[4 * c + 1] = __builtin_bit_cast(act2_t, w.y);
+          qg[4 * c + 2] = __builtin_bit_cast(act2_t, w.z);
+          qg[4 * c + 3] = __builtin_bit_cast(act2_t, w.w);
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          float d = dot2_first(qg[0], kh[i][0]);
+#pragma unroll
+          for (int c = 1; c < E2; ++c) d = dot2(qg[c], kh[i][c], d);
+          s[i][g] = d;
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       act2_t kh[E2];
@@ -254,6 +295,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
         for (int c = 1; c < E2; ++c) d = dot2(qh[g][c], kh[c], d);
         s[i][g] = d;
       }
+    }
     }
     group_sum_all<LPT, NL * G>(&s[0][0]);
     if (edge) {
