@@ -79,13 +79,14 @@ def test_null_and_empty_arguments():
     assert lib.pa_copy_blocks(ctypes.byref(d), None, None, None, None, None, 0, None) == 0
 
 
-def _attend(desc, hq, L, Q, maxb, ws_bytes=1 << 20, ptrs=True, opts=None):
+def _attend(desc, hq, L, Q, maxb, ws_bytes=1 << 20, ptrs=True, opts=None, scales=False):
     lib = pa.load_library()
     L = np.asarray(L, np.int32)
     Q = np.asarray(Q, np.int32)
     f = ctypes.c_void_p(256) if ptrs else None
+    s = f if scales else None
     o = opts or pa.AttendOpts()
-    return lib.pa_attend(ctypes.byref(desc), f, hq, f, f, None, None, f, maxb, f, f, len(L), pa._hp(L), pa._hp(Q),
+    return lib.pa_attend(ctypes.byref(desc), f, hq, f, f, s, s, f, maxb, f, f, len(L), pa._hp(L), pa._hp(Q),
                          ctypes.c_float(0.1), f, f, ws_bytes, ctypes.byref(o), None)
 
 
@@ -132,3 +133,12 @@ def test_layer_validation():
     assert _attend(d, 4, [5], [1], 4) == 2
     d.num_layers, d.layer = 3, 2
     assert _attend(d, 4, [5], [1], 4, ws_bytes=8) == 5   # a valid layer: validation reaches the workspace check
+
+
+def test_int8_scale_arrays_of_2gib_or_more_are_unsupported():
+    # the decode kernel's scale reads are range-checked with a 31-bit byte count
+    d = _desc(kv_dtype=1, num_blocks=1 << 26)          # 2 KV heads
+    d.num_layers, d.layer = 4, 0                       # 2^26 * 4 * 2 scales of 2 bytes: 1 GiB
+    assert _attend(d, 4, [5], [1], 4, ws_bytes=8, scales=True) == 5   # allowed: reaches the workspace check
+    d.num_layers = 8                                   # 2 GiB
+    assert _attend(d, 4, [5], [1], 4, ws_bytes=8, scales=True) == 4
