@@ -49,7 +49,7 @@ def draw_case(i: int):
 
 
 def test_draws_cover_the_features():   # host only: what the seeded draws contain
-    cases = [draw_case(i) for i in range(32)]
+    cases = [draw_case(i) for i in range(48)]
     assert {c["dt"] for c in cases} == {"f16", "i8", "bf16"}
     assert {c["d"] for c in cases} == {64, 128}
     assert {c["layers"] for c in cases} == {1, 2}
@@ -59,7 +59,7 @@ def test_draws_cover_the_features():   # host only: what the seeded draws contai
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("i", range(32))
+@pytest.mark.parametrize("i", range(48))
 def test_random_case(i):
     from paged_kv_cache_47_amd.workload import DeviceRun
     c = draw_case(i)
@@ -106,7 +106,7 @@ def draw_int8_writes(i: int):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(12))
 def test_random_int8_writes(i):
     from oracle import kv_write as okv
     from paged_kv_cache_47_amd import pa
