@@ -246,8 +246,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       for (int i = 0; i < NL; ++i)
 #pragma unroll
         for (int c = 0; c < ND; ++c) {
-          kh[i][2 * c] = sdwa_pair<0, 1>(kr[i].v[c], kr[i].v[c]);
-          kh[i][2 * c + 1] = sdwa_pair<2, 3>(kr[i].v[c], kr[i].v[c]);
+          if constexpr (PA_I8_SDWA) {
+            kh[i][2 * c] = sdwa_pair<0, 1>(kr[i].v[c], kr[i].v[c]);
+            kh[i][2 * c + 1] = sdwa_pair<2, 3>(kr[i].v[c], kr[i].v[c]);
+          } else {
+            i8x4_to_h2(kr[i].v[c], kh[i][2 * c], kh[i][2 * c + 1]);
+          }
         }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
