@@ -381,7 +381,8 @@ class ServeRun:
         self.width = 0
         # Per-step calls go straight to the library: the pools, their descriptors, the options and
         # the stream are fixed for the run and checked once here; the step's own arguments are
-        # produced by the scheduler.  The steps run on the stream current at construction.
+        # produced by the scheduler.  The library calls go to the stream current at construction,
+        # the metadata copy to the current stream: step with that same stream current.
         self._lib = pa.load_library()
         self._descs = [pa.cache_desc(self.k_cache, layer) for layer in range(rs.num_layers)]
         self._dptr = [ctypes.pointer(d) for d in self._descs]
