@@ -16,6 +16,7 @@ namespace pa {
 // with seq = -1, so kernels never read an unwritten entry even if the host and
 // device lengths disagree.
 constexpr int kPlanThreads = 1024;
+constexpr int64_t kDirectMaxGroups = 1024;   // decode workgroups of a batch that may skip the plan (about one round)
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 // Exclusive scan of four counters over the workgroup (one sequence per
@@ -430,7 +431,13 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   pl.cap_vtok = (int32_t)P.n_vtok;
   pl.cap_vunit = (int32_t)P.n_vunit;
   pl.cap_munit = (int32_t)P.n_munit;
-  if (!(opts && opts->reuse_plan) && launch_plan(pl, stream) != hipSuccess) return PA_ERR_HIP;
+  // A batch of one query row per sequence that no row splits and that fits in
+  // about one round of workgroups needs no plan: the decode kernel reads each
+  // sequence's length itself (longest-first ordering matters only when the
+  // workgroups queue), which saves the plan kernel's launch and latency.
+  bool direct = P.n_munit == 0 && P.max_parts <= 1 && (int64_t)num_seqs * desc->num_kv_heads <= kDirectMaxGroups;
+  for (int32_t i = 0; direct && i < num_seqs; ++i) direct = h_q_lens[i] == 1;
+  if (!direct && !(opts && opts->reuse_plan) && launch_plan(pl, stream) != hipSuccess) return PA_ERR_HIP;
 
   // the addressed layer's first tile of block 0; tiles of one block are num_layers * hkv apart
   const int64_t tile0 = (int64_t)desc->layer * desc->num_kv_heads;
@@ -459,6 +466,10 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.window = P.window;
   a.scale_log2 = scale * kLog2e;
   a.scale_count = (int64_t)desc->num_blocks * a.blk_tiles - tile0;
+  a.seq_lens = seq_lens;
+  a.q_lens = q_lens;
+  a.max_kv = pl.max_kv;
+  a.direct = direct ? 1 : 0;
 
   auto mark = [&](hipEvent_t ev) { return ev == nullptr || hipEventRecord(ev, stream) == hipSuccess; };
   if (P.n_vunit > 0) {

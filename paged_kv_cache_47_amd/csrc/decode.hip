@@ -141,24 +141,44 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   constexpr bool QLDS = I8 && G >= 4;
   __shared__ __attribute__((aligned(16))) act_t qs[QLDS ? G * D : 8];
 
-  const int u = a.vorder[blockIdx.x], h = blockIdx.y;   // units go out longest first
+  const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps block indices scalar
-  const int2 un = a.vunit[u];
-  if (un.x < 0) return;
-  const VTok vt = a.vtok[un.x];
-  if (vt.seq < 0) return;
-  const SeqInfo si = a.seqs[vt.seq];
-  const int nvis = si.kv_len - si.q_len + vt.t + 1;
+  // this workgroup's unit: its sequence, query row, partition and the row's partition count
+  int u, seq, t, part_idx, parts, kv_len, q_len, q_start;
+  if (a.direct) {
+    u = seq = blockIdx.x;
+    t = part_idx = 0;
+    parts = 1;
+    kv_len = min(max(a.seq_lens[seq], 0), a.max_kv);
+    q_len = min(max(a.q_lens[seq], 0), kv_len);
+    if (q_len == 0) return;
+    q_start = seq;
+  } else {
+    u = a.vorder[blockIdx.x];   // units go out longest first
+    const int2 un = a.vunit[u];
+    if (un.x < 0) return;
+    const VTok vt = a.vtok[un.x];
+    if (vt.seq < 0) return;
+    const SeqInfo si = a.seqs[vt.seq];
+    seq = vt.seq;
+    t = vt.t;
+    part_idx = un.y;
+    parts = vt.parts;
+    kv_len = si.kv_len;
+    q_len = si.q_len;
+    q_start = si.q_start;
+  }
+  const int nvis = kv_len - q_len + t + 1;
   const int klo = window_lo(nvis - 1, a.window);        // first visible key
   const int k0 = klo & ~(kBlockSize - 1);
   // a split row's units are equal (rounded up to 16 keys), not full partitions and a remainder
-  const int sz = vt.parts > 1 ? (((nvis - k0 + vt.parts - 1) / vt.parts + 15) & ~15) : a.part;
-  const int kbeg = k0 + un.y * sz;
+  const int sz = parts > 1 ? (((nvis - k0 + parts - 1) / parts + 15) & ~15) : a.part;
+  const int kbeg = k0 + part_idx * sz;
   const int kend = min(nvis, kbeg + sz);
   const int grp = lane / LPT, sub = lane % LPT;
-  const int64_t row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
-  const int32_t* tbl = a.block_tables + (int64_t)vt.seq * a.max_blocks;
+  const int64_t row0 = (int64_t)(q_start + t) * a.hq + (int64_t)h * G;
+  const int32_t* tbl = a.block_tables + (int64_t)seq * a.max_blocks;
 
   act2_t qh[QLDS ? 1 : G][E2];
   if constexpr (QLDS) {
@@ -450,7 +470,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
-  const bool split = vt.parts > 1;
+  const bool split = parts > 1;
   for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
     const int g = idx / D, d = idx % D;
     float M = sm[0][g];

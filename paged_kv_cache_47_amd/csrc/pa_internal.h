@@ -81,6 +81,13 @@ struct AttnArgs {
   int32_t window;      // sliding window in keys; 0 = none
   float scale_log2;    // scale * log2(e)
   int64_t scale_count; // int8: scales from ks (or vs) to the end of its array (bounds of the scale reads)
+  // direct != 0: a batch of one query row per sequence, unsplit, that needs no
+  // plan: decode workgroup x serves sequence x, reading its length here
+  // (clamped as the plan kernel clamps it: to max_kv, and the rows to the keys)
+  const int32_t* seq_lens;
+  const int32_t* q_lens;
+  int32_t max_kv;
+  int32_t direct;
 };
 
 // First key a query at position `pos` sees (0 without a window).
