@@ -200,6 +200,22 @@ def test_int8_write_from_crafted_block_states(d):
     assert eKS[4, 0] == -KS[4, 0] and eKS[5, 0] == 0 and eKS[6, 0] != KS[6, 0]
 
 
+@pytest.mark.parametrize("n,q2", [(100, False), (160, False), (100, True)])
+def test_pure_decode_batches_with_and_without_the_plan(n, q2):
+    # one query row per sequence, no split, at most 1024 (sequence, KV head) pairs: the decode kernel
+    # reads the lengths itself (100 x 8); more pairs (160 x 8) or a row with two queries go through the
+    # plan kernel; all against the oracle, with a window on half of them
+    rng = np.random.default_rng(5 + n + q2)
+    lens = [int(x) for x in rng.integers(1, 600, n)]
+    qls = [1] * n
+    if q2:
+        qls[7] = 2
+        lens[7] = max(lens[7], 2)
+    for window in (0, 100):
+        w = synthetic.custom(70 + n, lens, qls, 32, 8, 128, window=window)
+        _check_step(_run(w), OracleSide(w), 0, ({}, {"partition_tokens": -1}))
+
+
 def test_write_skips_negative_and_out_of_range_slots():
     from paged_kv_cache_47_amd import pa
     rng = np.random.default_rng(13)
