@@ -179,6 +179,40 @@ size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
                                  const int32_t* h_q_lens, const pa_attend_opts* opts);
 
 /*
+ * pa_attend_plan_info - how pa_attend would run this batch, decided from the
+ * host lengths alone (no device work; same arguments as
+ * pa_attend_workspace_bytes).  For callers that size buffers once for an
+ * upper bound on the lengths: with partition_tokens fixed to the value
+ * returned here, the workspace a batch needs never grows when its lengths
+ * shrink.
+ *   partition_tokens  the largest split-K partition in keys (0: rows are never
+ *                     split); rows longer than it are split
+ *   vector_rows       query rows on the vector path
+ *   vector_units      (row, partition) units of the vector path, per KV head
+ *   max_parts         the most partitions of one row (> 1: the merge kernel runs)
+ *   mfma_tiles        row tiles of the MFMA path, per KV head
+ *   plan_free         1 when the batch needs no plan kernel: one query row per
+ *                     sequence, no row split, no MFMA rows, and at most 1024
+ *                     (sequence, KV head) pairs, so each decode workgroup
+ *                     reads its sequence's length itself
+ *   workspace_bytes   what pa_attend_workspace_bytes returns
+ * Returns the status pa_attend would return for these host arguments.
+ */
+typedef struct {
+  int32_t partition_tokens;
+  int32_t vector_rows;
+  int32_t vector_units;
+  int32_t max_parts;
+  int32_t mfma_tiles;
+  int32_t plan_free;
+  size_t workspace_bytes;
+} pa_attend_info;
+
+pa_status pa_attend_plan_info(const pa_cache_desc* desc, int32_t num_q_heads, int32_t num_seqs,
+                              const int32_t* h_seq_lens, const int32_t* h_q_lens,
+                              const pa_attend_opts* opts, pa_attend_info* info);
+
+/*
  * pa_attend - scaled dot-product attention of a packed batch over paged K/V,
  * walking each sequence's block table ([pytorch] "Compute reference attention
  * without hiding the layout" for what is computed; "Map the PyTorch design to

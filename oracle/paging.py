@@ -45,12 +45,6 @@ def translate(pos: int, block_size: int) -> tuple:
     return pos // block_size, pos % block_size
 
 
-def slot_of(table, pos: int, block_size: int) -> int:
-    """Slot number of position ``pos`` of a sequence with block table ``table``."""
-    lb, off = translate(pos, block_size)
-    return int(table[lb]) * block_size + off
-
-
 class RefPool:
     """Free stack, allocated set and refcounts over ``num_blocks`` ids."""
 

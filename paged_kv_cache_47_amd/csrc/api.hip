@@ -222,6 +222,7 @@ struct HostPlan {
   int32_t part = 0, min_rows = 16, total_q = 0, window = 0;
   int64_t n_vtok = 0, n_vunit = 0, n_munit = 0;
   int32_t max_parts = 0;
+  bool direct = false;   // the batch skips the plan kernel (see make_plan)
   size_t off_seqs = 0, off_vtok = 0, off_vunit = 0, off_vorder = 0, off_vcost = 0, off_munit = 0, off_munit_tmp = 0,
          off_lse = 0, off_po = 0;
   size_t bytes = 0;
@@ -302,6 +303,12 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
     }
   }
   if (P.n_vunit >= INT32_MAX / 2 || P.n_munit >= INT32_MAX / 2) return PA_ERR_SHAPE;
+  // A batch of one query row per sequence that no row splits and that fits in
+  // about one round of workgroups needs no plan: the decode kernel reads each
+  // sequence's length itself (longest-first ordering matters only when the
+  // workgroups queue), which saves the plan kernel's launch and latency.
+  P.direct = P.n_munit == 0 && P.max_parts <= 1 && (int64_t)num_seqs * d->num_kv_heads <= kDirectMaxGroups;
+  for (int32_t i = 0; P.direct && i < num_seqs; ++i) P.direct = hQ[i] == 1;
   size_t off = 0;
   P.off_seqs = off;
   off = align_up(off + sizeof(SeqInfo) * (size_t)std::max(num_seqs, 1), 256);
@@ -385,6 +392,23 @@ size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
   return P.bytes;
 }
 
+pa_status pa_attend_plan_info(const pa_cache_desc* desc, int32_t num_q_heads, int32_t num_seqs,
+                              const int32_t* h_seq_lens, const int32_t* h_q_lens, const pa_attend_opts* opts,
+                              pa_attend_info* info) {
+  if (info == nullptr) return PA_ERR_NULL;
+  HostPlan P;
+  const pa_status st = make_plan(desc, num_q_heads, num_seqs, h_seq_lens, h_q_lens, INT32_MAX / kBlockSize, opts, P);
+  if (st != PA_OK) return st;
+  info->partition_tokens = P.part;
+  info->vector_rows = (int32_t)P.n_vtok;
+  info->vector_units = (int32_t)P.n_vunit;
+  info->max_parts = P.max_parts;
+  info->mfma_tiles = (int32_t)P.n_munit;
+  info->plan_free = P.direct ? 1 : 0;
+  info->workspace_bytes = P.bytes;
+  return PA_OK;
+}
+
 pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_heads, const void* k_cache,
                     const void* v_cache, const void* k_scale, const void* v_scale, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
@@ -431,12 +455,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   pl.cap_vtok = (int32_t)P.n_vtok;
   pl.cap_vunit = (int32_t)P.n_vunit;
   pl.cap_munit = (int32_t)P.n_munit;
-  // A batch of one query row per sequence that no row splits and that fits in
-  // about one round of workgroups needs no plan: the decode kernel reads each
-  // sequence's length itself (longest-first ordering matters only when the
-  // workgroups queue), which saves the plan kernel's launch and latency.
-  bool direct = P.n_munit == 0 && P.max_parts <= 1 && (int64_t)num_seqs * desc->num_kv_heads <= kDirectMaxGroups;
-  for (int32_t i = 0; direct && i < num_seqs; ++i) direct = h_q_lens[i] == 1;
+  const bool direct = P.direct;
   if (!direct && !(opts && opts->reuse_plan) && launch_plan(pl, stream) != hipSuccess) return PA_ERR_HIP;
 
   // the addressed layer's first tile of block 0; tiles of one block are num_layers * hkv apart

@@ -43,6 +43,13 @@ class AttendOpts(ctypes.Structure):
                 ("window", ctypes.c_int32), ("reuse_plan", ctypes.c_int32)]
 
 
+class AttendInfo(ctypes.Structure):
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("vector_rows", ctypes.c_int32),
+                ("vector_units", ctypes.c_int32), ("max_parts", ctypes.c_int32),
+                ("mfma_tiles", ctypes.c_int32), ("plan_free", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 _lib = None
 
 
@@ -61,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_write_kv.restype = ctypes.c_int
     lib.pa_attend_workspace_bytes.argtypes = [pdesc, i32, i32, vp, vp, popts]
     lib.pa_attend_workspace_bytes.restype = sz
+    lib.pa_attend_plan_info.argtypes = [pdesc, i32, i32, vp, vp, popts, ctypes.POINTER(AttendInfo)]
+    lib.pa_attend_plan_info.restype = ctypes.c_int
     lib.pa_attend.argtypes = [pdesc, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp,
                               ctypes.c_float, vp, vp, sz, popts, vp]
     lib.pa_attend.restype = ctypes.c_int
@@ -206,6 +215,21 @@ def pa_attend_workspace_bytes(k_cache, num_q_heads: int, h_seq_lens, h_q_lens,
     if n == 0:
         raise PagedAttentionError("pa_attend_workspace_bytes: invalid arguments")
     return int(n)
+
+
+def pa_attend_plan_info(k_cache, num_q_heads: int, h_seq_lens, h_q_lens, partition_tokens: int = 0,
+                        mfma_min_rows: int = 0, window: int = 0, layer: int = 0) -> dict:
+    """How ``pa_attend`` would run this batch (decided from the host lengths;
+    no device work): partition, vector rows and units, largest split, MFMA
+    row tiles, whether the plan kernel is skipped, workspace bytes."""
+    lib = load_library()
+    desc = cache_desc(k_cache, layer)
+    hl, hq = _host_i32(h_seq_lens), _host_i32(h_q_lens)
+    opts = _opts(partition_tokens, mfma_min_rows, window=window)
+    info = AttendInfo()
+    _check(lib.pa_attend_plan_info(ctypes.byref(desc), int(num_q_heads), len(hl), _host_addr(hl), _host_addr(hq),
+                                   ctypes.byref(opts), ctypes.byref(info)), "pa_attend_plan_info")
+    return {f: getattr(info, f) for f, _ in AttendInfo._fields_}
 
 
 def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,

@@ -256,6 +256,12 @@ class StaticSteps:
         self.new_v = torch.zeros((L, T, hkv, d), **f16)
         self.q = torch.zeros((L, T, hq, d), **f16)
         self.out = torch.zeros((L, T, hq, d), **f16)
+        # The automatic split size depends on the batch's total keys, so steps with shorter true
+        # lengths could pick a smaller partition and need more split units than the bound; fixing
+        # the partition the bound gets keeps every step's units (and workspace) within it.
+        if self.partition_tokens == 0:
+            info = pa.pa_attend_plan_info(run.k_cache, hq, self.h_len, self.h_ql, window=w.window)
+            self.partition_tokens = info["partition_tokens"] or -1
         need = pa.pa_attend_workspace_bytes(run.k_cache, hq, self.h_len, self.h_ql, self.partition_tokens, 0,
                                             w.window)
         self.ws = torch.empty(need, dtype=torch.uint8, device=run.device)

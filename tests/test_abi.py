@@ -142,3 +142,42 @@ def test_int8_scale_arrays_of_2gib_or_more_are_unsupported():
     assert _attend(d, 4, [5], [1], 4, ws_bytes=8, scales=True) == 5   # allowed: reaches the workspace check
     d.num_layers = 8                                   # 2 GiB
     assert _attend(d, 4, [5], [1], 4, ws_bytes=8, scales=True) == 4
+
+
+def _meta_pool(nb, hkv, d, dtype=None):
+    import torch
+    return torch.empty((nb, hkv, 16, d), dtype=dtype or torch.float16, device="meta")
+
+
+def test_plan_info_plan_free_decision():
+    """The plan kernel is skipped exactly for single-row, unsplit, vector-path
+    batches of at most 1024 (sequence, KV head) pairs."""
+    pool = _meta_pool(64, 8, 128)
+    info = pa.pa_attend_plan_info(pool, 32, [100] * 128, [1] * 128)
+    assert info["plan_free"] == 1 and info["max_parts"] == 1 and info["vector_units"] == 128
+    assert pa.pa_attend_plan_info(pool, 32, [100] * 129, [1] * 129)["plan_free"] == 0   # 1032 pairs
+    two = pa.pa_attend_plan_info(pool, 32, [100] * 4, [1, 1, 2, 1])                    # a two-row sequence
+    assert two["plan_free"] == 0 and two["vector_rows"] == 5
+    split = pa.pa_attend_plan_info(pool, 32, [100, 5000], [1, 1], partition_tokens=1024)
+    assert split["plan_free"] == 0 and split["max_parts"] == 5
+    mfma = pa.pa_attend_plan_info(pool, 32, [100, 50], [1, 4])                          # 16 rows: MFMA
+    assert mfma["plan_free"] == 0 and mfma["mfma_tiles"] == 1 and mfma["vector_rows"] == 1
+    i8 = pa.pa_attend_plan_info(_meta_pool(64, 8, 128, __import__("torch").int8), 64, [3000] * 128, [1] * 128)
+    assert i8["plan_free"] == 1                                                         # group 8, int8
+
+
+def test_fixed_partition_keeps_the_workspace_within_the_bound():
+    """With the partition fixed to the one the upper bound gets, no shorter
+    batch needs more workspace than the bound; the automatic choice alone can
+    (a smaller key total picks a smaller partition)."""
+    pool = _meta_pool(64, 8, 128)
+    S, W = 256, 3200
+    bound = pa.pa_attend_plan_info(pool, 32, [W] * S, [1] * S)
+    part = bound["partition_tokens"]
+    assert part > 0 and bound["workspace_bytes"] > 0
+    mixed = [3100] * 170 + [16] * 86
+    assert pa.pa_attend_workspace_bytes(pool, 32, mixed, [1] * S) > bound["workspace_bytes"]
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        L = rng.integers(1, W + 1, S)
+        assert pa.pa_attend_workspace_bytes(pool, 32, L, [1] * S, partition_tokens=part) <= bound["workspace_bytes"]

@@ -200,11 +200,14 @@ def test_int8_write_from_crafted_block_states(d):
     assert eKS[4, 0] == -KS[4, 0] and eKS[5, 0] == 0 and eKS[6, 0] != KS[6, 0]
 
 
-@pytest.mark.parametrize("n,q2", [(100, False), (160, False), (100, True)])
-def test_pure_decode_batches_with_and_without_the_plan(n, q2):
+@pytest.mark.parametrize("n,q2,hq,dt", [(100, False, 32, "f16"), (128, False, 32, "f16"), (129, False, 32, "f16"),
+                                        (160, False, 32, "f16"), (100, True, 32, "f16"), (128, False, 64, "i8")])
+def test_pure_decode_batches_with_and_without_the_plan(n, q2, hq, dt):
     # one query row per sequence, no split, at most 1024 (sequence, KV head) pairs: the decode kernel
-    # reads the lengths itself (100 x 8); more pairs (160 x 8) or a row with two queries go through the
-    # plan kernel; all against the oracle, with a window on half of them
+    # reads the lengths itself (100 and 128 x 8; int8 group 8 takes the query-rows-in-LDS kernel); more
+    # pairs (129 and 160 x 8) or a row with two queries go through the plan kernel; all against the
+    # oracle, with a window on half of them.  The library's own plan query says which path each took.
+    from paged_kv_cache_47_amd import pa
     rng = np.random.default_rng(5 + n + q2)
     lens = [int(x) for x in rng.integers(1, 600, n)]
     qls = [1] * n
@@ -212,8 +215,12 @@ def test_pure_decode_batches_with_and_without_the_plan(n, q2):
         qls[7] = 2
         lens[7] = max(lens[7], 2)
     for window in (0, 100):
-        w = synthetic.custom(70 + n, lens, qls, 32, 8, 128, window=window)
-        _check_step(_run(w), OracleSide(w), 0, ({}, {"partition_tokens": -1}))
+        w = synthetic.custom(70 + n, lens, qls, hq, 8, 128, dt, window=window)
+        run = _run(w)
+        for opts in ({}, {"partition_tokens": -1}):
+            info = pa.pa_attend_plan_info(run.k_cache, hq, lens, qls, window=window, **opts)
+            assert info["plan_free"] == (n <= 128 and not q2 and info["max_parts"] == 1), (n, q2, opts, info)
+        _check_step(run, OracleSide(w), 0, ({}, {"partition_tokens": -1}))
 
 
 def test_write_skips_negative_and_out_of_range_slots():
