@@ -15,7 +15,7 @@
  * - Every buffer argument is a DEVICE pointer unless its name starts with
  *   h_ (host memory).  The caller owns every buffer, including the attention
  *   workspace; the library allocates no device memory and keeps no global
- *   mutable state.
+ *   mutable state (except the fixed per-GPU scratch of pa_attend_noalloc).
  * - Work is enqueued on `stream` and returns without synchronising.  The
  *   status only covers what the host can check: argument validation and kernel
  *   launch errors.  Arguments are checked before anything is enqueued.
@@ -255,6 +255,35 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
                     const int32_t* h_seq_lens, const int32_t* h_q_lens,
                     float scale, void* out, void* workspace, size_t workspace_bytes,
                     const pa_attend_opts* opts, hipStream_t stream);
+
+/*
+ * pa_attend_noalloc - pa_attend without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments, results and errors are
+ * those of pa_attend; the workspace is a fixed device array of
+ * PA_ATTEND_SCRATCH_BYTES that the library holds per GPU (created with the
+ * library's code object on that device and kept until the process ends; its
+ * address is looked up on the first call on each device, with that device
+ * current).  The call itself allocates nothing.
+ *   - A batch whose pa_attend_workspace_bytes exceeds PA_ATTEND_SCRATCH_BYTES
+ *     returns PA_ERR_WORKSPACE, checked on the host before the GPU is used.
+ *   - Every call on one GPU shares that GPU's array.  Calls that may overlap
+ *     on the device (other streams, other threads) race on it and give wrong
+ *     results; order them on one stream.  opts->reuse_plan = 1 takes the plan
+ *     that the previous pa_attend_noalloc call on the device left there.
+ *   - The device current at the call must be the one `stream` belongs to.
+ * This is the one exception to "the library keeps no global mutable state".
+ */
+#define PA_ATTEND_SCRATCH_BYTES ((size_t)64 << 20)
+
+pa_status pa_attend_noalloc(const pa_cache_desc* desc, const void* q, int32_t num_q_heads,
+                            const void* k_cache, const void* v_cache,
+                            const void* k_scale, const void* v_scale,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
+                            const int32_t* h_seq_lens, const int32_t* h_q_lens,
+                            float scale, void* out, const pa_attend_opts* opts,
+                            hipStream_t stream);
 
 /*
  * pa_copy_blocks - copy whole blocks (every layer, every KV head, every slot,

@@ -1,7 +1,9 @@
 // C ABI of libpa.so: argument validation, workspace layout, dispatch.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstring>
+#include <mutex>
 
 #include "mfma_tile.h"
 
@@ -508,3 +510,57 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------ fixed scratch ----
+// pa_attend_noalloc's workspace: one array per GPU, allocated with the code
+// object when the library is first used on that device and held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it names a stand-in, not device memory): the device address is looked
+// up once per device and kept.
+namespace pa {
+
+static __device__ __align__(256) char scratch[PA_ATTEND_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array.
+static pa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PA_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" pa_status pa_attend_noalloc(const pa_cache_desc* desc, const void* q, int32_t num_q_heads,
+                                       const void* k_cache, const void* v_cache, const void* k_scale,
+                                       const void* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
+                                       const int32_t* h_seq_lens, const int32_t* h_q_lens, float scale, void* out,
+                                       const pa_attend_opts* opts, hipStream_t stream) {
+  // the size check needs only the host arguments: an oversized batch is refused before the GPU is touched
+  HostPlan P;
+  pa_status st = make_plan(desc, num_q_heads, num_seqs, h_seq_lens, h_q_lens,
+                           max_blocks_per_seq >= 0 ? max_blocks_per_seq : 0, opts, P);
+  if (st != PA_OK) return st;
+  if (P.bytes > (size_t)PA_ATTEND_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  if (P.total_q == 0) return PA_OK;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != PA_OK) return st;
+  return pa_attend(desc, q, num_q_heads, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                   seq_lens, q_lens, num_seqs, h_seq_lens, h_q_lens, scale, out, ws, PA_ATTEND_SCRATCH_BYTES, opts,
+                   stream);
+}

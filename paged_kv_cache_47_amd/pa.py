@@ -73,6 +73,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_attend.argtypes = [pdesc, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp,
                               ctypes.c_float, vp, vp, sz, popts, vp]
     lib.pa_attend.restype = ctypes.c_int
+    lib.pa_attend_noalloc.argtypes = [pdesc, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp,
+                                      ctypes.c_float, vp, popts, vp]
+    lib.pa_attend_noalloc.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [pdesc, vp, vp, vp, vp, vp, i32, vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_status_str.argtypes = [ctypes.c_int]
@@ -235,12 +238,13 @@ def pa_attend_plan_info(k_cache, num_q_heads: int, h_seq_lens, h_q_lens, partiti
 def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
                    out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
                    mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
-                   reuse_plan: bool = False) -> PreparedCall:
+                   reuse_plan: bool = False, noalloc: bool = False) -> PreparedCall:
     """``pa_attend`` as a prepared call (arguments as for ``pa_attend``; the
     output tensor is the call's ``keep[0]``).  ``h_seq_lens`` and ``h_q_lens``
     are passed by address: when they are int32 numpy arrays they are used in
     place, so a caller may update them between calls (the device lengths
-    must match them at each call)."""
+    must match them at each call).  ``noalloc``: call ``pa_attend_noalloc``
+    (the library's fixed per-GPU scratch; ``workspace`` must be None)."""
     lib = load_library()
     desc = cache_desc(k_cache, layer)
     _need(q, "q", _act_dtype(desc), 3)
@@ -266,6 +270,14 @@ def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_le
         if out.shape != q.shape:
             raise ValueError("out must match q")
     opts = _opts(partition_tokens, mfma_min_rows, events, window, reuse_plan)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("pa_attend_noalloc takes no workspace")
+        args = (ctypes.byref(desc), _ptr(q), q.shape[1], _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                _ptr(v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(q_lens), S,
+                _host_addr(hl), _host_addr(hq), ctypes.c_float(scale), _ptr(out), ctypes.byref(opts),
+                _stream(stream))
+        return PreparedCall(lib.pa_attend_noalloc, args, "pa_attend_noalloc", (out, desc, opts, hl, hq))
     if workspace is None:
         if reuse_plan:
             raise ValueError("reuse_plan needs the workspace of the call that planned")
@@ -297,6 +309,20 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
     call = prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale, out,
                           workspace, k_scale, v_scale, partition_tokens, mfma_min_rows, events, stream, window,
                           layer, reuse_plan)
+    call()
+    return call.keep[0]
+
+
+def pa_attend_noalloc(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
+                      out=None, k_scale=None, v_scale=None, partition_tokens: int = 0, mfma_min_rows: int = 0,
+                      events=None, stream=None, window: int = 0, layer: int = 0,
+                      reuse_plan: bool = False) -> torch.Tensor:
+    """``pa_attend`` on the library's fixed per-GPU scratch instead of a
+    caller workspace (``pa_attend_noalloc``: the call allocates nothing; batches
+    needing more than its size are refused; calls on one GPU must not overlap)."""
+    call = prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale, out,
+                          None, k_scale, v_scale, partition_tokens, mfma_min_rows, events, stream, window, layer,
+                          reuse_plan, noalloc=True)
     call()
     return call.keep[0]
 

@@ -181,3 +181,24 @@ def test_fixed_partition_keeps_the_workspace_within_the_bound():
     for _ in range(50):
         L = rng.integers(1, W + 1, S)
         assert pa.pa_attend_workspace_bytes(pool, 32, L, [1] * S, partition_tokens=part) <= bound["workspace_bytes"]
+
+
+def test_noalloc_refuses_batches_beyond_its_scratch_on_the_host():
+    """pa_attend_noalloc's fixed scratch holds PA_ATTEND_SCRATCH_BYTES (64 MiB);
+    a batch needing more is refused from the host arguments alone, before
+    any device work (nothing here has a GPU)."""
+    lib = pa.load_library()
+    d = _desc(num_blocks=1 << 16, num_kv_heads=8)
+    S, L = 512, 32768
+    hl = np.full(S, L, np.int32)
+    hq = np.ones(S, np.int32)
+    o = pa.AttendOpts()
+    o.partition_tokens = 64                     # 512 rows x 512 units x 32 heads x 129 floats
+    need = lib.pa_attend_workspace_bytes(ctypes.byref(d), 32, S, pa._hp(hl), pa._hp(hq), ctypes.byref(o))
+    assert need > (64 << 20)
+    fake = ctypes.c_void_p(256)
+    st = lib.pa_attend_noalloc(ctypes.byref(d), fake, 32, fake, fake, None, None, fake, L // 16, fake, fake, S,
+                               pa._hp(hl), pa._hp(hq), ctypes.c_float(0.1), fake, ctypes.byref(o), None)
+    assert st == 5                               # PA_ERR_WORKSPACE
+    assert lib.pa_attend_noalloc(None, fake, 32, fake, fake, None, None, fake, L // 16, fake, fake, S,
+                                 pa._hp(hl), pa._hp(hq), ctypes.c_float(0.1), fake, None, None) == 1
