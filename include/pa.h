@@ -191,10 +191,15 @@ size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
  *   vector_units      (row, partition) units of the vector path, per KV head
  *   max_parts         the most partitions of one row (> 1: the merge kernel runs)
  *   mfma_tiles        row tiles of the MFMA path, per KV head
- *   plan_free         1 when the batch needs no plan kernel: one query row per
- *                     sequence, no row split, no MFMA rows, and at most 1024
- *                     (sequence, KV head) pairs, so each decode workgroup
- *                     reads its sequence's length itself
+ *   plan_free         0 when a plan kernel turns the device lengths into work
+ *                     lists first; 1 for a batch of one query row per
+ *                     sequence, no row split and at most 1024 (sequence, KV
+ *                     head) pairs: decode workgroup x serves sequence x and
+ *                     reads its length itself; 2 for any other batch of one
+ *                     query row per sequence with at most 1024 sequences:
+ *                     every decode workgroup derives the same unit order
+ *                     (largest units first) from the device lengths and
+ *                     takes its own unit
  *   workspace_bytes   what pa_attend_workspace_bytes returns
  * Returns the status pa_attend would return for these host arguments.
  */

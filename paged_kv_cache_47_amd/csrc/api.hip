@@ -61,16 +61,6 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* lds, int4& total) {
   return make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
 }
 
-__host__ __device__ __forceinline__ int parts_for(int nkeys, int part) {
-  return part <= 0 ? 1 : (nkeys + part - 1) / part;
-}
-
-// Keys the vector path walks for the query at position `pos`: from the
-// 16-aligned start of its window (0 without one) to the query itself.
-__host__ __device__ __forceinline__ int vector_keys(int pos, int window) {
-  return pos + 1 - (window_lo(pos, window) & ~(kBlockSize - 1));
-}
-
 // First key the MFMA row tile starting at query position `qfirst` stages:
 // the step-aligned start of that row's window.
 __host__ __device__ __forceinline__ int tile_key0(int qfirst, int window) {
@@ -224,9 +214,10 @@ struct HostPlan {
   int32_t part = 0, min_rows = 16, total_q = 0, window = 0;
   int64_t n_vtok = 0, n_vunit = 0, n_munit = 0;
   int32_t max_parts = 0;
-  bool direct = false;   // the batch skips the plan kernel (see make_plan)
+  bool direct = false;     // one decode workgroup per sequence, no plan kernel (see make_plan)
+  bool selfplan = false;   // decode workgroups find their own units, no plan kernel (see make_plan)
   size_t off_seqs = 0, off_vtok = 0, off_vunit = 0, off_vorder = 0, off_vcost = 0, off_munit = 0, off_munit_tmp = 0,
-         off_lse = 0, off_po = 0;
+         off_lse = 0, off_po = 0, off_row_u0 = 0;
   size_t bytes = 0;
 };
 
@@ -309,8 +300,14 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   // about one round of workgroups needs no plan: the decode kernel reads each
   // sequence's length itself (longest-first ordering matters only when the
   // workgroups queue), which saves the plan kernel's launch and latency.
-  P.direct = P.n_munit == 0 && P.max_parts <= 1 && (int64_t)num_seqs * d->num_kv_heads <= kDirectMaxGroups;
-  for (int32_t i = 0; P.direct && i < num_seqs; ++i) P.direct = hQ[i] == 1;
+  bool one_row_each = P.n_munit == 0 && num_seqs > 0;
+  for (int32_t i = 0; one_row_each && i < num_seqs; ++i) one_row_each = hQ[i] == 1;
+  P.direct = one_row_each && P.max_parts <= 1 && (int64_t)num_seqs * d->num_kv_heads <= kDirectMaxGroups;
+  // Other pure-decode batches of up to kSelfPlanMaxSeqs sequences need no plan
+  // either: every decode workgroup derives the same bucketed unit order from
+  // the device lengths and takes its own unit (a few LDS scans at its start,
+  // beside other workgroups' loads, instead of a serial kernel in front).
+  P.selfplan = PA_SELFPLAN && one_row_each && !P.direct && num_seqs <= kSelfPlanMaxSeqs;
   size_t off = 0;
   P.off_seqs = off;
   off = align_up(off + sizeof(SeqInfo) * (size_t)std::max(num_seqs, 1), 256);
@@ -331,6 +328,8 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   if (split) off = align_up(off + sizeof(float) * (size_t)P.n_vunit * hq, 256);
   P.off_po = off;
   if (split) off = align_up(off + sizeof(float) * (size_t)P.n_vunit * hq * d->head_dim, 256);
+  P.off_row_u0 = off;
+  if (P.selfplan) off = align_up(off + sizeof(int32_t) * (size_t)num_seqs, 256);
   P.bytes = off;
   return PA_OK;
 }
@@ -406,7 +405,7 @@ pa_status pa_attend_plan_info(const pa_cache_desc* desc, int32_t num_q_heads, in
   info->vector_units = (int32_t)P.n_vunit;
   info->max_parts = P.max_parts;
   info->mfma_tiles = (int32_t)P.n_munit;
-  info->plan_free = P.direct ? 1 : 0;
+  info->plan_free = P.direct ? 1 : (P.selfplan ? 2 : 0);
   info->workspace_bytes = P.bytes;
   return PA_OK;
 }
@@ -458,7 +457,8 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   pl.cap_vunit = (int32_t)P.n_vunit;
   pl.cap_munit = (int32_t)P.n_munit;
   const bool direct = P.direct;
-  if (!direct && !(opts && opts->reuse_plan) && launch_plan(pl, stream) != hipSuccess) return PA_ERR_HIP;
+  if (!direct && !P.selfplan && !(opts && opts->reuse_plan) && launch_plan(pl, stream) != hipSuccess)
+    return PA_ERR_HIP;
 
   // the addressed layer's first tile of block 0; tiles of one block are num_layers * hkv apart
   const int64_t tile0 = (int64_t)desc->layer * desc->num_kv_heads;
@@ -491,12 +491,17 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.q_lens = q_lens;
   a.max_kv = pl.max_kv;
   a.direct = direct ? 1 : 0;
+  a.selfplan = P.selfplan ? 1 : 0;
+  a.num_seqs = num_seqs;
+  a.n_units = (int32_t)P.n_vunit;
+  a.row_u0 = P.selfplan ? (int32_t*)(ws + P.off_row_u0) : nullptr;
 
   auto mark = [&](hipEvent_t ev) { return ev == nullptr || hipEventRecord(ev, stream) == hipSuccess; };
   if (P.n_vunit > 0) {
     if (!mark(opts ? opts->vector_begin : nullptr)) return PA_ERR_HIP;
     if (launch_decode(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_vunit, stream) != hipSuccess) return PA_ERR_HIP;
     if (!mark(opts ? opts->vector_end : nullptr)) return PA_ERR_HIP;
+    // one merge workgroup per vector row (self-planned: per sequence, the same count)
     if (P.max_parts > 1 && launch_reduce(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_vtok, stream) != hipSuccess)
       return PA_ERR_HIP;
   }

@@ -93,12 +93,109 @@ __device__ __forceinline__ uint16_t scale_bits(__amdgpu_buffer_rsrc_t rs, int64_
 }
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)__builtin_bit_cast(half_t, b); }
 
+// ===================================================== self-planned units ===
+// Row i of a self-planned batch as every workgroup derives it from the device
+// lengths (clamped as the plan kernel clamps them): the keys its query walks,
+// its equal units and their cost bucket.  No query row: no units.
+struct SPRow {
+  int keys, parts, bucket;
+};
+
+__device__ __forceinline__ SPRow sp_row(const AttnArgs& a, int i) {
+  SPRow r = {0, 0, 0};
+  const int L = min(max(a.seq_lens[i], 0), a.max_kv);
+  if (min(a.q_lens[i], L) < 1) return r;
+  r.keys = vector_keys(L - 1, a.window);
+  r.parts = parts_for(r.keys, a.part);
+  const int sz = r.parts > 1 ? (((r.keys + r.parts - 1) / r.parts + 15) & ~15) : r.keys;
+  r.bucket = min(sz >> 6, kSelfPlanBuckets - 1);
+  return r;
+}
+
+// The x-th unit of the order every workgroup derives alike (cost bucket
+// descending, then sequence, then partition): a count of units per bucket,
+// a scan over the buckets to find x's bucket and its rank there, then a scan
+// over the sequences of that bucket to find the row.  Returns false when x
+// is past the last unit (the device lengths then disagree with the host's).
+struct SPUnit {
+  int seq, part, parts;
+};
+
+template <int NT>
+__device__ bool sp_locate(const AttnArgs& a, int x, SPUnit& out) {
+  static_assert(kSelfPlanBuckets == 64, "one lane per bucket");
+  constexpr int PER = kSelfPlanMaxSeqs / NT;   // sequences per thread, in order
+  __shared__ int cnt[kSelfPlanBuckets];
+  __shared__ int wsum[NT / 64];
+  __shared__ int sel[5];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid < kSelfPlanBuckets) cnt[tid] = 0;
+  if (tid == 0) sel[0] = -1;
+  __syncthreads();
+  SPRow rows[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid * PER + k;
+    rows[k] = i < a.num_seqs ? sp_row(a, i) : SPRow{0, 0, 0};
+    if (rows[k].parts > 0) atomicAdd(&cnt[rows[k].bucket], rows[k].parts);
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int b = kSelfPlanBuckets - 1 - lane;   // lane 0 holds the largest bucket
+    const int c = cnt[b];
+    int inc = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += t;
+    }
+    if (x >= inc - c && x < inc) {
+      sel[0] = b;
+      sel[1] = x - (inc - c);
+    }
+  }
+  __syncthreads();
+  const int B = sel[0], r = sel[1];
+  if (B < 0) return false;
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) mine += rows[k].bucket == B ? rows[k].parts : 0;
+  int inc = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int base = inc - mine;
+  for (int w = 0; w < wv; ++w) base += wsum[w];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int c = rows[k].bucket == B ? rows[k].parts : 0;
+    if (r >= base && r < base + c) {
+      sel[2] = tid * PER + k;
+      sel[3] = r - base;
+      sel[4] = rows[k].parts;
+    }
+    base += c;
+  }
+  __syncthreads();
+  out.seq = sel[2];
+  out.part = sel[3];
+  out.parts = sel[4];
+  return true;
+}
+
 // ============================================================ vector path ===
 #ifndef PA_DECODE_NW
 #define PA_DECODE_NW 4   // waves per workgroup
 #endif
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1   // 1: K/V tile loads carry the nontemporal hint (each tile is read once)
+#endif
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 2   // tiles in flight per wave while one is processed (fp16/bf16, some groups: 1 or 2)
 #endif
 
 template <int N>
@@ -132,6 +229,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   // int8 with G >= 4 gets them by keeping Q in LDS (below); with smaller
   // groups one loop body keeps more waves resident.
   constexpr bool PINGPONG = I8 ? G >= 4 : true;
+  // 16-bit pools whose group fits beside a third buffer (G * D of 256 or 512:
+  // d128 with G 2 or 4, d64 with G 4 or 8) keep two tiles in flight per wave
+  // while a third is processed: fewer waves fit (two per SIMD at d128 G = 4
+  // instead of three) but more bytes are in flight per compute unit.
+  constexpr bool DEPTH2 = !I8 && PA_DECODE_DEPTH == 2 && G * D >= 256 && G * D <= 512;
 
   __shared__ float sm[NW][G], sl[NW][G];
   __shared__ float so[NW][G][D];
@@ -154,6 +256,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     q_len = min(max(a.q_lens[seq], 0), kv_len);
     if (q_len == 0) return;
     q_start = seq;
+  } else if (a.selfplan) {
+    SPUnit su;
+    if (!sp_locate<NW * 64>(a, blockIdx.x, su)) return;
+    u = blockIdx.x;
+    seq = su.seq;
+    t = 0;
+    part_idx = su.part;
+    parts = su.parts;
+    kv_len = min(max(a.seq_lens[seq], 0), a.max_kv);
+    q_len = 1;
+    q_start = seq;   // one query row per sequence: packed row = sequence
+    if (part_idx == 0 && h == 0 && threadIdx.x == 0) a.row_u0[seq] = u;
   } else {
     u = a.vorder[blockIdx.x];   // units go out longest first
     const int2 un = a.vunit[u];
@@ -169,6 +283,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     q_len = si.q_len;
     q_start = si.q_start;
   }
+  // device lengths that split a row the host's lengths did not: no partial buffer to write to
+  if (parts > 1 && a.po == nullptr) return;
   const int nvis = kv_len - q_len + t + 1;
   const int klo = window_lo(nvis - 1, a.window);        // first visible key
   const int k0 = klo & ~(kBlockSize - 1);
@@ -403,7 +519,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   };
 
   // The wave's next block is in flight while the current one is processed.
-  if constexpr (PINGPONG) {
+  if constexpr (DEPTH2) {
+    // three tile buffers used in turn: two tiles in flight while one is processed
+    Dw<ND> ka[NL], va[NL], kb[NL], vb[NL], kc[NL], vc[NL];
+    uint16_t kqa = 0, vqa = 0, kqb = 0, vqb = 0, kqc = 0, vqc = 0;
+    if (b < bend) load_tile(table_at(b), ka, va, kqa, vqa);
+    if (b + NW < bend) load_tile(table_at(b + NW), kb, vb, kqb, vqb);
+    int pn = table_at(b + 2 * NW);
+    while (b < bend) {
+      if (b + 2 * NW < bend) load_tile(pn, kc, vc, kqc, vqc);
+      pn = table_at(b + 3 * NW);
+      process(ka, va, kqa, vqa, b);
+      b += NW;
+      if (b >= bend) break;
+      if (b + 2 * NW < bend) load_tile(pn, ka, va, kqa, vqa);
+      pn = table_at(b + 3 * NW);
+      process(kb, vb, kqb, vqb, b);
+      b += NW;
+      if (b >= bend) break;
+      if (b + 2 * NW < bend) load_tile(pn, kb, vb, kqb, vqb);
+      pn = table_at(b + 3 * NW);
+      process(kc, vc, kqc, vqc, b);
+      b += NW;
+    }
+  } else if constexpr (PINGPONG) {
     // two tile buffers used in turn (no register copies between iterations)
     Dw<ND> ka[NL], va[NL], kb[NL], vb[NL];
     uint16_t kqa = 0, vqa = 0, kqb = 0, vqb = 0;
@@ -497,19 +636,33 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 // base-2 log-sum-exp: out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M).
 template <int D, int G, typename OUT>
 __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
-  const VTok vt = a.vtok[blockIdx.x];
-  if (vt.seq < 0 || vt.parts <= 1) return;
   const int h = blockIdx.y;
-  const SeqInfo si = a.seqs[vt.seq];
-  const int64_t row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
+  int u0, parts;
+  int64_t row0;
+  if (a.selfplan) {
+    // grid x = sequence; its units start where its first unit recorded
+    const SPRow r = sp_row(a, blockIdx.x);
+    if (r.parts <= 1) return;
+    u0 = a.row_u0[blockIdx.x];
+    parts = r.parts;
+    if (u0 < 0 || u0 + parts > a.n_units) return;   // only if device and host lengths disagree
+    row0 = (int64_t)blockIdx.x * a.hq + (int64_t)h * G;
+  } else {
+    const VTok vt = a.vtok[blockIdx.x];
+    if (vt.seq < 0 || vt.parts <= 1) return;
+    const SeqInfo si = a.seqs[vt.seq];
+    u0 = vt.u0;
+    parts = vt.parts;
+    row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
+  }
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int g = idx / D, d = idx % D;
     const int64_t col = (int64_t)h * G + g;
     float M = -__builtin_inff();
-    for (int p = 0; p < vt.parts; ++p) M = fmaxf(M, a.plse[(int64_t)(vt.u0 + p) * a.hq + col]);
+    for (int p = 0; p < parts; ++p) M = fmaxf(M, a.plse[(int64_t)(u0 + p) * a.hq + col]);
     float S = 0.f, O = 0.f;
-    for (int p = 0; p < vt.parts; ++p) {
-      const int64_t pr = (int64_t)(vt.u0 + p) * a.hq + col;
+    for (int p = 0; p < parts; ++p) {
+      const int64_t pr = (int64_t)(u0 + p) * a.hq + col;
       const float wgt = fast_exp2(a.plse[pr] - M);
       S += wgt;
       O = fmaf(wgt, a.po[pr * D + d], O);

@@ -88,12 +88,42 @@ struct AttnArgs {
   const int32_t* q_lens;
   int32_t max_kv;
   int32_t direct;
+  // selfplan != 0: a self-planned decode batch (see kSelfPlanMaxSeqs): decode
+  // workgroup x takes the x-th unit of the bucketed order it derives from
+  // seq_lens / q_lens; the first unit of each row records its index in
+  // row_u0[row] for the merge kernel
+  int32_t selfplan;
+  int32_t num_seqs;
+  int32_t n_units;     // units of the launch (the decode grid's x extent)
+  int32_t* row_u0;     // [num_seqs]
 };
 
 // First key a query at position `pos` sees (0 without a window).
 __host__ __device__ __forceinline__ int window_lo(int pos, int window) {
   return window > 0 ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
 }
+
+// Split-K partitions of a row of `nkeys` keys (part <= 0: never split).
+__host__ __device__ __forceinline__ int parts_for(int nkeys, int part) {
+  return part <= 0 ? 1 : (nkeys + part - 1) / part;
+}
+
+// Keys the vector path walks for the query at position `pos`: from the
+// 16-aligned start of its window (0 without one) to the query itself.
+__host__ __device__ __forceinline__ int vector_keys(int pos, int window) {
+  return pos + 1 - (window_lo(pos, window) & ~(kBlockSize - 1));
+}
+
+// Self-planned decode batches (one query row per sequence, at most
+// kSelfPlanMaxSeqs sequences, no MFMA rows): no plan kernel runs; each decode
+// workgroup finds its own unit.  Units are ordered by cost bucket (the size
+// of the row's equal units in 64-key steps, capped), largest first, then by
+// sequence, then by partition, so a row's units are consecutive.
+constexpr int kSelfPlanMaxSeqs = 1024;
+constexpr int kSelfPlanBuckets = 64;
+#ifndef PA_SELFPLAN
+#define PA_SELFPLAN 1   // 0: such batches go through the plan kernel too
+#endif
 
 struct PlanArgs {
   const int32_t* seq_lens;

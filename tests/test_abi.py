@@ -150,20 +150,26 @@ def _meta_pool(nb, hkv, d, dtype=None):
 
 
 def test_plan_info_plan_free_decision():
-    """The plan kernel is skipped exactly for single-row, unsplit, vector-path
-    batches of at most 1024 (sequence, KV head) pairs."""
+    """No plan kernel for batches of one query row per sequence: one decode
+    workgroup per sequence when no row splits and there are at most 1024
+    (sequence, KV head) pairs (1), self-planned units for the others of up to
+    1024 sequences (2); a plan kernel otherwise (0)."""
     pool = _meta_pool(64, 8, 128)
     info = pa.pa_attend_plan_info(pool, 32, [100] * 128, [1] * 128)
     assert info["plan_free"] == 1 and info["max_parts"] == 1 and info["vector_units"] == 128
-    assert pa.pa_attend_plan_info(pool, 32, [100] * 129, [1] * 129)["plan_free"] == 0   # 1032 pairs
+    assert pa.pa_attend_plan_info(pool, 32, [100] * 129, [1] * 129)["plan_free"] == 2   # 1032 pairs
     two = pa.pa_attend_plan_info(pool, 32, [100] * 4, [1, 1, 2, 1])                    # a two-row sequence
     assert two["plan_free"] == 0 and two["vector_rows"] == 5
     split = pa.pa_attend_plan_info(pool, 32, [100, 5000], [1, 1], partition_tokens=1024)
-    assert split["plan_free"] == 0 and split["max_parts"] == 5
+    assert split["plan_free"] == 2 and split["max_parts"] == 5 and split["vector_units"] == 6
     mfma = pa.pa_attend_plan_info(pool, 32, [100, 50], [1, 4])                          # 16 rows: MFMA
     assert mfma["plan_free"] == 0 and mfma["mfma_tiles"] == 1 and mfma["vector_rows"] == 1
     i8 = pa.pa_attend_plan_info(_meta_pool(64, 8, 128, __import__("torch").int8), 64, [3000] * 128, [1] * 128)
     assert i8["plan_free"] == 1                                                         # group 8, int8
+    assert pa.pa_attend_plan_info(pool, 32, [3000] * 1024, [1] * 1024)["plan_free"] == 2
+    assert pa.pa_attend_plan_info(pool, 32, [3000] * 1025, [1] * 1025)["plan_free"] == 0   # too many sequences
+    zero = pa.pa_attend_plan_info(pool, 32, [3000] * 200 + [5], [1] * 200 + [0])         # a row with no query
+    assert zero["plan_free"] == 0
 
 
 def test_fixed_partition_keeps_the_workspace_within_the_bound():

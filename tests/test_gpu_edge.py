@@ -219,8 +219,30 @@ def test_pure_decode_batches_with_and_without_the_plan(n, q2, hq, dt):
         run = _run(w)
         for opts in ({}, {"partition_tokens": -1}):
             info = pa.pa_attend_plan_info(run.k_cache, hq, lens, qls, window=window, **opts)
-            assert info["plan_free"] == (n <= 128 and not q2 and info["max_parts"] == 1), (n, q2, opts, info)
+            want = 0 if q2 else (1 if (n <= 128 and info["max_parts"] == 1) else 2)
+            assert info["plan_free"] == want, (n, q2, opts, info)
         _check_step(run, OracleSide(w), 0, ({}, {"partition_tokens": -1}))
+
+
+@pytest.mark.parametrize("n,hi,hq,hkv,dt,window", [
+    (256, 6000, 32, 8, "f16", 0), (1024, 400, 32, 8, "f16", 0), (300, 3000, 64, 8, "i8", 0),
+    (200, 5000, 16, 2, "bf16", 700), (97, 9000, 8, 8, "f16", 0), (130, 2000, 4, 4, "i8", 100),
+])
+def test_self_planned_decode_batches(n, hi, hq, hkv, dt, window):
+    # pure-decode batches that split rows or exceed 1024 (sequence, KV head) pairs: no plan kernel,
+    # every decode workgroup derives the bucketed unit order from the device lengths and takes its unit
+    from paged_kv_cache_47_amd import pa
+    rng = np.random.default_rng(900 + n + hi)
+    lens = [int(x) for x in rng.integers(1, hi, n)]
+    lens[n // 2] = hi                                       # the longest row sits mid-batch
+    w = synthetic.custom(800 + n, lens, [1] * n, hq, hkv, 128, dt, window=window)
+    run = _run(w)
+    opts_list = ({}, {"partition_tokens": 16}, {"partition_tokens": 256}, {"partition_tokens": 4096},
+                 {"partition_tokens": -1})
+    for opts in opts_list:
+        info = pa.pa_attend_plan_info(run.k_cache, hq, lens, [1] * n, window=window, **opts)
+        assert info["plan_free"] == (1 if (info["max_parts"] == 1 and n * hkv <= 1024) else 2), (opts, info)
+    _check_step(run, OracleSide(w), 0, opts_list)
 
 
 def test_write_skips_negative_and_out_of_range_slots():
