@@ -3,7 +3,10 @@
     python -m paged_kv_cache_47_amd.build [--debug]
 
 Every source under ``csrc/`` is compiled to an object (in parallel) and
-linked into ``paged_kv_cache_47_amd/libpa.so``: ``.hip`` files (kernels and
+linked into ``paged_kv_cache_47_amd/libpa.so`` (``--debug``: into
+``libpa_debug.so``, built with ``PA_DEBUG=1``: every write, attention and
+copy first checks its device metadata and refuses a call that breaks a
+precondition): ``.hip`` files (kernels and
 the device-side C ABI) with hipcc, ``.cpp`` files (host bookkeeping, no GPU
 code) with the host C++ compiler.  Packed-fp32 instructions are disabled for
 every HIP compile; there is no fast-math (the int8 write relies on IEEE fp32
@@ -23,6 +26,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpa.so")
+LIB_DEBUG = os.path.join(HERE, "libpa_debug.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -71,12 +75,13 @@ def _run(cmd):
 
 def build(debug: bool = False, verbose: bool = False) -> str:
     cc = hipcc()
-    os.makedirs(BUILD, exist_ok=True)
-    extra = ["-DPA_DEBUG=1", "-g"] if debug else []
+    out_dir = os.path.join(BUILD, "debug") if debug else BUILD
+    os.makedirs(out_dir, exist_ok=True)
+    extra = ["-DPA_DEBUG=1"] if debug else []
     objs = []
 
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
         if src.endswith(".cpp"):
             cmd = [cxx(), *CXX_FLAGS, *extra]
         else:
@@ -88,10 +93,11 @@ def build(debug: bool = False, verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(compile_one, sources()))
-    tmp = LIB + ".tmp"
+    lib = LIB_DEBUG if debug else LIB
+    tmp = lib + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

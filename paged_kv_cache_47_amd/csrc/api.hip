@@ -349,6 +349,7 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported block size, head dim or group size";
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP launch failed";
+    case PA_ERR_METADATA: return "device metadata breaks a precondition (debug build check)";
   }
   return "unknown status";
 }
@@ -361,10 +362,12 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v, c
   if (num_tokens < 0) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  if (desc->kv_dtype == PA_KV_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+#if PA_DEBUG
+  if ((st = debug_check_write(*desc, slot_mapping, num_tokens, stream)) != PA_OK) return st;
+#endif
   hipError_t e;
   if (desc->kv_dtype == PA_KV_I8) {
-    if (!k_scale || !v_scale) return PA_ERR_NULL;
-    if (num_tokens > 2147483647 / 1) return PA_ERR_SHAPE;
     e = launch_write_i8(*desc, k, v, slot_mapping, num_tokens, k_cache, v_cache, k_scale, v_scale, stream);
   } else {
     e = launch_write_f16(*desc, k, v, slot_mapping, num_tokens, k_cache, v_cache, stream);
@@ -380,8 +383,45 @@ pa_status pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !src_dst) return PA_ERR_NULL;
   if (desc->kv_dtype == PA_KV_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+#if PA_DEBUG
+  if ((st = debug_check_copy(*desc, src_dst, num_pairs, stream)) != PA_OK) return st;
+#endif
   hipError_t e = launch_copy(*desc, k_cache, v_cache, k_scale, v_scale, src_dst, num_pairs, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_check_write(const pa_cache_desc* desc, const int32_t* slot_mapping, int32_t num_tokens,
+                         int32_t* status, hipStream_t stream) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (!status || (num_tokens > 0 && !slot_mapping)) return PA_ERR_NULL;
+  return launch_check_write(*desc, slot_mapping, num_tokens, status, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_check_attend(const pa_cache_desc* desc, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
+                          const int32_t* h_seq_lens, const int32_t* h_q_lens, const pa_attend_opts* opts,
+                          int32_t* status, hipStream_t stream) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq < 0) return PA_ERR_SHAPE;
+  if (opts && opts->window < 0) return PA_ERR_SHAPE;
+  if (!status || (num_seqs > 0 && (!block_tables || !seq_lens || !q_lens || !h_seq_lens || !h_q_lens)))
+    return PA_ERR_NULL;
+  return launch_check_attend(*desc, block_tables, max_blocks_per_seq, seq_lens, q_lens, num_seqs, h_seq_lens,
+                             h_q_lens, opts ? opts->window : 0, status, stream) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+pa_status pa_check_copy(const pa_cache_desc* desc, const int32_t* src_dst, int32_t num_pairs, int32_t* status,
+                        hipStream_t stream) {
+  pa_status st = check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (!status || (num_pairs > 0 && !src_dst)) return PA_ERR_NULL;
+  return launch_check_copy(*desc, src_dst, num_pairs, status, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads, int32_t num_seqs,
@@ -431,6 +471,11 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   if (max_blocks_per_seq == 0) return PA_ERR_SHAPE;
   if (!(scale > 0.f) || scale > 3.0e38f) return PA_ERR_SHAPE;   // positive and finite
   if (workspace_bytes < P.bytes) return PA_ERR_WORKSPACE;
+#if PA_DEBUG
+  if ((st = debug_check_attend(*desc, block_tables, max_blocks_per_seq, seq_lens, q_lens, num_seqs, h_seq_lens,
+                               h_q_lens, P.window, stream)) != PA_OK)
+    return st;
+#endif
 
   char* ws = (char*)workspace;
   const int g = num_q_heads / desc->num_kv_heads;

@@ -157,6 +157,25 @@ hipError_t launch_write_i8(const pa_cache_desc& d, const void* k, const void* v,
 hipError_t launch_copy(const pa_cache_desc& d, void* kc, void* vc, void* ks, void* vs,
                        const int32_t* pairs, int32_t n, hipStream_t s);
 
+// Metadata checks (check.hip): each clears `st` and records a violation there.
+hipError_t launch_check_write(const pa_cache_desc& d, const int32_t* slots, int32_t T, int32_t* st, hipStream_t s);
+hipError_t launch_check_attend(const pa_cache_desc& d, const int32_t* tables, int32_t max_blocks,
+                               const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
+                               const int32_t* hL, const int32_t* hQ, int32_t window, int32_t* st, hipStream_t s);
+hipError_t launch_check_copy(const pa_cache_desc& d, const int32_t* pairs, int32_t n, int32_t* st, hipStream_t s);
+#ifndef PA_DEBUG
+#define PA_DEBUG 0
+#endif
+#if PA_DEBUG
+// Debug builds: run the check on the library's own status words, wait, and
+// return PA_ERR_METADATA on a violation.
+pa_status debug_check_write(const pa_cache_desc& d, const int32_t* slots, int32_t T, hipStream_t s);
+pa_status debug_check_attend(const pa_cache_desc& d, const int32_t* tables, int32_t max_blocks,
+                             const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs, const int32_t* hL,
+                             const int32_t* hQ, int32_t window, hipStream_t s);
+pa_status debug_check_copy(const pa_cache_desc& d, const int32_t* pairs, int32_t n, hipStream_t s);
+#endif
+
 // ----------------------------------------------------------------------------
 // Device helpers
 // ----------------------------------------------------------------------------

@@ -51,6 +51,8 @@ class AttendInfo(ctypes.Structure):
 
 
 _lib = None
+_debug_lib = None
+DEBUG_LIB_PATH = LIB_PATH.replace("libpa.so", "libpa_debug.so")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -62,6 +64,24 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib = cdll(path)
     except LibraryMissing as e:
         raise LibraryNotBuilt(str(e)) from None
+    _lib = _bind(lib)
+    return _lib
+
+
+def load_debug_library(path: str = DEBUG_LIB_PATH) -> ctypes.CDLL:
+    """libpa_debug.so (the same entry points; every write, attention and copy
+    checks its device metadata first and returns PA_ERR_METADATA on a
+    violation).  Loaded beside libpa.so, never in its place."""
+    global _debug_lib
+    if _debug_lib is None:
+        import os
+        if not os.path.exists(path):
+            raise LibraryNotBuilt(f"{path} is missing: build it with `python -m paged_kv_cache_47_amd.build --debug`")
+        _debug_lib = _bind(ctypes.CDLL(path))
+    return _debug_lib
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pdesc, popts = ctypes.POINTER(CacheDesc), ctypes.POINTER(AttendOpts)
     lib.pa_write_kv.argtypes = [pdesc, vp, vp, vp, i32, vp, vp, vp, vp, vp]
@@ -80,8 +100,65 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_status_str.argtypes = [ctypes.c_int]
     lib.pa_status_str.restype = ctypes.c_char_p
-    _lib = lib
+    lib.pa_check_write.argtypes = [pdesc, vp, i32, vp, vp]
+    lib.pa_check_write.restype = ctypes.c_int
+    lib.pa_check_attend.argtypes = [pdesc, vp, i32, vp, vp, i32, vp, vp, popts, vp, vp]
+    lib.pa_check_attend.restype = ctypes.c_int
+    lib.pa_check_copy.argtypes = [pdesc, vp, i32, vp, vp]
+    lib.pa_check_copy.restype = ctypes.c_int
     return lib
+
+
+PA_ERR_METADATA = 7
+CHECK_CODES = {0: "ok", 1: "slot out of range", 2: "duplicate slot", 3: "int8 block tokens not consecutive",
+               4: "lengths out of range", 5: "device lengths differ from the host copies",
+               6: "block id out of range", 7: "bad copy pair"}
+
+
+def _status_buffer(device) -> torch.Tensor:
+    return torch.empty(8, dtype=torch.int32, device=device)
+
+
+def pa_check_write(slot_mapping, k_cache, layer: int = 0, stream=None) -> np.ndarray:
+    """Check ``pa_write_kv``'s slot preconditions on the device; returns the
+    status words (synchronises): [code, index, value, bound]."""
+    lib = load_library()
+    desc = cache_desc(k_cache, layer)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    st = _status_buffer(slot_mapping.device)
+    _check(lib.pa_check_write(ctypes.byref(desc), _ptr(slot_mapping), slot_mapping.shape[0], _ptr(st),
+                              _stream(stream)), "pa_check_write")
+    return st[:4].cpu().numpy()
+
+
+def pa_check_attend(k_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, window: int = 0,
+                    stream=None) -> np.ndarray:
+    """Check ``pa_attend``'s metadata preconditions on the device; returns the
+    status words (synchronises)."""
+    lib = load_library()
+    desc = cache_desc(k_cache)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(q_lens, "q_lens", torch.int32, 1)
+    hl, hq = _host_i32(h_seq_lens), _host_i32(h_q_lens)
+    opts = _opts(window=window)
+    st = _status_buffer(seq_lens.device)
+    _check(lib.pa_check_attend(ctypes.byref(desc), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                               _ptr(q_lens), len(hl), _host_addr(hl), _host_addr(hq), ctypes.byref(opts), _ptr(st),
+                               _stream(stream)), "pa_check_attend")
+    return st[:4].cpu().numpy()
+
+
+def pa_check_copy(k_cache, src_dst, stream=None) -> np.ndarray:
+    """Check ``pa_copy_blocks``'s pair preconditions on the device; returns the
+    status words (synchronises)."""
+    lib = load_library()
+    desc = cache_desc(k_cache)
+    _need(src_dst, "src_dst", torch.int32, 2)
+    st = _status_buffer(src_dst.device)
+    _check(lib.pa_check_copy(ctypes.byref(desc), _ptr(src_dst), src_dst.shape[0], _ptr(st), _stream(stream)),
+           "pa_check_copy")
+    return st[:4].cpu().numpy()
 
 
 def _check(status: int, what: str) -> None:

@@ -35,8 +35,8 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = pa.load_library()
-    for code in range(7):
-        assert lib.pa_status_str(code)
+    for code in range(8):
+        assert lib.pa_status_str(code) and lib.pa_status_str(code) != lib.pa_status_str(99)
     assert b"unknown" in lib.pa_status_str(99)
 
 
@@ -116,13 +116,41 @@ def test_workspace_sizes():
     assert _ws(d, 32, [600], [512]) < _ws(d, 32, [600], [1], pa.AttendOpts(64, 0))
 
 
-def test_library_is_newer_than_its_sources():
-    # a stale libpa.so would silently test old kernels: rebuild after editing csrc/ or include/
-    lib = os.path.join(ROOT, "paged_kv_cache_47_amd", "libpa.so")
+@pytest.mark.parametrize("name", ["libpa.so", "libpa_debug.so"])
+def test_library_is_newer_than_its_sources(name):
+    # a stale library would silently test old kernels: rebuild after editing csrc/ or include/
+    lib = os.path.join(ROOT, "paged_kv_cache_47_amd", name)
     srcs = [os.path.join(d, f) for d in (os.path.join(ROOT, "paged_kv_cache_47_amd", "csrc"), os.path.join(ROOT, "include"))
             for f in os.listdir(d)]
     newest = max(os.path.getmtime(p) for p in srcs)
-    assert os.path.getmtime(lib) >= newest, "libpa.so is older than its sources"
+    assert os.path.getmtime(lib) >= newest, f"{name} is older than its sources"
+
+
+def test_debug_library_exports_the_same_entry_points():
+    dbg = pa.load_debug_library()
+    for n in _declared():
+        assert hasattr(dbg, n), n
+    assert dbg is not pa.load_library()
+
+
+def test_check_entry_points_validate_on_the_host():
+    """The metadata checks reject bad host arguments before anything is
+    enqueued (no GPU here): a missing status buffer, negative counts."""
+    for lib in (pa.load_library(), pa.load_debug_library()):
+        d = _desc()
+        fake = ctypes.c_void_p(256)
+        assert lib.pa_check_write(ctypes.byref(d), fake, 4, None, None) == 1
+        assert lib.pa_check_write(ctypes.byref(d), fake, -1, fake, None) == 2
+        assert lib.pa_check_write(ctypes.byref(_desc(head_dim=96)), fake, 4, fake, None) == 4
+        L = np.array([5], np.int32)
+        assert lib.pa_check_attend(ctypes.byref(d), fake, 1, fake, fake, 1, pa._hp(L), pa._hp(L), None, None,
+                                   None) == 1
+        assert lib.pa_check_attend(ctypes.byref(d), fake, 1, fake, fake, -1, pa._hp(L), pa._hp(L), None, fake,
+                                   None) == 2
+        assert lib.pa_check_attend(ctypes.byref(d), None, 1, fake, fake, 1, pa._hp(L), pa._hp(L), None, fake,
+                                   None) == 1
+        assert lib.pa_check_copy(ctypes.byref(d), fake, 2, None, None) == 1
+        assert lib.pa_check_copy(ctypes.byref(d), fake, -2, fake, None) == 2
 
 
 def test_layer_validation():
