@@ -512,6 +512,10 @@ def main(argv=None) -> int:
     ap.add_argument("--system-prompts", type=int, default=0,
                     help="workload 6: requests start with one of this many shared system prompts, served from "
                          "the prefix cache")
+    ap.add_argument("--w5-pool", default="i8", choices=("i8", "f16", "bf16"),
+                    help="workload 5: the pool type of the same packed batch (f16/bf16: N(0,1) contents in place)")
+    ap.add_argument("--w5-chunks-only", action="store_true",
+                    help="workload 5: the 8 prefill chunks alone (no decode sequences): the MFMA kernel by itself")
     ap.add_argument("--no-share", action="store_true",
                     help="workload 4 control: every sequence owns its own copy of the prefix (no sharing, no forks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -541,7 +545,8 @@ def main(argv=None) -> int:
         return 0
     if args.summarize_trace:
         import synthetic
-        w = synthetic.CONFIGS[args.workload]()
+        w = (synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192)
+             if args.workload == 5 else synthetic.CONFIGS[args.workload]())
         w.window = args.window
         L, Q = _step_lengths(w, 1 if args.workload == 2 else 0)
         vb, mf, _ = work_split(w, L, Q)
@@ -575,8 +580,13 @@ def main(argv=None) -> int:
     if args.kv_dtype == "i8" and args.workload != 6:
         print("--kv-dtype i8 applies to workload 6 (workload 5 is the int8 kernel workload)", file=sys.stderr)
         return 2
+    if (args.w5_pool != "i8" or args.w5_chunks_only) and args.workload != 5:
+        print("--w5-pool and --w5-chunks-only apply to workload 5 only", file=sys.stderr)
+        return 2
     if args.workload == 4 and args.no_share:
         w = synthetic.config4(share=False)
+    elif args.workload == 5:
+        w = synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192)
     elif args.workload == 2:
         w = synthetic.config2(num_layers=args.layers, kv_dtype=args.kv_dtype)
     elif args.workload == 3:
@@ -741,7 +751,9 @@ def main(argv=None) -> int:
                    + (f" [sliding window of {args.window} keys]" if args.window else "")
                    + (f" [{w.num_layers} layers per block: every step writes and attends each]"
                       if w.num_layers > 1 else "")
-                   + (" [bf16 KV, queries and outputs]" if w.kv_dtype == "bf16" else ""),
+                   + (" [bf16 KV, queries and outputs]" if w.kv_dtype == "bf16" else "")
+                   + (f" [{args.w5_pool} pool with N(0,1) contents]" if args.w5_pool != "i8" else "")
+                   + (" [the 8 prefill chunks only]" if args.w5_chunks_only else ""),
                    "num_seqs": S, "kv_tokens": int(L.sum()),
                    "query_rows": int(Q.sum()), "num_blocks": w.num_blocks,
                    "partition_tokens": args.partition_tokens, "window": args.window, "layers": w.num_layers},

@@ -10,6 +10,9 @@ namespace pa {
 #endif
 constexpr int kMfmaWaves = PA_PF_WAVES;          // waves per MFMA workgroup, 32 query rows each
 constexpr int kMfmaRows = 32 * kMfmaWaves;
-constexpr int kMfmaBN = 64;   // keys per step of a row tile       // query rows per MFMA workgroup
+#ifndef PA_PF_BN
+#define PA_PF_BN 64
+#endif
+constexpr int kMfmaBN = PA_PF_BN;   // keys per step of a row tile
 
 }  // namespace pa

@@ -18,6 +18,7 @@ typedef __bf16 bf164_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Pool element kinds the kernels are built for (the pa_kv_dtype values).
 constexpr int kKvF16 = PA_KV_F16, kKvI8 = PA_KV_I8, kKvBF16 = PA_KV_BF16;
@@ -180,7 +181,6 @@ pa_status debug_check_copy(const pa_cache_desc& d, const int32_t* pairs, int32_t
 // Device helpers
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // Pair dot products with an fp32 accumulator, and the 16x16x32 matrix
 // product, for either 16-bit type.
 __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }

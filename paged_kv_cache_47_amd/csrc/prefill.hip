@@ -115,7 +115,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
     for (int nt = 0; nt < NT; ++nt) o[rb][nt] = (float4_t)0.f;
   }
 
-  uint4 stk[PT], stv[PT];
+  // native vectors: an array of HIP's uint4 class type was kept in private memory (80 B per lane
+  // of scratch traffic each step on 16-bit pools); these stay in registers
+  u32x4_t stk[PT], stv[PT];
   float nks[KB];  // int8: K scales of the four 16-key blocks of the tiles in flight
   float nvc[PT];  // int8: V scale of the 16-key block of each of this thread's staging chunks
   // Physical blocks, read one step before the tiles they address: per 16-key
@@ -167,8 +169,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
           (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.chunk[i]), a.num_blocks) * a.blk_tiles + h;
       if constexpr (I8) nvc[i] = (float)(a.vs + tile)[vz];
       const uint32_t off = (uint32_t)((kg % kBlockSize) * D * EB + ch * 16);
-      stk[i] = *(const uint4*)((const char*)a.kc + tile * kTileBytes + off);
-      stv[i] = *(const uint4*)((const char*)a.vc + tile * kTileBytes + off);
+      stk[i] = *(const u32x4_t*)((const char*)a.kc + tile * kTileBytes + off);
+      stv[i] = *(const u32x4_t*)((const char*)a.vc + tile * kTileBytes + off);
     }
   };
   // int8 tiles become fp16: K as exact codes (its scale multiplies the
@@ -186,8 +188,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
         const half2_t vs2 = {vh, vh};
         half_t* kd = &ldk[buf][key * LDK + ch * 16];
         half_t* vd = &ldv[buf][key * LDV + ch * 16];
-        const uint32_t kw[4] = {stk[i].x, stk[i].y, stk[i].z, stk[i].w};
-        const uint32_t vw[4] = {stv[i].x, stv[i].y, stv[i].z, stv[i].w};
+        const uint32_t kw[4] = {stk[i][0], stk[i][1], stk[i][2], stk[i][3]};
+        const uint32_t vw[4] = {stv[i][0], stv[i][1], stv[i][2], stv[i][3]};
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           const half2_t a0 = sdwa_pair<0, 1>(kw[2 * c2], kw[2 * c2]), a1 = sdwa_pair<2, 3>(kw[2 * c2], kw[2 * c2]);
@@ -204,8 +206,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
           *(half8_t*)(vd + 8 * c2) = (half8_t){b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
         }
       } else {
-        *(uint4*)&ldk[buf][key * LDK + ch * 8] = stk[i];
-        *(uint4*)&ldv[buf][key * LDV + ch * 8] = stv[i];
+        *(u32x4_t*)&ldk[buf][key * LDK + ch * 8] = stk[i];
+        *(u32x4_t*)&ldv[buf][key * LDV + ch * 8] = stv[i];
       }
     }
   };
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
       }
     }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < KB / 2; ++hh) {
       // this half's V operands (transposing LDS reads) are requested before its weights are formed
       act8_t vq[NT];
 #pragma unroll

@@ -355,12 +355,17 @@ def config4(seed: int = 47004, num_requests: int = 64, prefix: int = 1024, min_s
 
 
 def config5(seed: int = 47005, num_chunks: int = 8, chunk_q: int = 512, max_chunk_ctx: int = 8192,
-            num_decode: int = 192, max_decode_len: int = 32768) -> Workload:
+            num_decode: int = 192, max_decode_len: int = 32768, kv_dtype: str = "i8") -> Workload:
     """Packed chunked prefill + decode over an int8 pool: ``num_chunks``
     segments of ``chunk_q`` query tokens with cached context U[0,8192], then
     ``num_decode`` decode sequences with post-write length U[1,32768].  The
     cached context is N(0,1) fp16 K/V, written into the int8 pool token by
-    token before the step.  Unused pool slots hold uniform int8 filler."""
+    token before the step.  Unused pool slots hold uniform int8 filler.
+
+    ``kv_dtype`` "f16" / "bf16": the same batch over a 16-bit pool whose
+    contents are N(0,1) (the context already in place, as in workload 3);
+    with ``num_decode=0`` that is the chunks alone (the same contexts: they
+    are drawn first)."""
     hq, hkv, d = 32, 8, 128
     rng = np.random.default_rng([seed, S_META])
     cctx = rng.integers(0, max_chunk_ctx + 1, num_chunks).astype(np.int64)
@@ -376,6 +381,13 @@ def config5(seed: int = 47005, num_chunks: int = 8, chunk_q: int = 512, max_chun
         return (normal_f16((seed, S_CTX_K, i), (n, hkv, d)),
                 normal_f16((seed, S_CTX_V, i), (n, hkv, d)))
 
+    if kv_dtype != "i8":
+        return Workload(
+            name=f"packed-{kv_dtype}-prefill" + ("-decode" if num_decode else ""), seed=seed, num_q_heads=hq,
+            num_kv_heads=hkv, head_dim=d, block_size=BLOCK_SIZE, kv_dtype=kv_dtype, scale=1.0 / math.sqrt(d),
+            num_blocks=nb, first_pops=perm, ctx_lens=ctx, pool_draws=_f16_pool(seed, nb, hkv, d, kv_dtype=kv_dtype),
+            steps=[_step(seed, (0,), q_lens, hq, hkv, d, kv_dtype=kv_dtype)],
+        )
     return Workload(
         name="packed-int8-prefill-decode", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
         block_size=BLOCK_SIZE, kv_dtype="i8", scale=1.0 / math.sqrt(d), num_blocks=nb,
