@@ -122,8 +122,11 @@ def window_lo(pos: int, window: int) -> int:
 
 def work_split(w, L, Q):
     """Algorithmic work of one step: (vector-path KV bytes, MFMA-path flops,
-    total KV bytes).  Rows with q_len * group >= 16 go to the MFMA path.  A
-    vector-path row reads the K and V of the keys it sees (int8: plus one
+    total KV bytes).  Sequences with q_len * group >= 16 rows go to the row
+    tiles (with groups of 16 or 32: from two query rows; single query rows
+    then take the decode units on the matrix cores, which like the vector
+    path are bound by KV bytes).  A decode-unit row reads the K and V of the
+    keys it sees (int8: plus one
     scale per block and head for each); a sequence's total counts the keys
     any of its rows sees once; with a sliding window only keys inside it."""
     eb = 1 if w.kv_dtype == "i8" else 2
@@ -139,7 +142,7 @@ def work_split(w, L, Q):
         total += keys_bytes(window_lo(l - q, w.window), l)
         if q == 0:
             continue
-        if q * w.group >= 16:
+        if q * w.group >= (2 * w.group if w.group >= 16 else 16):
             vis = sum(l - q + t + 1 - window_lo(l - q + t, w.window) for t in range(q))
             mfma_flops += 4 * w.head_dim * w.num_q_heads * vis
         else:
@@ -512,6 +515,9 @@ def main(argv=None) -> int:
     ap.add_argument("--system-prompts", type=int, default=0,
                     help="workload 6: requests start with one of this many shared system prompts, served from "
                          "the prefix cache")
+    ap.add_argument("--w3-q-heads", type=int, default=32, choices=(8, 16, 32, 64, 128, 256),
+                    help="workload 3: query heads over the 8 KV heads (128 and 256: groups of 16 and 32, on the "
+                         "matrix-core decode kernel)")
     ap.add_argument("--w5-pool", default="i8", choices=("i8", "f16", "bf16"),
                     help="workload 5: the pool type of the same packed batch (f16/bf16: N(0,1) contents in place)")
     ap.add_argument("--w5-chunks-only", action="store_true",
@@ -590,7 +596,7 @@ def main(argv=None) -> int:
     elif args.workload == 2:
         w = synthetic.config2(num_layers=args.layers, kv_dtype=args.kv_dtype)
     elif args.workload == 3:
-        w = synthetic.config3(kv_dtype=args.kv_dtype)
+        w = synthetic.config3(kv_dtype=args.kv_dtype, num_q_heads=args.w3_q_heads)
     else:
         w = synthetic.CONFIGS[args.workload]()
     w.window = args.window
@@ -689,9 +695,12 @@ def main(argv=None) -> int:
         ach = roof_bytes / (k_ms * 1e-3) / 1e9
         roof.append({"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(ach / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profile() if (args.workload == 3 and not args.partition_tokens
+                     "traffic": traffic_from_profile() if (args.workload == 3 and args.w3_q_heads == 32
+                                                           and args.kv_dtype == "f16" and not args.partition_tokens
                                                            and not args.window) else None,
-                     "kernel": "decode_kernel (split-K vector path)", "kernel_ms": round(k_ms, 5),
+                     "kernel": ("decode_mfma_kernel (split-K units on the matrix cores)"
+                                if w.num_q_heads // w.num_kv_heads >= 16 else "decode_kernel (split-K vector path)"),
+                     "kernel_ms": round(k_ms, 5),
                      "kernel_ms_median": round(float(np.median(k_all)), 5),
                      "algorithmic_bytes_per_launch": roof_bytes})
         if shared:
@@ -752,6 +761,7 @@ def main(argv=None) -> int:
                    + (f" [{w.num_layers} layers per block: every step writes and attends each]"
                       if w.num_layers > 1 else "")
                    + (" [bf16 KV, queries and outputs]" if w.kv_dtype == "bf16" else "")
+                   + (f" [{args.w3_q_heads} query heads]" if args.w3_q_heads != 32 else "")
                    + (f" [{args.w5_pool} pool with N(0,1) contents]" if args.w5_pool != "i8" else "")
                    + (" [the 8 prefill chunks only]" if args.w5_chunks_only else ""),
                    "num_seqs": S, "kv_tokens": int(L.sum()),

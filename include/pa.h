@@ -34,7 +34,7 @@
  *   v_scale [num_blocks][num_layers][num_kv_heads] ([engine] "INT8 KV cache
  *   design": symmetric, no zero point, one scale per block per head).
  * - Supported shapes: block_size 16, head_dim 64 or 128, num_q_heads a
- *   multiple of num_kv_heads with a group size of 1, 2, 4 or 8,
+ *   multiple of num_kv_heads with a group size of 1, 2, 4, 8, 16 or 32,
  *   num_blocks * block_size < 2^31, and for int8 pools scale arrays of
  *   less than 2^31 bytes (pa_attend).  Anything else returns
  *   PA_ERR_UNSUPPORTED (or PA_ERR_SHAPE for inconsistent sizes).
@@ -131,9 +131,14 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v,
  *                     what remains).  0 = p chosen from the batch, > 0 = p
  *                     (a multiple of 16), < 0 = never split.
  *   mfma_min_rows     a sequence whose q_len * group rows reach this count
- *                     runs on the MFMA path, otherwise on the vector path:
- *                     0 = default (16), 1 = every sequence on MFMA,
- *                     INT32_MAX = every sequence on the vector path.
+ *                     runs on the row-tile (prefill) kernel, otherwise its
+ *                     query rows are split-K units of the decode kernel:
+ *                     0 = default (16; 2 * group for groups of 16 or 32),
+ *                     1 = every sequence on row tiles, INT32_MAX = every
+ *                     query row as decode units.  Groups of 16 or 32 run
+ *                     their decode units on the matrix cores too (one query
+ *                     row is already 16 or 32 rows of a dense product); the
+ *                     smaller groups on the vector ALUs.
  *   vector_begin/end  optional caller-created HIP events, recorded on
  *   mfma_begin/end    `stream` immediately before and after the vector-path
  *                     (resp. MFMA-path) attention kernel when that kernel is

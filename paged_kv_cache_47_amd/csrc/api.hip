@@ -237,7 +237,7 @@ static pa_status check_desc(const pa_cache_desc* d) {
 static pa_status check_heads(const pa_cache_desc* d, int32_t hq) {
   if (hq <= 0 || hq % d->num_kv_heads != 0) return PA_ERR_SHAPE;
   const int g = hq / d->num_kv_heads;
-  if (g != 1 && g != 2 && g != 4 && g != 8) return PA_ERR_UNSUPPORTED;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16 && g != 32) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -265,7 +265,11 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   if (num_seqs > 0 && (hL == nullptr || hQ == nullptr)) return PA_ERR_NULL;
   const int g = hq / d->num_kv_heads;
   int32_t req_part = opts ? opts->partition_tokens : 0;
-  P.min_rows = (opts && opts->mfma_min_rows > 0) ? opts->mfma_min_rows : 16;
+  // Row-tile (prefill) kernel from 16 rows of a sequence up; with groups of 16
+  // or 32 a single query row already has that many, and its G rows go to the
+  // matrix-core decode kernel instead (split-K units, one row per unit), so
+  // there the row tiles start at two query rows.
+  P.min_rows = (opts && opts->mfma_min_rows > 0) ? opts->mfma_min_rows : (g >= 16 ? 2 * g : 16);
   P.window = opts ? opts->window : 0;
   if (req_part > 0 && req_part % kBlockSize != 0) return PA_ERR_SHAPE;
   if (P.window < 0) return PA_ERR_SHAPE;

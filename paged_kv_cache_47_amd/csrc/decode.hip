@@ -22,7 +22,7 @@
 // log-sum-exp form by `reduce_kernel` (a kernel boundary, not a device-scope
 // fence: each XCD has its own L2, so a device-wide release/acquire inside
 // the kernel would write back and invalidate whole caches).
-#include "pa_internal.h"
+#include "units.h"
 
 namespace pa {
 
@@ -93,100 +93,6 @@ __device__ __forceinline__ uint16_t scale_bits(__amdgpu_buffer_rsrc_t rs, int64_
 }
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)__builtin_bit_cast(half_t, b); }
 
-// ===================================================== self-planned units ===
-// Row i of a self-planned batch as every workgroup derives it from the device
-// lengths (clamped as the plan kernel clamps them): the keys its query walks,
-// its equal units and their cost bucket.  No query row: no units.
-struct SPRow {
-  int keys, parts, bucket;
-};
-
-__device__ __forceinline__ SPRow sp_row(const AttnArgs& a, int i) {
-  SPRow r = {0, 0, 0};
-  const int L = min(max(a.seq_lens[i], 0), a.max_kv);
-  if (min(a.q_lens[i], L) < 1) return r;
-  r.keys = vector_keys(L - 1, a.window);
-  r.parts = parts_for(r.keys, a.part);
-  const int sz = r.parts > 1 ? (((r.keys + r.parts - 1) / r.parts + 15) & ~15) : r.keys;
-  r.bucket = min(sz >> 6, kSelfPlanBuckets - 1);
-  return r;
-}
-
-// The x-th unit of the order every workgroup derives alike (cost bucket
-// descending, then sequence, then partition): a count of units per bucket,
-// a scan over the buckets to find x's bucket and its rank there, then a scan
-// over the sequences of that bucket to find the row.  Returns false when x
-// is past the last unit (the device lengths then disagree with the host's).
-struct SPUnit {
-  int seq, part, parts;
-};
-
-template <int NT>
-__device__ bool sp_locate(const AttnArgs& a, int x, SPUnit& out) {
-  static_assert(kSelfPlanBuckets == 64, "one lane per bucket");
-  constexpr int PER = kSelfPlanMaxSeqs / NT;   // sequences per thread, in order
-  __shared__ int cnt[kSelfPlanBuckets];
-  __shared__ int wsum[NT / 64];
-  __shared__ int sel[5];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (tid < kSelfPlanBuckets) cnt[tid] = 0;
-  if (tid == 0) sel[0] = -1;
-  __syncthreads();
-  SPRow rows[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int i = tid * PER + k;
-    rows[k] = i < a.num_seqs ? sp_row(a, i) : SPRow{0, 0, 0};
-    if (rows[k].parts > 0) atomicAdd(&cnt[rows[k].bucket], rows[k].parts);
-  }
-  __syncthreads();
-  if (wv == 0) {
-    const int b = kSelfPlanBuckets - 1 - lane;   // lane 0 holds the largest bucket
-    const int c = cnt[b];
-    int inc = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(inc, off, 64);
-      if (lane >= off) inc += t;
-    }
-    if (x >= inc - c && x < inc) {
-      sel[0] = b;
-      sel[1] = x - (inc - c);
-    }
-  }
-  __syncthreads();
-  const int B = sel[0], r = sel[1];
-  if (B < 0) return false;
-  int mine = 0;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) mine += rows[k].bucket == B ? rows[k].parts : 0;
-  int inc = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += t;
-  }
-  if (lane == 63) wsum[wv] = inc;
-  __syncthreads();
-  int base = inc - mine;
-  for (int w = 0; w < wv; ++w) base += wsum[w];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int c = rows[k].bucket == B ? rows[k].parts : 0;
-    if (r >= base && r < base + c) {
-      sel[2] = tid * PER + k;
-      sel[3] = r - base;
-      sel[4] = rows[k].parts;
-    }
-    base += c;
-  }
-  __syncthreads();
-  out.seq = sel[2];
-  out.part = sel[3];
-  out.parts = sel[4];
-  return true;
-}
-
 // ============================================================ vector path ===
 #ifndef PA_DECODE_NW
 #define PA_DECODE_NW 4   // waves per workgroup
@@ -247,51 +153,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps block indices scalar
   // this workgroup's unit: its sequence, query row, partition and the row's partition count
-  int u, seq, t, part_idx, parts, kv_len, q_len, q_start;
-  if (a.direct) {
-    u = seq = blockIdx.x;
-    t = part_idx = 0;
-    parts = 1;
-    kv_len = min(max(a.seq_lens[seq], 0), a.max_kv);
-    q_len = min(max(a.q_lens[seq], 0), kv_len);
-    if (q_len == 0) return;
-    q_start = seq;
-  } else if (a.selfplan) {
-    SPUnit su;
-    if (!sp_locate<NW * 64>(a, blockIdx.x, su)) return;
-    u = blockIdx.x;
-    seq = su.seq;
-    t = 0;
-    part_idx = su.part;
-    parts = su.parts;
-    kv_len = min(max(a.seq_lens[seq], 0), a.max_kv);
-    q_len = 1;
-    q_start = seq;   // one query row per sequence: packed row = sequence
-    if (part_idx == 0 && h == 0 && threadIdx.x == 0) a.row_u0[seq] = u;
-  } else {
-    u = a.vorder[blockIdx.x];   // units go out longest first
-    const int2 un = a.vunit[u];
-    if (un.x < 0) return;
-    const VTok vt = a.vtok[un.x];
-    if (vt.seq < 0) return;
-    const SeqInfo si = a.seqs[vt.seq];
-    seq = vt.seq;
-    t = vt.t;
-    part_idx = un.y;
-    parts = vt.parts;
-    kv_len = si.kv_len;
-    q_len = si.q_len;
-    q_start = si.q_start;
-  }
-  // device lengths that split a row the host's lengths did not: no partial buffer to write to
-  if (parts > 1 && a.po == nullptr) return;
-  const int nvis = kv_len - q_len + t + 1;
-  const int klo = window_lo(nvis - 1, a.window);        // first visible key
-  const int k0 = klo & ~(kBlockSize - 1);
-  // a split row's units are equal (rounded up to 16 keys), not full partitions and a remainder
-  const int sz = parts > 1 ? (((nvis - k0 + parts - 1) / parts + 15) & ~15) : a.part;
-  const int kbeg = k0 + part_idx * sz;
-  const int kend = min(nvis, kbeg + sz);
+  Unit un;
+  if (!resolve_unit<NW * 64>(a, h, un)) return;
+  const int u = un.u, seq = un.seq, t = un.t, parts = un.parts, q_start = un.q_start;
+  const int klo = un.klo, kbeg = un.kbeg, kend = un.kend;
   const int grp = lane / LPT, sub = lane % LPT;
   const int64_t row0 = (int64_t)(q_start + t) * a.hq + (int64_t)h * G;
   const int32_t* tbl = a.block_tables + (int64_t)seq * a.max_blocks;
@@ -703,6 +568,8 @@ static hipError_t decode_d(const AttnArgs& a, int g, int kv, int n, hipStream_t 
 }
 
 hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, int kv, int n, hipStream_t s) {
+  // groups of 16 or more rows: the same units on the matrix cores (decode_mfma.hip)
+  if (group >= 16) return launch_decode_mfma(a, head_dim, group, kv, n, s);
   return head_dim == 128 ? decode_d<128>(a, group, kv, n, s) : decode_d<64>(a, group, kv, n, s);
 }
 
@@ -714,6 +581,8 @@ static hipError_t reduce_g(const AttnArgs& a, int g, int n, hipStream_t s) {
     case 2: reduce_kernel<D, 2, OUT><<<grid, 256, 0, s>>>(a); break;
     case 4: reduce_kernel<D, 4, OUT><<<grid, 256, 0, s>>>(a); break;
     case 8: reduce_kernel<D, 8, OUT><<<grid, 256, 0, s>>>(a); break;
+    case 16: reduce_kernel<D, 16, OUT><<<grid, 256, 0, s>>>(a); break;
+    case 32: reduce_kernel<D, 32, OUT><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

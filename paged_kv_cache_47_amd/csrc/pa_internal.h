@@ -149,6 +149,7 @@ struct PlanArgs {
 // Launchers (one translation unit each); all return hipGetLastError() after launch.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, int kv, int n_vunit, hipStream_t s);
+hipError_t launch_decode_mfma(const AttnArgs& a, int head_dim, int group, int kv, int n_vunit, hipStream_t s);
 hipError_t launch_reduce(const AttnArgs& a, int head_dim, int group, int kv, int n_vtok, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs& a, int head_dim, int group, int kv, int n_munit, hipStream_t s);
 hipError_t launch_write_f16(const pa_cache_desc& d, const void* k, const void* v, const int32_t* slots,

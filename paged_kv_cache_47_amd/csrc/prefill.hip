@@ -368,6 +368,8 @@ static hipError_t prefill_g(const AttnArgs& a, int g, int n, hipStream_t s) {
     case 2: prefill_kernel<D, 2, KV><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
     case 4: prefill_kernel<D, 4, KV><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
     case 8: prefill_kernel<D, 8, KV><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 16: prefill_kernel<D, 16, KV><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
+    case 32: prefill_kernel<D, 32, KV><<<grid, 64 * kMfmaWaves, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -93,7 +93,8 @@ def _attend(desc, hq, L, Q, maxb, ws_bytes=1 << 20, ptrs=True, opts=None, scales
 def test_attend_validation():
     d = _desc()
     assert _attend(d, 3, [5], [1], 4) == 2            # q heads not a multiple of kv heads
-    assert _attend(d, 32, [5], [1], 4) == 4           # group 16 is not built
+    assert _attend(d, 128, [5], [1], 4) == 4          # group 64 is not built (1, 2, 4, 8, 16 and 32 are)
+    assert _attend(d, 12, [5], [1], 4) == 4           # nor group 6
     assert _attend(d, 4, [5], [6], 4) == 2            # q_len > kv_len
     assert _attend(d, 4, [65], [1], 4) == 2           # longer than the table row
     assert _attend(d, 4, [5], [1], 4, ws_bytes=8) == 5
@@ -236,3 +237,16 @@ def test_noalloc_refuses_batches_beyond_its_scratch_on_the_host():
     assert st == 5                               # PA_ERR_WORKSPACE
     assert lib.pa_attend_noalloc(None, fake, 32, fake, fake, None, None, fake, L // 16, fake, fake, S,
                                  pa._hp(hl), pa._hp(hq), ctypes.c_float(0.1), fake, None, None) == 1
+
+
+def test_plan_info_for_groups_of_16_and_32():
+    """With 16 or 32 query heads per KV head a single query row is already 16
+    or 32 rows: it takes the matrix-core decode units (split-K like the vector
+    path); sequences with two or more query rows take the row tiles."""
+    pool = _meta_pool(64, 2, 128)
+    i16 = pa.pa_attend_plan_info(pool, 32, [100, 300, 5000], [1, 2, 1], partition_tokens=1024)
+    assert i16["vector_rows"] == 2 and i16["mfma_tiles"] == 1 and i16["max_parts"] == 5
+    i32 = pa.pa_attend_plan_info(pool, 64, [100] * 8, [1] * 8)
+    assert i32["vector_rows"] == 8 and i32["mfma_tiles"] == 0 and i32["plan_free"] == 1
+    forced = pa.pa_attend_plan_info(pool, 64, [100, 300], [1, 3], mfma_min_rows=1)
+    assert forced["vector_rows"] == 0 and forced["mfma_tiles"] == 2
