@@ -88,6 +88,28 @@ class TimingEvents:
         return float(ms.value)
 
 
+class SideStream:
+    """A second stream (default priority) and two untimed events for
+    pa_attend's side-stream option: the row tiles of a packed batch run there,
+    beside the decode units."""
+    DISABLE_TIMING = 0x2
+
+    def __init__(self):
+        import ctypes
+        import torch
+        self.stream = torch.cuda.Stream()
+        hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(2):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.DISABLE_TIMING)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def handles(self):
+        return (self.stream.cuda_stream, self.ev[0].value, self.ev[1].value)
+
+
 # the sources of the vector-path kernel whose HBM traffic the PMC summary records
 DECODE_SOURCES = ("decode.hip", "pa_internal.h")
 
@@ -515,6 +537,9 @@ def main(argv=None) -> int:
     ap.add_argument("--system-prompts", type=int, default=0,
                     help="workload 6: requests start with one of this many shared system prompts, served from "
                          "the prefix cache")
+    ap.add_argument("--side-stream", action="store_true",
+                    help="packed batches (workload 5): the row-tile kernel on a second stream beside the decode "
+                         "kernels (pa_attend's side-stream option)")
     ap.add_argument("--w3-q-heads", type=int, default=32, choices=(8, 16, 32, 64, 128, 256),
                     help="workload 3: query heads over the 8 KV heads (128 and 256: groups of 16 and 32, on the "
                          "matrix-core decode kernel)")
@@ -625,6 +650,7 @@ def main(argv=None) -> int:
     # timed variant records the kernel events around the first layer's attention kernels
     kc, vc, ks, vs = run.k_cache, run.v_cache, run.k_scale, run.v_scale
     outs = [torch.empty_like(run.layer_acts(x, l)[2]) for l in range(w.num_layers)]
+    side = SideStream().handles() if args.side_stream else None
 
     def step_calls(i, timed_kernel):
         calls = [pa.prepare_copy_blocks(kc, vc, x.copy_pairs, ks, vs)] if x.copy_pairs.shape[0] else []
@@ -635,7 +661,7 @@ def main(argv=None) -> int:
             calls.append(pa.prepare_attend(q, kc, vc, x.block_tables, x.seq_lens, x.q_lens, x.batch.seq_lens,
                                            x.batch.q_lens, w.scale, out=outs[layer], workspace=ws, k_scale=ks,
                                            v_scale=vs, partition_tokens=args.partition_tokens, events=ev,
-                                           window=w.window, layer=layer, reuse_plan=layer > 0))
+                                           window=w.window, layer=layer, reuse_plan=layer > 0, side=side))
         return calls
 
     prepared = {(i, tk): step_calls(i, tk) for i in range(n) for tk in (True, False)}
@@ -762,6 +788,7 @@ def main(argv=None) -> int:
                       if w.num_layers > 1 else "")
                    + (" [bf16 KV, queries and outputs]" if w.kv_dtype == "bf16" else "")
                    + (f" [{args.w3_q_heads} query heads]" if args.w3_q_heads != 32 else "")
+                   + (" [row tiles on a side stream]" if args.side_stream else "")
                    + (f" [{args.w5_pool} pool with N(0,1) contents]" if args.w5_pool != "i8" else "")
                    + (" [the 8 prefill chunks only]" if args.w5_chunks_only else ""),
                    "num_seqs": S, "kv_tokens": int(L.sum()),

@@ -163,6 +163,19 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v,
  *                     block tables and lengths ([engine] "07 Open items":
  *                     build the step's block table and batch metadata once
  *                     per step, not once per layer).
+ *   side_stream       optional second stream (same device, default priority)
+ *   side_fork         with two caller-created events (hipEventDisableTiming
+ *   side_join         is enough): when a batch has both decode units and row
+ *                     tiles ([engine] "02 The engine": one packed batch of
+ *                     prefill chunks and decode rows), the row-tile kernel
+ *                     runs on side_stream beside the decode kernels on
+ *                     `stream` (side_stream waits for side_fork, recorded on
+ *                     `stream` after the plan; `stream` waits for side_join,
+ *                     recorded on side_stream after the row tiles), so the
+ *                     HBM-bound and the matrix-bound kernels can share the
+ *                     GPU.  All three NULL: everything on `stream`.  Either
+ *                     way the call's work is complete when `stream` reaches
+ *                     the point after the call.
  */
 typedef struct {
   int32_t partition_tokens;
@@ -173,6 +186,9 @@ typedef struct {
   hipEvent_t mfma_end;
   int32_t window;
   int32_t reuse_plan;
+  hipStream_t side_stream;
+  hipEvent_t side_fork;
+  hipEvent_t side_join;
 } pa_attend_opts;
 
 /*

@@ -474,6 +474,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
     return PA_ERR_UNSUPPORTED;
   if (max_blocks_per_seq == 0) return PA_ERR_SHAPE;
   if (!(scale > 0.f) || scale > 3.0e38f) return PA_ERR_SHAPE;   // positive and finite
+  if (opts && opts->side_stream && (!opts->side_fork || !opts->side_join)) return PA_ERR_NULL;
   if (workspace_bytes < P.bytes) return PA_ERR_WORKSPACE;
 #if PA_DEBUG
   if ((st = debug_check_attend(*desc, block_tables, max_blocks_per_seq, seq_lens, q_lens, num_seqs, h_seq_lens,
@@ -545,20 +546,32 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.n_units = (int32_t)P.n_vunit;
   a.row_u0 = P.selfplan ? (int32_t*)(ws + P.off_row_u0) : nullptr;
 
-  auto mark = [&](hipEvent_t ev) { return ev == nullptr || hipEventRecord(ev, stream) == hipSuccess; };
+  auto mark = [&](hipEvent_t ev, hipStream_t s) { return ev == nullptr || hipEventRecord(ev, s) == hipSuccess; };
+  // With a side stream the row tiles run there, beside the decode units on `stream`.
+  const bool side = opts && opts->side_stream && P.n_vunit > 0 && P.n_munit > 0;
+  const hipStream_t rs = side ? opts->side_stream : stream;
+  auto row_tiles = [&]() {
+    if (!mark(opts ? opts->mfma_begin : nullptr, rs)) return false;
+    if (launch_prefill(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_munit, rs) != hipSuccess) return false;
+    return mark(opts ? opts->mfma_end : nullptr, rs);
+  };
+  if (side && (hipEventRecord(opts->side_fork, stream) != hipSuccess ||
+               hipStreamWaitEvent(opts->side_stream, opts->side_fork, 0) != hipSuccess || !row_tiles()))
+    return PA_ERR_HIP;
   if (P.n_vunit > 0) {
-    if (!mark(opts ? opts->vector_begin : nullptr)) return PA_ERR_HIP;
+    if (!mark(opts ? opts->vector_begin : nullptr, stream)) return PA_ERR_HIP;
     if (launch_decode(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_vunit, stream) != hipSuccess) return PA_ERR_HIP;
-    if (!mark(opts ? opts->vector_end : nullptr)) return PA_ERR_HIP;
+    if (!mark(opts ? opts->vector_end : nullptr, stream)) return PA_ERR_HIP;
     // one merge workgroup per vector row (self-planned: per sequence, the same count)
     if (P.max_parts > 1 && launch_reduce(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_vtok, stream) != hipSuccess)
       return PA_ERR_HIP;
   }
-  if (P.n_munit > 0) {
-    if (!mark(opts ? opts->mfma_begin : nullptr)) return PA_ERR_HIP;
-    if (launch_prefill(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_munit, stream) != hipSuccess)
+  if (side) {
+    if (hipEventRecord(opts->side_join, opts->side_stream) != hipSuccess ||
+        hipStreamWaitEvent(stream, opts->side_join, 0) != hipSuccess)
       return PA_ERR_HIP;
-    if (!mark(opts ? opts->mfma_end : nullptr)) return PA_ERR_HIP;
+  } else if (P.n_munit > 0 && !row_tiles()) {
+    return PA_ERR_HIP;
   }
   return PA_OK;
 }

@@ -40,7 +40,8 @@ class AttendOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("mfma_min_rows", ctypes.c_int32),
                 ("vector_begin", ctypes.c_void_p), ("vector_end", ctypes.c_void_p),
                 ("mfma_begin", ctypes.c_void_p), ("mfma_end", ctypes.c_void_p),
-                ("window", ctypes.c_int32), ("reuse_plan", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("reuse_plan", ctypes.c_int32),
+                ("side_stream", ctypes.c_void_p), ("side_fork", ctypes.c_void_p), ("side_join", ctypes.c_void_p)]
 
 
 class AttendInfo(ctypes.Structure):
@@ -226,10 +227,11 @@ def _hp(a: np.ndarray):
 
 
 def _opts(partition_tokens: int = 0, mfma_min_rows: int = 0, events=None, window: int = 0,
-          reuse_plan: bool = False) -> AttendOpts:
+          reuse_plan: bool = False, side=None) -> AttendOpts:
     ev = list(events) if events is not None else [None] * 4
+    sd = list(side) if side is not None else [None] * 3
     return AttendOpts(int(partition_tokens), int(mfma_min_rows), *[None if e is None else int(e) for e in ev],
-                      int(window), int(bool(reuse_plan)))
+                      int(window), int(bool(reuse_plan)), *[None if x is None else int(x) for x in sd])
 
 
 class PreparedCall:
@@ -315,7 +317,7 @@ def pa_attend_plan_info(k_cache, num_q_heads: int, h_seq_lens, h_q_lens, partiti
 def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
                    out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
                    mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
-                   reuse_plan: bool = False, noalloc: bool = False) -> PreparedCall:
+                   reuse_plan: bool = False, noalloc: bool = False, side=None) -> PreparedCall:
     """``pa_attend`` as a prepared call (arguments as for ``pa_attend``; the
     output tensor is the call's ``keep[0]``).  ``h_seq_lens`` and ``h_q_lens``
     are passed by address: when they are int32 numpy arrays they are used in
@@ -346,7 +348,7 @@ def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_le
         _need(out, "out", _act_dtype(desc), 3)
         if out.shape != q.shape:
             raise ValueError("out must match q")
-    opts = _opts(partition_tokens, mfma_min_rows, events, window, reuse_plan)
+    opts = _opts(partition_tokens, mfma_min_rows, events, window, reuse_plan, side)
     if noalloc:
         if workspace is not None:
             raise ValueError("pa_attend_noalloc takes no workspace")
@@ -371,7 +373,7 @@ def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_le
 def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
               out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
               mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
-              reuse_plan: bool = False) -> torch.Tensor:
+              reuse_plan: bool = False, side=None) -> torch.Tensor:
     """Paged attention of the packed batch ``q [T, Hq, D]``; returns ``out [T, Hq, D]``
     (fp16; bf16 for bf16 pools).
 
@@ -385,7 +387,7 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
     hipEvent_t handles (ints or None) recorded around the two attention kernels."""
     call = prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale, out,
                           workspace, k_scale, v_scale, partition_tokens, mfma_min_rows, events, stream, window,
-                          layer, reuse_plan)
+                          layer, reuse_plan, side=side)
     call()
     return call.keep[0]
 

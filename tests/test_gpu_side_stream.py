@@ -1,0 +1,49 @@
+"""pa_attend's side-stream option ([engine] "02 The engine": one packed
+batch of prefill chunks and decode rows): the row tiles run on a second
+stream beside the decode units.  The same kernels compute the same values,
+so the outputs must equal the single-stream call's bit for bit, and the
+call's work must be complete once the caller's stream reaches it."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from tests.oracle_side import OracleSide, assert_attn_close, dev_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _side():
+    hip = ctypes.CDLL("libamdhip64.so")
+    ev = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(2)) == 0   # timing disabled
+        ev.append(e)
+    s = torch.cuda.Stream()
+    return s, (s.cuda_stream, ev[0].value, ev[1].value)
+
+
+@pytest.mark.parametrize("dt", ["f16", "i8"])
+def test_side_stream_equals_one_stream(dt):
+    from paged_kv_cache_47_amd.workload import DeviceRun
+    rng = np.random.default_rng(61)
+    lens = [int(x) for x in rng.integers(1, 3000, 40)] + [700, 1200, 530]
+    qls = [1] * 40 + [300, 64, 512]
+    w = synthetic.custom(6101, lens, qls, 32, 8, 128, dt)
+    run, ora = DeviceRun(w), OracleSide(w)
+    x = run.prepare(0)
+    slots, copies = ora.reserve(0)
+    run.write(x)
+    ora.write(0, slots, copies)
+    ref = ora.attend(0)
+    keep, side = _side()
+    for opts in ({}, {"partition_tokens": 128}):
+        want = run.attend(x, **opts).clone()
+        got = run.attend(x, side=side, **opts)
+        # the caller's stream alone orders what follows: read on it without a device-wide sync
+        host = got.to("cpu", non_blocking=False)
+        assert torch.equal(host, want.cpu()), opts
+        assert_attn_close(dev_np(got), ref, dt, f"side stream {opts}")
