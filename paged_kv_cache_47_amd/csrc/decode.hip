@@ -551,7 +551,8 @@ static hipError_t decode_g(const AttnArgs& a, int g, int n, hipStream_t s) {
     case 1: decode_kernel<D, 1, KV, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
     case 2: decode_kernel<D, 2, KV, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
     case 4: decode_kernel<D, 4, KV, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
-    case 8: decode_kernel<D, 8, KV, PA_DECODE_NW, kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
+    // int8 with eight rows: 8-byte loads, so the accumulators (G x elements per lane) fit two waves per SIMD
+    case 8: decode_kernel<D, 8, KV, PA_DECODE_NW, KV == kKvI8 ? 8 : kVB><<<grid, PA_DECODE_NW * 64, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
