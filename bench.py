@@ -192,6 +192,56 @@ def unique_kv_bytes(w, tables, L, Q) -> int:
     return sum(valid.values()) * w.num_kv_heads * w.head_dim * 2 * eb
 
 
+def hbm_ceilings(pool_bytes: int = 4 << 30, reps: int = 5, rounds: int = 3) -> dict:
+    """What HBM delivers to plain reads on this GPU (pa_ceiling.h): a 4 GiB
+    buffer read front to back (the best of four grid sizes), and the same
+    buffer as two pools of 4 KiB K and V tiles read in a seeded random
+    order, 16 or 64 pairs per wave with one or two more in flight (the
+    decode kernel's access pattern at 256- and 1024-token partitions), the
+    best of each.  Best of ``rounds`` timings of ``reps`` launches each, from
+    events on the launching stream."""
+    import torch
+    from paged_kv_cache_47_amd import pa
+
+    buf = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    half = pool_bytes // 2
+    k_tiles, v_tiles = buf[:half], buf[half:]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(47)
+    ids = torch.randperm(half // 4096, generator=g).to(torch.int32).cuda()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best_gbs(launch, nbytes):
+        for _ in range(2):
+            launch()
+        best = 0.0
+        for _ in range(rounds):
+            a.record()
+            for _ in range(reps):
+                launch()
+            b.record()
+            b.synchronize()
+            best = max(best, nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9)
+        return best
+
+    stream = {wg: best_gbs(lambda wg=wg: pa.pa_ceiling_stream_read(buf, sink, workgroups=wg), pool_bytes)
+              for wg in (2048, 8192, 32768, 65536)}
+    gather = {(n, d): best_gbs(lambda n=n, d=d: pa.pa_ceiling_gather(k_tiles, v_tiles, ids, sink, ids_per_wave=n,
+                                                                     depth=d), pool_bytes)
+              for n in (16, 64) for d in (1, 2)}
+    del buf
+    top, gtop = max(stream.values()), max(gather.values())
+    return {"stream_read_gbs": round(top, 1), "stream_read_frac": round(top / PEAK_HBM_GBS, 4),
+            "stream_read_by_workgroups": {str(k): round(v, 1) for k, v in stream.items()},
+            "tile_gather_gbs": round(gtop, 1), "tile_gather_frac": round(gtop / PEAK_HBM_GBS, 4),
+            "tile_gather_by_pairs_per_wave_and_depth": {f"{n}/{d}": round(v, 1) for (n, d), v in gather.items()},
+            "note": "pa_ceiling_stream_read over 4 GiB (best grid); pa_ceiling_gather over 2 x 2 GiB of 4 KiB "
+                    "K/V tiles in a seeded random order, 16 or 64 pairs per wave, 1 or 2 more in flight (best); "
+                    "best of 3 x 5 launches each"}
+
+
 def cpu_baseline(w, step: int, budget_s: float):
     """The oracle (gather through the block table + fp64 attention) on the
     first sequences of the same step, until ``budget_s`` of CPU time."""
@@ -522,6 +572,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", type=int, default=3, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the HBM read ceilings (stream read, random 4 KiB tile gather) in the JSON line")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--cold", type=int, default=-1, choices=(-1, 0, 1),
                     help="also time steps after a 1 GiB scratch write that evicts the 256 MB MALL "
@@ -545,6 +597,8 @@ def main(argv=None) -> int:
                          "matrix-core decode kernel)")
     ap.add_argument("--w5-pool", default="i8", choices=("i8", "f16", "bf16"),
                     help="workload 5: the pool type of the same packed batch (f16/bf16: N(0,1) contents in place)")
+    ap.add_argument("--w5-q-heads", type=int, default=32, choices=(32, 64),
+                    help="workload 5: query heads over the 8 KV heads (64: groups of eight)")
     ap.add_argument("--w5-chunks-only", action="store_true",
                     help="workload 5: the 8 prefill chunks alone (no decode sequences): the MFMA kernel by itself")
     ap.add_argument("--no-share", action="store_true",
@@ -576,7 +630,8 @@ def main(argv=None) -> int:
         return 0
     if args.summarize_trace:
         import synthetic
-        w = (synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192)
+        w = (synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192,
+                              num_q_heads=args.w5_q_heads)
              if args.workload == 5 else synthetic.CONFIGS[args.workload]())
         w.window = args.window
         L, Q = _step_lengths(w, 1 if args.workload == 2 else 0)
@@ -611,13 +666,14 @@ def main(argv=None) -> int:
     if args.kv_dtype == "i8" and args.workload != 6:
         print("--kv-dtype i8 applies to workload 6 (workload 5 is the int8 kernel workload)", file=sys.stderr)
         return 2
-    if (args.w5_pool != "i8" or args.w5_chunks_only) and args.workload != 5:
-        print("--w5-pool and --w5-chunks-only apply to workload 5 only", file=sys.stderr)
+    if (args.w5_pool != "i8" or args.w5_chunks_only or args.w5_q_heads != 32) and args.workload != 5:
+        print("--w5-pool, --w5-q-heads and --w5-chunks-only apply to workload 5 only", file=sys.stderr)
         return 2
     if args.workload == 4 and args.no_share:
         w = synthetic.config4(share=False)
     elif args.workload == 5:
-        w = synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192)
+        w = synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192,
+                              num_q_heads=args.w5_q_heads)
     elif args.workload == 2:
         w = synthetic.config2(num_layers=args.layers, kv_dtype=args.kv_dtype)
     elif args.workload == 3:
@@ -788,6 +844,7 @@ def main(argv=None) -> int:
                       if w.num_layers > 1 else "")
                    + (" [bf16 KV, queries and outputs]" if w.kv_dtype == "bf16" else "")
                    + (f" [{args.w3_q_heads} query heads]" if args.w3_q_heads != 32 else "")
+                   + (f" [{args.w5_q_heads} query heads]" if args.w5_q_heads != 32 else "")
                    + (" [row tiles on a side stream]" if args.side_stream else "")
                    + (f" [{args.w5_pool} pool with N(0,1) contents]" if args.w5_pool != "i8" else "")
                    + (" [the 8 prefill chunks only]" if args.w5_chunks_only else ""),
@@ -812,6 +869,11 @@ def main(argv=None) -> int:
         res["value_unique"] = round(ub / (ms * 1e-3) / 1e9, 2)
         res["pct_of_peak"] = round(100 * ub / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)   # of unique bytes
         res["config"]["shared_prefix"] = not args.no_share
+    if not args.no_ceilings:
+        c = hbm_ceilings()
+        if roof and roof[0]["bound"] == "hbm":
+            c["roofline_over_tile_gather"] = round(roof[0]["achieved"] / c["tile_gather_gbs"], 4)
+        res["hbm_ceilings"] = c
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, step_index, args.cpu_budget)
     print(json.dumps(res), flush=True)

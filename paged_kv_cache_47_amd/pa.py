@@ -107,6 +107,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.pa_check_attend.restype = ctypes.c_int
     lib.pa_check_copy.argtypes = [pdesc, vp, i32, vp, vp]
     lib.pa_check_copy.restype = ctypes.c_int
+    lib.pa_ceiling_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.pa_ceiling_stream_read.restype = ctypes.c_int
+    lib.pa_ceiling_gather.argtypes = [vp, vp, ctypes.c_int64, vp, ctypes.c_int64, i32, i32, vp, vp]
+    lib.pa_ceiling_gather.restype = ctypes.c_int
     return lib
 
 
@@ -427,3 +431,27 @@ def prepare_copy_blocks(k_cache, v_cache, src_dst, k_scale=None, v_scale=None, s
 def pa_copy_blocks(k_cache, v_cache, src_dst, k_scale=None, v_scale=None, stream=None) -> None:
     """Copy whole blocks (every layer and head) for copy-on-write: ``src_dst [n, 2]`` int32 (src, dst) pairs."""
     prepare_copy_blocks(k_cache, v_cache, src_dst, k_scale, v_scale, stream)()
+
+
+def pa_ceiling_stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, stream=None) -> None:
+    """Read every byte of ``buf`` once (pa_ceiling.h); enqueue only."""
+    lib = load_library()
+    if not buf.is_contiguous():
+        raise PagedAttentionError("buf must be contiguous")
+    _check(lib.pa_ceiling_stream_read(_ptr(buf), buf.numel() * buf.element_size(), workgroups, _ptr(sink),
+                                      _stream(stream)), "pa_ceiling_stream_read")
+
+
+def pa_ceiling_gather(k_tiles: torch.Tensor, v_tiles: torch.Tensor, tile_ids: torch.Tensor, sink: torch.Tensor,
+                      ids_per_wave: int = 16, depth: int = 2, stream=None) -> None:
+    """Read the 4 KiB K and V tiles ``tile_ids`` names (pa_ceiling.h);
+    enqueue only.  ``k_tiles``/``v_tiles``: contiguous, a whole number of
+    4 KiB tiles, the same size."""
+    lib = load_library()
+    nbytes = k_tiles.numel() * k_tiles.element_size()
+    if (not k_tiles.is_contiguous() or not v_tiles.is_contiguous() or nbytes % 4096
+            or v_tiles.numel() * v_tiles.element_size() != nbytes):
+        raise PagedAttentionError("k_tiles and v_tiles must be contiguous, equal, whole 4 KiB tiles")
+    _need(tile_ids, "tile_ids", torch.int32, 1)
+    _check(lib.pa_ceiling_gather(_ptr(k_tiles), _ptr(v_tiles), nbytes // 4096, _ptr(tile_ids), tile_ids.shape[0],
+                                 ids_per_wave, depth, _ptr(sink), _stream(stream)), "pa_ceiling_gather")

@@ -250,3 +250,28 @@ def test_plan_info_for_groups_of_16_and_32():
     assert i32["vector_rows"] == 8 and i32["mfma_tiles"] == 0 and i32["plan_free"] == 1
     forced = pa.pa_attend_plan_info(pool, 64, [100, 300], [1, 3], mfma_min_rows=1)
     assert forced["vector_rows"] == 0 and forced["mfma_tiles"] == 2
+
+
+def test_ceiling_calls_refuse_bad_arguments_on_the_host():
+    """The HBM-ceiling reads (pa_ceiling.h) check their sizes and alignment
+    before any device work: nothing here has a GPU, so every call below must
+    be refused on the host."""
+    lib = pa.load_library()
+    fake, sink = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
+    assert lib.pa_ceiling_stream_read(None, 4096, 0, sink, None) == 1
+    assert lib.pa_ceiling_stream_read(fake, 4096, 0, None, None) == 1
+    assert lib.pa_ceiling_stream_read(fake, 0, 0, sink, None) == 2
+    assert lib.pa_ceiling_stream_read(fake, 4100, 0, sink, None) == 2          # not whole 16-byte words
+    assert lib.pa_ceiling_stream_read(ctypes.c_void_p(4104), 4096, 0, sink, None) == 2
+    assert lib.pa_ceiling_stream_read(fake, 4096, -1, sink, None) == 2
+    assert lib.pa_ceiling_stream_read(fake, 4096, 65537, sink, None) == 2
+    ids = ctypes.c_void_p(12288)
+    assert lib.pa_ceiling_gather(None, fake, 4, ids, 4, 16, 2, sink, None) == 1
+    assert lib.pa_ceiling_gather(fake, fake, 4, None, 4, 16, 2, sink, None) == 1
+    assert lib.pa_ceiling_gather(fake, fake, 0, ids, 4, 16, 2, sink, None) == 2
+    assert lib.pa_ceiling_gather(fake, fake, (1 << 28) + 1, ids, 4, 16, 2, sink, None) == 2
+    assert lib.pa_ceiling_gather(fake, fake, 4, ids, 0, 16, 2, sink, None) == 2
+    assert lib.pa_ceiling_gather(fake, fake, 4, ids, 4, 0, 2, sink, None) == 2
+    assert lib.pa_ceiling_gather(fake, fake, 4, ids, 4, 16, 3, sink, None) == 2
+    assert lib.pa_ceiling_gather(ctypes.c_void_p(4100), fake, 4, ids, 4, 16, 2, sink, None) == 2
+    assert lib.pa_ceiling_gather(fake, fake, 4, ids, 1 << 40, 1, 2, sink, None) == 2   # grid beyond 2^31
