@@ -111,7 +111,7 @@ class SideStream:
 
 
 # the sources of the vector-path kernel whose HBM traffic the PMC summary records
-DECODE_SOURCES = ("decode.hip", "pa_internal.h")
+DECODE_SOURCES = ("decode.hip", "pa_internal.h", "units.h")
 
 
 def source_hash() -> str:

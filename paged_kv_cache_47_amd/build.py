@@ -33,6 +33,9 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
+    # a lambda parameter that shadows a local of the kernel around it has sent
+    # a load to the wrong address: refuse such shadowing outright
+    "-Werror=shadow-all",
 ]
 
 
