@@ -244,13 +244,15 @@ static pa_status check_heads(const pa_cache_desc* d, int32_t hq) {
 // Largest split-K partition when the caller leaves it to the library (a row
 // is then split into equal parts of at most this many keys): aim
 // for about 16 workgroups per compute unit over the whole vector path, but
-// give every partition at least 768 KB of K and V (1536 keys of fp16 at head
-// dim 128): below that the partial outputs and the merge kernel cost more
-// than the extra parallelism gains (measured on batches of 1k-key rows and
-// on 32-sequence decode steps); at most 4096 keys.
+// give every partition at least 1 MiB of K and V (2048 keys of fp16 at head
+// dim 128): each unit pays for filling and draining its waves' load
+// pipelines, its merge and its partials, which shorter units amortise worse
+// (256 decode rows of 1-4096 keys: 1536-key units 0.365 ms, 2048-3072 keys
+// 0.360 ms; 1k-key rows and 32-sequence decode steps also lose to smaller
+// units); at most 4096 keys.
 static int32_t auto_part(int64_t total_keys, int32_t hkv, int32_t head_dim, int32_t elem_bytes) {
   const int64_t target_units = 256 * 16;
-  const int64_t min_keys = (int64_t)(768 << 10) / (2 * head_dim * elem_bytes);
+  const int64_t min_keys = (int64_t)(1 << 20) / (2 * head_dim * elem_bytes);
   int64_t p = std::max(total_keys * hkv / target_units, min_keys);
   p = (p + 255) / 256 * 256;
   return (int32_t)std::min<int64_t>(4096, p);

@@ -206,11 +206,11 @@ def test_fixed_partition_keeps_the_workspace_within_the_bound():
     batch needs more workspace than the bound; the automatic choice alone can
     (a smaller key total picks a smaller partition)."""
     pool = _meta_pool(64, 8, 128)
-    S, W = 256, 3200
+    S, W = 256, 6400
     bound = pa.pa_attend_plan_info(pool, 32, [W] * S, [1] * S)
     part = bound["partition_tokens"]
     assert part > 0 and bound["workspace_bytes"] > 0
-    mixed = [3100] * 170 + [16] * 86
+    mixed = [6300] * 170 + [16] * 86
     assert pa.pa_attend_workspace_bytes(pool, 32, mixed, [1] * S) > bound["workspace_bytes"]
     rng = np.random.default_rng(5)
     for _ in range(50):
