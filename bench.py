@@ -630,9 +630,13 @@ def main(argv=None) -> int:
         return 0
     if args.summarize_trace:
         import synthetic
-        w = (synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192,
-                              num_q_heads=args.w5_q_heads)
-             if args.workload == 5 else synthetic.CONFIGS[args.workload]())
+        if args.workload == 5:
+            w = synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192,
+                                  num_q_heads=args.w5_q_heads)
+        elif args.workload == 3:
+            w = synthetic.config3(kv_dtype=args.kv_dtype, num_q_heads=args.w3_q_heads)
+        else:
+            w = synthetic.CONFIGS[args.workload]()
         w.window = args.window
         L, Q = _step_lengths(w, 1 if args.workload == 2 else 0)
         vb, mf, _ = work_split(w, L, Q)
