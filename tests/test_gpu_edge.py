@@ -28,6 +28,7 @@ def _run(w):
 @pytest.mark.parametrize("hq,hkv,d,dt", [
     (8, 1, 128, "f16"), (16, 2, 128, "f16"), (8, 4, 64, "f16"), (4, 4, 128, "f16"),
     (4, 4, 64, "i8"), (16, 2, 64, "i8"), (8, 8, 128, "i8"), (32, 8, 128, "i8"),
+    (16, 2, 128, "i8"),   # int8 groups of eight at head dim 128: K read four lanes per token row
 ])
 def test_shapes_and_groups(hq, hkv, d, dt):
     w = synthetic.custom(101 + hq + d, LENS, QLS, hq, hkv, d, dt)

@@ -45,6 +45,7 @@ def test_window_mixed_batch_int8(window):
 
 @pytest.mark.parametrize("hq,hkv,d,dt,window", [
     (12, 12, 64, "f16", 33), (32, 4, 128, "f16", 129), (16, 2, 64, "i8", 48), (8, 1, 128, "f16", 16),
+    (16, 2, 128, "i8", 17), (64, 8, 128, "i8", 100),   # int8 groups of eight at head dim 128 (quad K layout)
 ])
 def test_window_groups_and_head_dims(hq, hkv, d, dt, window):
     w = synthetic.custom(400 + window, LENS, QLS, hq, hkv, d, dt, window=window)
