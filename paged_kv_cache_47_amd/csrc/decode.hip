@@ -250,7 +250,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   auto process = [&](Dw<ND>* kr, Dw<ND>* vr, const uint16_t kq, const uint16_t vq, const int blk) {
     float ksc = a.scale_log2, vsc = 1.f;
     if constexpr (I8) {
-      ksc *= half_bits_to_float(kq);
+      // a zero K scale (a block whose K rows are all zero) becomes the least
+      // normal float: its scores stay 0 and masked ones stay -inf, not -inf * 0
+      ksc = fmaxf(ksc * half_bits_to_float(kq), 1.17549435e-38f);
       vsc = half_bits_to_float(vq);
     }
     const int tok0 = blk * kBlockSize + grp;

@@ -133,7 +133,9 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
         const uint2 hi = *(const uint2*)(kt + l16 * D + (2 * j + 1) * 32 + 8 * grp);
         tl.k[j] = (u32x4_t){lo.x, lo.y, hi.x, hi.y};
       }
-      tl.ksc = a.scale_log2 * bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(ks_rs, (int)(tile * 2), 0, 0));
+      // a zero K scale becomes the least normal float: masked scores stay -inf, not -inf * 0
+      tl.ksc = fmaxf(a.scale_log2 * bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(ks_rs, (int)(tile * 2), 0, 0)),
+                     1.17549435e-38f);
       tl.vsc = bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(vs_rs, (int)(tile * 2), 0, 0));
     } else {
 #pragma unroll

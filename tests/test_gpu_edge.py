@@ -298,3 +298,23 @@ def test_decode_of_length_one_is_v0():
     v = w.step(0).new_v
     assert np.array_equal(out, np.repeat(v, 4, axis=1))
     ora.reserve(0)
+
+
+@pytest.mark.parametrize("hq", [8, 16, 32])
+def test_int8_block_with_zero_key_scale(hq):
+    # A block whose written K rows are all exactly zero gets a zero K scale ([engine] "INT8 KV
+    # cache design": scale = max |x| / 127, zero codes).  Here each chosen sequence's new token
+    # opens a block, so that block holds one visible key with a zero scale and 15 masked slots:
+    # the masked scores must stay -inf (not -inf * 0) on the vector path, the eight-row quad layout
+    # and the matrix-core decode alike, and the outputs must match the oracle.
+    lens = [17, 33, 161, 49, 1, 400, 65, 2]
+    w = synthetic.custom(77 + hq, lens, [1] * len(lens), hq, 2, 128, "i8")
+    st = w.step(0)
+    for i, L in enumerate(lens):
+        if (L - 1) % 16 == 0:                 # the new token is the first of its block
+            st.new_k[i] = 0
+    run = _run(w)
+    x = _check_step(run, OracleSide(w), 0, SPLITS + ({"mfma_min_rows": 1}, {"mfma_min_rows": 2 ** 31 - 1}))
+    tab = x.batch.block_tables
+    zero = [int(tab[i][(L - 1) // 16]) for i, L in enumerate(lens) if (L - 1) % 16 == 0]
+    assert len(zero) == 6 and (run.k_scale[zero].float() == 0).all()
