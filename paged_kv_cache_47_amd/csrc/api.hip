@@ -249,10 +249,12 @@ static pa_status check_heads(const pa_cache_desc* d, int32_t hq) {
 // pipelines, its merge and its partials, which shorter units amortise worse
 // (256 decode rows of 1-4096 keys: 1536-key units 0.365 ms, 2048-3072 keys
 // 0.360 ms; 1k-key rows and 32-sequence decode steps also lose to smaller
-// units); at most 4096 keys.
-static int32_t auto_part(int64_t total_keys, int32_t hkv, int32_t head_dim, int32_t elem_bytes) {
+// units); twice that with groups of 16 or 32, whose units merge and write 4-8
+// times the rows (the same rows unsplit: 0.444 -> 0.429 ms at G = 16, 0.486 ->
+// 0.465 ms at G = 32); at most 4096 keys.
+static int32_t auto_part(int64_t total_keys, int32_t hkv, int32_t head_dim, int32_t elem_bytes, int32_t group) {
   const int64_t target_units = 256 * 16;
-  const int64_t min_keys = (int64_t)(1 << 20) / (2 * head_dim * elem_bytes);
+  const int64_t min_keys = (int64_t)(group >= 16 ? 2 << 20 : 1 << 20) / (2 * head_dim * elem_bytes);
   int64_t p = std::max(total_keys * hkv / target_units, min_keys);
   p = (p + 255) / 256 * 256;
   return (int32_t)std::min<int64_t>(4096, p);
@@ -287,7 +289,7 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   P.total_q = (int32_t)total_q;
   P.part = req_part > 0 ? req_part
                        : (req_part < 0 ? 0 : auto_part(vec_keys, d->num_kv_heads, d->head_dim,
-                                                       d->kv_dtype == PA_KV_I8 ? 1 : 2));
+                                                       d->kv_dtype == PA_KV_I8 ? 1 : 2, g));
   for (int i = 0; i < num_seqs; ++i) {
     const int L = hL[i], Q = hQ[i];
     if (Q > 0 && (int64_t)Q * g >= P.min_rows) {

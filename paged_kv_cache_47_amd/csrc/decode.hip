@@ -637,6 +637,38 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
     parts = vt.parts;
     row0 = (int64_t)(si.q_start + vt.t) * a.hq + (int64_t)h * G;
   }
+  // Up to kMaxParts partials: the weights 2^(lse_p - M) / sum_p 2^(lse_p - M)
+  // of each query head are formed once in LDS, and every output element is a
+  // plain weighted sum of its partials (the element loop below otherwise
+  // re-reads the log-sum-exps of every partial for each of the G * D elements).
+  constexpr int kMaxParts = 64;
+  __shared__ float wsh[G][kMaxParts];
+  if (parts <= kMaxParts) {
+    for (int i = threadIdx.x; i < G * parts; i += 256)
+      wsh[i / parts][i % parts] = a.plse[(int64_t)(u0 + i % parts) * a.hq + (int64_t)h * G + i / parts];
+    __syncthreads();
+    if (threadIdx.x < G) {
+      float* w = wsh[threadIdx.x];
+      float M = -__builtin_inff();
+      for (int p = 0; p < parts; ++p) M = fmaxf(M, w[p]);
+      float S = 0.f;
+      for (int p = 0; p < parts; ++p) {
+        w[p] = fast_exp2(w[p] - M);
+        S += w[p];
+      }
+      const float inv = 1.f / S;
+      for (int p = 0; p < parts; ++p) w[p] *= inv;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+      const int g = idx / D, d = idx % D;
+      const float* po = a.po + ((int64_t)u0 * a.hq + (int64_t)h * G + g) * D + d;
+      float O = 0.f;
+      for (int p = 0; p < parts; ++p) O = fmaf(wsh[g][p], po[(int64_t)p * a.hq * D], O);
+      ((OUT*)a.out)[(row0 + g) * D + d] = (OUT)O;
+    }
+    return;
+  }
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int g = idx / D, d = idx % D;
     const int64_t col = (int64_t)h * G + g;
