@@ -646,7 +646,7 @@ def main(argv=None) -> int:
                         0 if mfma else vb, mf if mfma else 0, args.summary_kernel)
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
     if args.workload == 6:

@@ -181,7 +181,7 @@ static pa_status debug_status_ptr(int32_t** out) {
 }
 
 // Waits for the checks just enqueued and turns a violation into a status.
-static pa_status debug_verdict(int32_t* st, hipStream_t s) {
+static pa_status debug_outcome(int32_t* st, hipStream_t s) {
   int32_t h[4] = {0, 0, 0, 0};
   if (hipMemcpyAsync(h, st, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess) return PA_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_HIP;
@@ -193,7 +193,7 @@ pa_status debug_check_write(const pa_cache_desc& d, const int32_t* slots, int32_
   pa_status r = debug_status_ptr(&st);
   if (r != PA_OK) return r;
   if (launch_check_write(d, slots, T, st, s) != hipSuccess) return PA_ERR_HIP;
-  return debug_verdict(st, s);
+  return debug_outcome(st, s);
 }
 
 pa_status debug_check_attend(const pa_cache_desc& d, const int32_t* tables, int32_t max_blocks,
@@ -204,7 +204,7 @@ pa_status debug_check_attend(const pa_cache_desc& d, const int32_t* tables, int3
   if (r != PA_OK) return r;
   if (launch_check_attend(d, tables, max_blocks, seq_lens, q_lens, num_seqs, hL, hQ, window, st, s) != hipSuccess)
     return PA_ERR_HIP;
-  return debug_verdict(st, s);
+  return debug_outcome(st, s);
 }
 
 pa_status debug_check_copy(const pa_cache_desc& d, const int32_t* pairs, int32_t n, hipStream_t s) {
@@ -212,7 +212,7 @@ pa_status debug_check_copy(const pa_cache_desc& d, const int32_t* pairs, int32_t
   pa_status r = debug_status_ptr(&st);
   if (r != PA_OK) return r;
   if (launch_check_copy(d, pairs, n, st, s) != hipSuccess) return PA_ERR_HIP;
-  return debug_verdict(st, s);
+  return debug_outcome(st, s);
 }
 #endif
 
