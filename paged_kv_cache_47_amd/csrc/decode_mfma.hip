@@ -29,6 +29,9 @@
 namespace pa {
 
 constexpr int kMfmaDecodeWaves = 4;
+#ifndef PA_MFD_DEPTH
+#define PA_MFD_DEPTH 2   // tiles in flight per wave while one is processed (groups of 16: 1 or 2)
+#endif
 
 __device__ __forceinline__ float bits_to_float(uint16_t b) { return (float)__builtin_bit_cast(half_t, b); }
 
@@ -59,6 +62,7 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
   // 2^6.5 * 516 < 65504 keeps them finite.
   constexpr float kThr = I8 ? 6.5f : 8.0f;
   static_assert(G == 16 || G == 32, "groups of 16 or 32");
+  constexpr bool DEPTH2 = G == 16 && PA_MFD_DEPTH == 2;
 
   __shared__ __attribute__((aligned(16))) half_t vtile[NW][2][kBlockSize * LDV];
   __shared__ float sm[NW][G];
@@ -248,22 +252,44 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
     __builtin_amdgcn_wave_barrier();   // the reads of this tile precede the next write to it
   };
 
-  // the wave's blocks in turn, the next block's tile in flight while one is processed (a third
-  // tile in flight measured no faster at G = 16)
+  // the wave's blocks in turn, the next block's tile in flight while one is
+  // processed; with 16 rows two tiles in flight (a three-tile ring)
   int b = un.kbeg / kBlockSize + wave;
-  Tile ta, tb;
   int vb = 0;
-  if (b < bend) load_tile(b, ta);
-  while (b < bend) {
+  if constexpr (DEPTH2) {
+    Tile ta, tb, tc;
+    if (b < bend) load_tile(b, ta);
     if (b + NW < bend) load_tile(b + NW, tb);
-    process(ta, b, vb);
-    b += NW;
-    vb ^= 1;
-    if (b >= bend) break;
-    if (b + NW < bend) load_tile(b + NW, ta);
-    process(tb, b, vb);
-    b += NW;
-    vb ^= 1;
+    while (b < bend) {
+      if (b + 2 * NW < bend) load_tile(b + 2 * NW, tc);
+      process(ta, b, vb);
+      b += NW;
+      vb ^= 1;
+      if (b >= bend) break;
+      if (b + 2 * NW < bend) load_tile(b + 2 * NW, ta);
+      process(tb, b, vb);
+      b += NW;
+      vb ^= 1;
+      if (b >= bend) break;
+      if (b + 2 * NW < bend) load_tile(b + 2 * NW, tb);
+      process(tc, b, vb);
+      b += NW;
+      vb ^= 1;
+    }
+  } else {
+    Tile ta, tb;
+    if (b < bend) load_tile(b, ta);
+    while (b < bend) {
+      if (b + NW < bend) load_tile(b + NW, tb);
+      process(ta, b, vb);
+      b += NW;
+      vb ^= 1;
+      if (b >= bend) break;
+      if (b + NW < bend) load_tile(b + NW, ta);
+      process(tb, b, vb);
+      b += NW;
+      vb ^= 1;
+    }
   }
 
   // row sums over the row's four lanes, then the waves merged in turn through LDS
