@@ -66,7 +66,10 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
 
   __shared__ __attribute__((aligned(16))) half_t vtile[NW][2][kBlockSize * LDV];
   __shared__ float sm[NW][G];
-  __shared__ float sacc[G * D];
+  // merge buffer of the waves' accumulators; rows padded by 4 floats so the 16
+  // rows a column tile writes at once fall on different LDS banks
+  constexpr int LDA = D + 4;
+  __shared__ float sacc[G * LDA];
   __shared__ float ssum[G];
 
   const int h = blockIdx.y;
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float* dst = &sacc[row * D + nt * 16 + 4 * grp + e];
+            float* dst = &sacc[row * LDA + nt * 16 + 4 * grp + e];
             *dst = (w == 0 ? 0.f : *dst) + o[rb][nt][e] * f[rb];
           }
         if (grp == 0) ssum[row] = (w == 0 ? 0.f : ssum[row]) + lsum[rb] * f[rb];
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
     float M = sm[0][g];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, sm[w][g]);
-    const float L = ssum[g], O = sacc[idx];
+    const float L = ssum[g], O = sacc[g * LDA + d];
     if (!split) {
       ((act_t*)a.out)[(row0 + g) * D + d] = (act_t)(O / L);
     } else {
