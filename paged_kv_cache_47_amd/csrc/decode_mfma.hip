@@ -29,6 +29,17 @@
 namespace pa {
 
 constexpr int kMfmaDecodeWaves = 4;
+#ifndef PA_MFD_NTV
+#define PA_MFD_NTV 1   // V tile loads (whole 128-byte lines per instruction) with the nontemporal hint
+#endif
+#ifndef PA_MFD_NTK
+#define PA_MFD_NTK 0   // K tile loads (half lines per instruction, the other half read by the next) likewise
+#endif
+template <typename T>
+__device__ __forceinline__ T ldk(const char* p) {
+  if constexpr (PA_MFD_NTK) return __builtin_nontemporal_load((const T*)p);
+  else return *(const T*)p;
+}
 #ifndef PA_MFD_DEPTH
 #define PA_MFD_DEPTH 2   // tiles in flight per wave while one is processed (groups of 16: 1 or 2)
 #endif
@@ -136,8 +147,9 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
       // codes of key l16, dims 32 * ks + 8 * grp + [0, 8): 8 bytes per k-step, two k-steps per register quad
 #pragma unroll
       for (int j = 0; j < KS / 2; ++j) {
-        const uint2 lo = *(const uint2*)(kt + l16 * D + (2 * j) * 32 + 8 * grp);
-        const uint2 hi = *(const uint2*)(kt + l16 * D + (2 * j + 1) * 32 + 8 * grp);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t lo = ldk<u32x2_t>(kt + l16 * D + (2 * j) * 32 + 8 * grp);
+        const u32x2_t hi = ldk<u32x2_t>(kt + l16 * D + (2 * j + 1) * 32 + 8 * grp);
         tl.k[j] = (u32x4_t){lo.x, lo.y, hi.x, hi.y};
       }
       // a zero K scale becomes the least normal float: masked scores stay -inf, not -inf * 0
@@ -146,12 +158,15 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
       tl.vsc = bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(vs_rs, (int)(tile * 2), 0, 0));
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) tl.k[ks] = *(const u32x4_t*)(kt + (l16 * D + ks * 32 + 8 * grp) * 2);
+      for (int ks = 0; ks < KS; ++ks) tl.k[ks] = ldk<u32x4_t>(kt + (l16 * D + ks * 32 + 8 * grp) * 2);
       tl.ksc = a.scale_log2;
       tl.vsc = 1.f;
     }
 #pragma unroll
-    for (int i = 0; i < VL; ++i) tl.v[i] = *(const u32x4_t*)(vt + (i * 64 + lane) * 16);
+    for (int i = 0; i < VL; ++i) {
+      const u32x4_t* vp = (const u32x4_t*)(vt + (i * 64 + lane) * 16);
+      tl.v[i] = PA_MFD_NTV ? __builtin_nontemporal_load(vp) : *vp;
+    }
   };
 
   auto process = [&](const Tile& tl, int blk, int vb) {
