@@ -35,6 +35,9 @@ constexpr int kMfmaDecodeWaves = 4;
 #ifndef PA_MFD_NTK
 #define PA_MFD_NTK 0   // K tile loads (half lines per instruction, the other half read by the next) likewise
 #endif
+#ifndef PA_MFD_KLDS
+#define PA_MFD_KLDS 1  // 16-bit pools: K loaded like V (whole lines, nontemporal) and read as operands from LDS
+#endif
 template <typename T>
 __device__ __forceinline__ T ldk(const char* p) {
   if constexpr (PA_MFD_NTK) return __builtin_nontemporal_load((const T*)p);
@@ -74,8 +77,16 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
   constexpr float kThr = I8 ? 6.5f : 8.0f;
   static_assert(G == 16 || G == 32, "groups of 16 or 32");
   constexpr bool DEPTH2 = G == 16 && PA_MFD_DEPTH == 2;
+  // 16-bit pools: K rows are loaded whole (like V, every instruction covering
+  // whole 128-byte lines, nontemporal) and staged through a per-wave LDS tile
+  // from which the A operands are read; loading them straight into the
+  // operand layout reads half lines per instruction.
+  constexpr bool KLDS = !I8 && PA_MFD_KLDS;
+  constexpr int LDK = D + 8;   // LDS row stride of a K tile (halves): conflict-free operand reads
 
-  __shared__ __attribute__((aligned(16))) half_t vtile[NW][2][kBlockSize * LDV];
+  // one V (and K) tile per wave: a wave's LDS accesses stay in program order
+  __shared__ __attribute__((aligned(16))) half_t vtile[NW][kBlockSize * LDV];
+  __shared__ __attribute__((aligned(16))) half_t ktile[KLDS ? NW : 1][KLDS ? kBlockSize * LDK : 8];
   __shared__ float sm[NW][G];
   // merge buffer of the waves' accumulators; rows padded by 4 floats so the 16
   // rows a column tile writes at once fall on different LDS banks
@@ -129,7 +140,7 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
   // load per k-step; int8: eight codes per k-step), V in its natural layout
   // (chunk c = i * 64 + lane: key c / (D * EB / 16), 16 bytes at (c % (D * EB / 16)) * 16).
   struct Tile {
-    u32x4_t k[I8 ? KS / 2 : KS];
+    u32x4_t k[I8 ? KS / 2 : (KLDS ? VL : KS)];
     u32x4_t v[VL];
     float ksc, vsc;
   };
@@ -156,6 +167,11 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
       tl.ksc = fmaxf(a.scale_log2 * bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(ks_rs, (int)(tile * 2), 0, 0)),
                      1.17549435e-38f);
       tl.vsc = bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(vs_rs, (int)(tile * 2), 0, 0));
+    } else if constexpr (KLDS) {
+#pragma unroll
+      for (int i = 0; i < VL; ++i) tl.k[i] = __builtin_nontemporal_load((const u32x4_t*)(kt + (i * 64 + lane) * 16));
+      tl.ksc = a.scale_log2;
+      tl.vsc = 1.f;
     } else {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) tl.k[ks] = ldk<u32x4_t>(kt + (l16 * D + ks * 32 + 8 * grp) * 2);
@@ -169,9 +185,18 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
     }
   };
 
-  auto process = [&](const Tile& tl, int blk, int vb) {
+  auto process = [&](const Tile& tl, int blk) {
     // V into this wave's LDS tile (fp16 codes for int8), read back transposed below
-    half_t* vd = vtile[wave][vb];
+    half_t* vd = vtile[wave];
+    if constexpr (KLDS) {
+      // K rows into this wave's K tile, read back below as A operands
+      constexpr int CPR = D / 8;
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int c = i * 64 + lane;
+        *(u32x4_t*)(ktile[wave] + (c / CPR) * LDK + (c % CPR) * 8) = tl.k[i];
+      }
+    }
     if constexpr (I8) {
       constexpr int CPR = D / 16;   // 16-code chunks per key row
 #pragma unroll
@@ -206,6 +231,8 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
         const half2_t c0 = sdwa_pair<0, 1>(w0, w0), c1 = sdwa_pair<2, 3>(w0, w0);
         const half2_t c2 = sdwa_pair<0, 1>(w1, w1), c3 = sdwa_pair<2, 3>(w1, w1);
         kop = (half8_t){c0.x, c0.y, c1.x, c1.y, c2.x, c2.y, c3.x, c3.y};
+      } else if constexpr (KLDS) {
+        kop = *(const act8_t*)(ktile[wave] + l16 * LDK + ks * 32 + 8 * grp);
       } else {
         kop = __builtin_bit_cast(act8_t, tl.k[ks]);
       }
@@ -273,40 +300,34 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
   // the wave's blocks in turn, the next block's tile in flight while one is
   // processed; with 16 rows two tiles in flight (a three-tile ring)
   int b = un.kbeg / kBlockSize + wave;
-  int vb = 0;
   if constexpr (DEPTH2) {
     Tile ta, tb, tc;
     if (b < bend) load_tile(b, ta);
     if (b + NW < bend) load_tile(b + NW, tb);
     while (b < bend) {
       if (b + 2 * NW < bend) load_tile(b + 2 * NW, tc);
-      process(ta, b, vb);
+      process(ta, b);
       b += NW;
-      vb ^= 1;
       if (b >= bend) break;
       if (b + 2 * NW < bend) load_tile(b + 2 * NW, ta);
-      process(tb, b, vb);
+      process(tb, b);
       b += NW;
-      vb ^= 1;
       if (b >= bend) break;
       if (b + 2 * NW < bend) load_tile(b + 2 * NW, tb);
-      process(tc, b, vb);
+      process(tc, b);
       b += NW;
-      vb ^= 1;
     }
   } else {
     Tile ta, tb;
     if (b < bend) load_tile(b, ta);
     while (b < bend) {
       if (b + NW < bend) load_tile(b + NW, tb);
-      process(ta, b, vb);
+      process(ta, b);
       b += NW;
-      vb ^= 1;
       if (b >= bend) break;
       if (b + NW < bend) load_tile(b + NW, ta);
-      process(tb, b, vb);
+      process(tb, b);
       b += NW;
-      vb ^= 1;
     }
   }
 
