@@ -597,8 +597,9 @@ def main(argv=None) -> int:
                          "matrix-core decode kernel)")
     ap.add_argument("--w5-pool", default="i8", choices=("i8", "f16", "bf16"),
                     help="workload 5: the pool type of the same packed batch (f16/bf16: N(0,1) contents in place)")
-    ap.add_argument("--w5-q-heads", type=int, default=32, choices=(32, 64),
-                    help="workload 5: query heads over the 8 KV heads (64: groups of eight)")
+    ap.add_argument("--w5-q-heads", type=int, default=32, choices=(32, 64, 128),
+                    help="workload 5: query heads over the 8 KV heads (64: groups of eight; 128: groups of 16, "
+                         "the decode rows on the matrix cores)")
     ap.add_argument("--w5-chunks-only", action="store_true",
                     help="workload 5: the 8 prefill chunks alone (no decode sequences): the MFMA kernel by itself")
     ap.add_argument("--no-share", action="store_true",

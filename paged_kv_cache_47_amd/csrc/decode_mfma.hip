@@ -36,7 +36,7 @@ constexpr int kMfmaDecodeWaves = 4;
 #define PA_MFD_NTK 0   // K tile loads (half lines per instruction, the other half read by the next) likewise
 #endif
 #ifndef PA_MFD_KLDS
-#define PA_MFD_KLDS 1  // 16-bit pools: K loaded like V (whole lines, nontemporal) and read as operands from LDS
+#define PA_MFD_KLDS 1  // K loaded like V (whole lines, nontemporal) and read as operands from LDS
 #endif
 template <typename T>
 __device__ __forceinline__ T ldk(const char* p) {
@@ -77,11 +77,11 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
   constexpr float kThr = I8 ? 6.5f : 8.0f;
   static_assert(G == 16 || G == 32, "groups of 16 or 32");
   constexpr bool DEPTH2 = G == 16 && PA_MFD_DEPTH == 2;
-  // 16-bit pools: K rows are loaded whole (like V, every instruction covering
-  // whole 128-byte lines, nontemporal) and staged through a per-wave LDS tile
-  // from which the A operands are read; loading them straight into the
-  // operand layout reads half lines per instruction.
-  constexpr bool KLDS = !I8 && PA_MFD_KLDS;
+  // K rows are loaded whole (like V, every instruction covering whole 128-byte
+  // lines, nontemporal) and staged through a per-wave LDS tile (int8: as exact
+  // fp16 codes) from which the A operands are read; loading them straight into
+  // the operand layout reads half (int8: quarter) lines per instruction.
+  constexpr bool KLDS = PA_MFD_KLDS;
   constexpr int LDK = D + 8;   // LDS row stride of a K tile (halves): conflict-free operand reads
 
   // one V (and K) tile per wave: a wave's LDS accesses stay in program order
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
   // load per k-step; int8: eight codes per k-step), V in its natural layout
   // (chunk c = i * 64 + lane: key c / (D * EB / 16), 16 bytes at (c % (D * EB / 16)) * 16).
   struct Tile {
-    u32x4_t k[I8 ? KS / 2 : (KLDS ? VL : KS)];
+    u32x4_t k[KLDS ? VL : (I8 ? KS / 2 : KS)];
     u32x4_t v[VL];
     float ksc, vsc;
   };
@@ -154,10 +154,14 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
     const int64_t tile = (int64_t)ph * a.blk_tiles + h;
     const char* kt = (const char*)a.kc + tile * TILE;
     const char* vt = (const char*)a.vc + tile * TILE;
+    if constexpr (KLDS) {
+#pragma unroll
+      for (int i = 0; i < VL; ++i) tl.k[i] = __builtin_nontemporal_load((const u32x4_t*)(kt + (i * 64 + lane) * 16));
+    }
     if constexpr (I8) {
       // codes of key l16, dims 32 * ks + 8 * grp + [0, 8): 8 bytes per k-step, two k-steps per register quad
 #pragma unroll
-      for (int j = 0; j < KS / 2; ++j) {
+      for (int j = 0; j < (KLDS ? 0 : KS / 2); ++j) {
         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
         const u32x2_t lo = ldk<u32x2_t>(kt + l16 * D + (2 * j) * 32 + 8 * grp);
         const u32x2_t hi = ldk<u32x2_t>(kt + l16 * D + (2 * j + 1) * 32 + 8 * grp);
@@ -167,14 +171,9 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
       tl.ksc = fmaxf(a.scale_log2 * bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(ks_rs, (int)(tile * 2), 0, 0)),
                      1.17549435e-38f);
       tl.vsc = bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(vs_rs, (int)(tile * 2), 0, 0));
-    } else if constexpr (KLDS) {
-#pragma unroll
-      for (int i = 0; i < VL; ++i) tl.k[i] = __builtin_nontemporal_load((const u32x4_t*)(kt + (i * 64 + lane) * 16));
-      tl.ksc = a.scale_log2;
-      tl.vsc = 1.f;
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) tl.k[ks] = ldk<u32x4_t>(kt + (l16 * D + ks * 32 + 8 * grp) * 2);
+      for (int ks = 0; ks < (KLDS ? 0 : KS); ++ks) tl.k[ks] = ldk<u32x4_t>(kt + (l16 * D + ks * 32 + 8 * grp) * 2);
       tl.ksc = a.scale_log2;
       tl.vsc = 1.f;
     }
@@ -188,7 +187,22 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
   auto process = [&](const Tile& tl, int blk) {
     // V into this wave's LDS tile (fp16 codes for int8), read back transposed below
     half_t* vd = vtile[wave];
-    if constexpr (KLDS) {
+    if constexpr (KLDS && I8) {
+      // K codes into this wave's K tile as exact fp16, read back below as A operands
+      constexpr int CPR = D / 16;   // 16-code chunks per key row
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int c = i * 64 + lane, key = c / CPR, col = (c % CPR) * 16;
+        const uint32_t w[4] = {tl.k[i][0], tl.k[i][1], tl.k[i][2], tl.k[i][3]};
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const half2_t a0 = sdwa_pair<0, 1>(w[2 * q], w[2 * q]), a1 = sdwa_pair<2, 3>(w[2 * q], w[2 * q]);
+          const half2_t a2 = sdwa_pair<0, 1>(w[2 * q + 1], w[2 * q + 1]);
+          const half2_t a3 = sdwa_pair<2, 3>(w[2 * q + 1], w[2 * q + 1]);
+          *(half8_t*)(ktile[wave] + key * LDK + col + 8 * q) = (half8_t){a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+        }
+      }
+    } else if constexpr (KLDS) {
       // K rows into this wave's K tile, read back below as A operands
       constexpr int CPR = D / 8;
 #pragma unroll
@@ -226,13 +240,13 @@ __global__ __launch_bounds__(64 * kMfmaDecodeWaves) void decode_mfma_kernel(Attn
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       act8_t kop;
-      if constexpr (I8) {
+      if constexpr (KLDS) {
+        kop = *(const act8_t*)(ktile[wave] + l16 * LDK + ks * 32 + 8 * grp);
+      } else if constexpr (I8) {
         const uint32_t w0 = tl.k[ks / 2][2 * (ks & 1)], w1 = tl.k[ks / 2][2 * (ks & 1) + 1];
         const half2_t c0 = sdwa_pair<0, 1>(w0, w0), c1 = sdwa_pair<2, 3>(w0, w0);
         const half2_t c2 = sdwa_pair<0, 1>(w1, w1), c3 = sdwa_pair<2, 3>(w1, w1);
         kop = (half8_t){c0.x, c0.y, c1.x, c1.y, c2.x, c2.y, c3.x, c3.y};
-      } else if constexpr (KLDS) {
-        kop = *(const act8_t*)(ktile[wave] + l16 * LDK + ks * 32 + 8 * grp);
       } else {
         kop = __builtin_bit_cast(act8_t, tl.k[ks]);
       }
