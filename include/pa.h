@@ -38,6 +38,9 @@
  *   num_blocks * block_size < 2^31, and for int8 pools scale arrays of
  *   less than 2^31 bytes (pa_attend).  Anything else returns
  *   PA_ERR_UNSUPPORTED (or PA_ERR_SHAPE for inconsistent sizes).
+ * - Device arrays: q, k, v, out, the pools and the workspace 16-byte
+ *   aligned (the kernels move them in 16-byte vectors), int32 arrays 4-byte
+ *   and fp16 scale arrays 2-byte aligned; PA_ERR_SHAPE otherwise.
  * - Device-side integer data (slots, block ids, lengths) are preconditions.
  *   Kernels never read or write outside the pools for out-of-range values:
  *   an out-of-range slot is skipped and an out-of-range block id reads block
@@ -57,7 +60,8 @@ extern "C" {
 typedef enum {
   PA_OK = 0,
   PA_ERR_NULL = 1,         /* a required pointer is NULL                       */
-  PA_ERR_SHAPE = 2,        /* sizes inconsistent with each other               */
+  PA_ERR_SHAPE = 2,        /* sizes inconsistent with each other, or a
+                              misaligned device array                        */
   PA_ERR_DTYPE = 3,        /* unknown kv_dtype                                 */
   PA_ERR_UNSUPPORTED = 4,  /* valid but not built: block size, head dim, group */
   PA_ERR_WORKSPACE = 5,    /* workspace smaller than pa_attend_workspace_bytes */

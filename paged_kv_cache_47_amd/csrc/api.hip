@@ -223,6 +223,13 @@ struct HostPlan {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The kernels move q, k, v, out, pool tiles and workspace records in 16-byte
+// vectors and read int32 metadata and fp16 scales one element at a time.
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+static bool scales_aligned(const pa_cache_desc* d, const void* ks, const void* vs) {
+  return d->kv_dtype != PA_KV_I8 || (aligned(ks, 2) && aligned(vs, 2));
+}
+
 static pa_status check_desc(const pa_cache_desc* d) {
   if (d == nullptr) return PA_ERR_NULL;
   if (d->kv_dtype != PA_KV_F16 && d->kv_dtype != PA_KV_I8 && d->kv_dtype != PA_KV_BF16) return PA_ERR_DTYPE;
@@ -352,7 +359,7 @@ const char* pa_status_str(pa_status s) {
   switch (s) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
-    case PA_ERR_SHAPE: return "sizes are inconsistent";
+    case PA_ERR_SHAPE: return "sizes are inconsistent, or an array is misaligned";
     case PA_ERR_DTYPE: return "unknown kv dtype";
     case PA_ERR_UNSUPPORTED: return "unsupported block size, head dim or group size";
     case PA_ERR_WORKSPACE: return "workspace too small";
@@ -371,6 +378,9 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v, c
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
   if (desc->kv_dtype == PA_KV_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 4) || !scales_aligned(desc, k_scale, v_scale))
+    return PA_ERR_SHAPE;
 #if PA_DEBUG
   if ((st = debug_check_write(*desc, slot_mapping, num_tokens, stream)) != PA_OK) return st;
 #endif
@@ -391,6 +401,9 @@ pa_status pa_copy_blocks(const pa_cache_desc* desc, void* k_cache, void* v_cache
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !src_dst) return PA_ERR_NULL;
   if (desc->kv_dtype == PA_KV_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(src_dst, 4) ||
+      !scales_aligned(desc, k_scale, v_scale))
+    return PA_ERR_SHAPE;
 #if PA_DEBUG
   if ((st = debug_check_copy(*desc, src_dst, num_pairs, stream)) != PA_OK) return st;
 #endif
@@ -404,6 +417,7 @@ pa_status pa_check_write(const pa_cache_desc* desc, const int32_t* slot_mapping,
   if (st != PA_OK) return st;
   if (num_tokens < 0) return PA_ERR_SHAPE;
   if (!status || (num_tokens > 0 && !slot_mapping)) return PA_ERR_NULL;
+  if (!aligned(status, 4) || !aligned(slot_mapping, 4)) return PA_ERR_SHAPE;
   return launch_check_write(*desc, slot_mapping, num_tokens, status, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -417,6 +431,8 @@ pa_status pa_check_attend(const pa_cache_desc* desc, const int32_t* block_tables
   if (opts && opts->window < 0) return PA_ERR_SHAPE;
   if (!status || (num_seqs > 0 && (!block_tables || !seq_lens || !q_lens || !h_seq_lens || !h_q_lens)))
     return PA_ERR_NULL;
+  if (!aligned(status, 4) || !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(q_lens, 4))
+    return PA_ERR_SHAPE;
   return launch_check_attend(*desc, block_tables, max_blocks_per_seq, seq_lens, q_lens, num_seqs, h_seq_lens,
                              h_q_lens, opts ? opts->window : 0, status, stream) == hipSuccess
              ? PA_OK
@@ -429,6 +445,7 @@ pa_status pa_check_copy(const pa_cache_desc* desc, const int32_t* src_dst, int32
   if (st != PA_OK) return st;
   if (num_pairs < 0) return PA_ERR_SHAPE;
   if (!status || (num_pairs > 0 && !src_dst)) return PA_ERR_NULL;
+  if (!aligned(status, 4) || !aligned(src_dst, 4)) return PA_ERR_SHAPE;
   return launch_check_copy(*desc, src_dst, num_pairs, status, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -472,6 +489,10 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   if (P.total_q == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !q_lens || !out || !workspace) return PA_ERR_NULL;
   if (desc->kv_dtype == PA_KV_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(q_lens, 4) ||
+      !scales_aligned(desc, k_scale, v_scale))
+    return PA_ERR_SHAPE;
   // the decode kernel's scale reads are range-checked against a 31-bit byte count
   if (desc->kv_dtype == PA_KV_I8 &&
       (int64_t)desc->num_blocks * std::max(desc->num_layers, 1) * desc->num_kv_heads * 2 > INT32_MAX)

@@ -79,6 +79,31 @@ def test_null_and_empty_arguments():
     assert lib.pa_copy_blocks(ctypes.byref(d), None, None, None, None, None, 0, None) == 0
 
 
+def test_misaligned_device_arrays_are_refused_on_the_host():
+    """q, k, v, out, pools and workspace move in 16-byte vectors, int32 arrays and
+    fp16 scales element by element: a pointer off those boundaries is PA_ERR_SHAPE
+    before anything is enqueued (the addresses here are never dereferenced)."""
+    lib = pa.load_library()
+    d, di8 = _desc(), _desc(kv_dtype=1)
+    ok, off8, off2, odd = (ctypes.c_void_p(a) for a in (4096, 4104, 4098, 4097))
+    w = lambda desc, k=ok, v=ok, sl=ok, kc=ok, vc=ok, ks=None, vs=None: lib.pa_write_kv(
+        ctypes.byref(desc), k, v, sl, 3, kc, vc, ks, vs, None)
+    assert w(d, k=off8) == 2 and w(d, v=off8) == 2 and w(d, kc=off8) == 2 and w(d, vc=off8) == 2
+    assert w(d, sl=off2) == 2
+    assert w(di8, ks=ok, vs=odd) == 2
+    assert lib.pa_copy_blocks(ctypes.byref(d), off8, ok, None, None, ok, 1, None) == 2
+    assert lib.pa_copy_blocks(ctypes.byref(d), ok, ok, None, None, off2, 1, None) == 2
+    L, Q = np.asarray([5], np.int32), np.asarray([1], np.int32)
+
+    def attend(q=ok, kc=ok, tbl=ok, lens=ok, out=ok, ws=ok):
+        return lib.pa_attend(ctypes.byref(d), q, 4, kc, ok, None, None, tbl, 4, lens, ok, 1, pa._hp(L), pa._hp(Q),
+                             ctypes.c_float(0.1), out, ws, 1 << 20, None, None)
+    assert attend(q=off8) == 2 and attend(kc=off8) == 2 and attend(out=off8) == 2 and attend(ws=off8) == 2
+    assert attend(tbl=off2) == 2 and attend(lens=off2) == 2
+    assert lib.pa_check_write(ctypes.byref(d), ok, 4, off2, None) == 2
+    assert lib.pa_check_copy(ctypes.byref(d), off2, 2, ok, None) == 2
+
+
 def _attend(desc, hq, L, Q, maxb, ws_bytes=1 << 20, ptrs=True, opts=None, scales=False):
     lib = pa.load_library()
     L = np.asarray(L, np.int32)
