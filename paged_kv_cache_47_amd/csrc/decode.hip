@@ -106,6 +106,9 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)
 #ifndef PA_DECODE_KQ
 #define PA_DECODE_KQ 1      // int8 d128, G = 8: K read four lanes per token row (see the kernel)
 #endif
+#ifndef PA_DECODE_RS
+#define PA_DECODE_RS 1      // int8 d128, G = 4: scores summed by reduce-scatter (see the kernel)
+#endif
 
 template <int N, bool NT = PA_DECODE_NT>
 __device__ __forceinline__ Dw<N> load_dw(const uint32_t* p) {
@@ -162,6 +165,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   // faster than the 16-lane sums; with four rows (8 lanes per row) the same
   // layout was 7-13% slower than three butterfly steps, so it is not used there.
   constexpr bool KQ = I8 && QLDS && D == 128 && NL == 4 && PA_DECODE_KQ;
+  // int8 at head dim 128 with four rows (16-byte loads, 8 lanes per token row,
+  // two token rows per lane): the 8 lanes of a token row hold the four query
+  // rows in a lane-dependent order, slot j holding row fr ^ j with
+  // fr = (b0 ^ b2) | b2 << 1 for lane bits b0..b2 in the row.  The partner of
+  // each DPP step then holds in the same register the rows this lane keeps, so
+  // the sums reduce-scatter without selects: row half-mirror (lane ^ 7) halves
+  // the rows, quad xor 1 halves them again and quad xor 2 finishes the sum.
+  // Each lane ends with its own row's two scores: 8 DPP adds instead of 24, and
+  // the softmax of one row (2 exponentials instead of 8).  The other rows'
+  // weight pairs come back with three DPP moves (lane ^ 1: row fr ^ 1, lane ^ 7:
+  // fr ^ 2, both: fr ^ 3), so accumulator slot j is row fr ^ j too; the rows
+  // return to their order once, after the last block.
+  constexpr bool RS = I8 && QLDS && D == 128 && G == 4 && LPT == 8 && NL == 2 && PA_DECODE_RS;
 
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -173,6 +189,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   const int klo = un.klo, kbeg = un.kbeg, kend = un.kend;
   const int grp = lane / LPT, sub = lane % LPT;
   const int kquad = sub >> 2;   // KQ: the lane's quad inside its V lane group
+  const int fr = ((sub ^ (sub >> 2)) & 1) | (sub & 4) >> 1;   // RS: the row in slot 0
   const int64_t row0 = (int64_t)(q_start + t) * a.hq + (int64_t)h * G;
   const int32_t* tbl = a.block_tables + (int64_t)seq * a.max_blocks;
 
@@ -342,6 +359,87 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < E; ++e) acc[g][e] = dot2(pp, vp[e], acc[g][e]);
         }
+      }
+      return;
+    }
+
+    if constexpr (RS) {
+      act2_t kh[NL][E2];
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int c = 0; c < ND; ++c) {
+          kh[i][2 * c] = sdwa_pair<0, 1>(kr[i].v[c], kr[i].v[c]);
+          kh[i][2 * c + 1] = sdwa_pair<2, 3>(kr[i].v[c], kr[i].v[c]);
+        }
+      float s[NL][G];   // token i, row slot j (row fr ^ j)
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        act2_t qg[E2];
+#pragma unroll
+        for (int c = 0; c < E2 / 4; ++c) {
+          const uint4 w = ((const uint4*)(qs + (fr ^ j) * D + sub * E))[c];
+          qg[4 * c + 0] = __builtin_bit_cast(act2_t, w.x);
+          qg[4 * c + 1] = __builtin_bit_cast(act2_t, w.y);
+          qg[4 * c + 2] = __builtin_bit_cast(act2_t, w.z);
+          qg[4 * c + 3] = __builtin_bit_cast(act2_t, w.w);
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          float d = dot2_first(qg[0], kh[i][0]);
+#pragma unroll
+          for (int c = 1; c < E2; ++c) d = dot2(qg[c], kh[i][c], d);
+          s[i][j] = d;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) s[i][j] += dpp<0x141>(s[i][j ^ 2]);   // row half-mirror: lane ^ 7
+#pragma unroll
+      for (int i = 0; i < NL; ++i) s[i][0] += dpp<0xB1>(s[i][1]);          // lane ^ 1
+#pragma unroll
+      for (int i = 0; i < NL; ++i) s[i][0] += dpp<0x4E>(s[i][0]);          // lane ^ 2
+      if (edge) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+          if (hidden(tok0 + i * TPL)) s[i][0] = -__builtin_inff();
+      }
+      // lazy rescale as below, each lane testing its own row; the maxima of
+      // the other slots' rows come from their owners
+      const float mb = fmaxf(s[0][0], s[1][0]) * ksc;
+      if (__builtin_amdgcn_ballot_w64(mb > m[0] + kRescaleI8)) {
+        float mbs[G];
+        mbs[0] = mb;
+        mbs[1] = dpp<0xB1>(mb);
+        mbs[2] = dpp<0x141>(mb);
+        mbs[3] = dpp<0x141>(mbs[1]);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          if (mbs[j] > m[j] + kRescaleI8) {
+            const float al = fast_exp2(m[j] - mbs[j]);
+            m[j] = mbs[j];
+            l[j] *= al;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[j][e] *= al;
+          }
+        }
+      }
+      const float p0 = fast_exp2(fmaf(s[0][0], ksc, -m[0]));
+      const float p1 = fast_exp2(fmaf(s[1][0], ksc, -m[0]));
+      l[0] += p0 + p1;   // only the own row's sum is kept (slot 0)
+      float pp[G];       // fp16 weight pairs (token 0, token 1) of each slot's row, as raw bits
+      pp[0] = __builtin_bit_cast(float, (act2_t){(act_t)(p0 * vsc), (act_t)(p1 * vsc)});
+      pp[1] = dpp<0xB1>(pp[0]);
+      pp[2] = dpp<0x141>(pp[0]);
+      pp[3] = dpp<0x141>(pp[1]);
+      act2_t vp[E];
+      v_token_pairs<I8, ND>(vr[0], vr[1], vp);
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const act2_t pj = __builtin_bit_cast(act2_t, pp[j]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[j][e] = dot2(pj, vp[e], acc[j][e]);
       }
       return;
     }
@@ -556,6 +654,34 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     }
   }
 
+  if constexpr (RS) {
+    // the row sums from their owners (slot j holds row fr ^ j), then every
+    // lane's rows back in order
+    float ls[G];
+    ls[0] = l[0];
+    ls[1] = dpp<0xB1>(l[0]);
+    ls[2] = dpp<0x141>(l[0]);
+    ls[3] = dpp<0x141>(ls[1]);
+    auto pick = [&](int k, float x0, float x1, float x2, float x3) {
+      return k == 0 ? x0 : k == 1 ? x1 : k == 2 ? x2 : x3;
+    };
+    float mr[G], lr[G], ar[G][E];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int k = g ^ fr;
+      mr[g] = pick(k, m[0], m[1], m[2], m[3]);
+      lr[g] = pick(k, ls[0], ls[1], ls[2], ls[3]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) ar[g][e] = pick(k, acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = mr[g];
+      l[g] = lr[g];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] = ar[g][e];
+    }
+  }
   if constexpr (KQ) {
     // each quad summed its own token's weights: the lane group's row sums
 #pragma unroll
