@@ -107,7 +107,7 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)
 #define PA_DECODE_KQ 1      // int8 d128, G = 8: K read four lanes per token row (see the kernel)
 #endif
 #ifndef PA_DECODE_RS
-#define PA_DECODE_RS 1      // int8 d128, G = 4: scores summed by reduce-scatter (see the kernel)
+#define PA_DECODE_RS 1      // d128, G = 4: scores summed by reduce-scatter (see the kernel)
 #endif
 
 template <int N, bool NT = PA_DECODE_NT>
@@ -165,19 +165,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   // faster than the 16-lane sums; with four rows (8 lanes per row) the same
   // layout was 7-13% slower than three butterfly steps, so it is not used there.
   constexpr bool KQ = I8 && QLDS && D == 128 && NL == 4 && PA_DECODE_KQ;
-  // int8 at head dim 128 with four rows (16-byte loads, 8 lanes per token row,
-  // two token rows per lane): the 8 lanes of a token row hold the four query
-  // rows in a lane-dependent order, slot j holding row fr ^ j with
-  // fr = (b0 ^ b2) | b2 << 1 for lane bits b0..b2 in the row.  The partner of
-  // each DPP step then holds in the same register the rows this lane keeps, so
-  // the sums reduce-scatter without selects: row half-mirror (lane ^ 7) halves
-  // the rows, quad xor 1 halves them again and quad xor 2 finishes the sum.
-  // Each lane ends with its own row's two scores: 8 DPP adds instead of 24, and
-  // the softmax of one row (2 exponentials instead of 8).  The other rows'
-  // weight pairs come back with three DPP moves (lane ^ 1: row fr ^ 1, lane ^ 7:
-  // fr ^ 2, both: fr ^ 3), so accumulator slot j is row fr ^ j too; the rows
-  // return to their order once, after the last block.
-  constexpr bool RS = I8 && QLDS && D == 128 && G == 4 && LPT == 8 && NL == 2 && PA_DECODE_RS;
+  // Head dim 128 with four rows (16-byte loads: an int8 token row spans 8
+  // lanes, two token rows per lane; a 16-bit one spans 16 lanes, four token
+  // rows per lane): the lanes of a token row hold the four query rows in a
+  // lane-dependent order, slot j holding row fr ^ j, with fr chosen so that
+  // the partner of each DPP step holds in the same register the rows this
+  // lane keeps.  The sums then reduce-scatter without selects: two halving
+  // steps (int8: row half-mirror, lane ^ 7, then quad xor 1; 16-bit: row
+  // mirror, lane ^ 15, then row half-mirror) and all-reduce steps over the
+  // rest of the row (quad xor 2; quad xor 1 and 2), and each lane ends with its
+  // own row's scores: 8 DPP adds instead of 24 (int8), 20 instead of 64
+  // (16-bit), and the softmax of one row (a quarter of the exponentials).  The
+  // other rows' weight pairs come back with three DPP moves per pair (from1:
+  // row fr ^ 1, from2: row fr ^ 2, both: fr ^ 3), so accumulator slot j is row
+  // fr ^ j too; the rows return to their order once, after the last block.
+  constexpr bool RS = D == 128 && G == 4 && PA_DECODE_RS &&
+                      ((I8 && QLDS && LPT == 8 && NL == 2) || (!I8 && LPT == 16 && NL == 4));
 
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -189,7 +192,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   const int klo = un.klo, kbeg = un.kbeg, kend = un.kend;
   const int grp = lane / LPT, sub = lane % LPT;
   const int kquad = sub >> 2;   // KQ: the lane's quad inside its V lane group
-  const int fr = ((sub ^ (sub >> 2)) & 1) | (sub & 4) >> 1;   // RS: the row in slot 0
+  // RS: the row in slot 0 (int8: bits b0 ^ b2, b2 of the lane in its row; 16-bit: b2 ^ b3, b3)
+  const int fr = LPT == 8 ? (((sub ^ (sub >> 2)) & 1) | (sub & 4) >> 1) : ((((sub >> 2) ^ (sub >> 3)) & 1) | (sub >> 2 & 2));
+  // RS: the same register of the lane holding row fr ^ 1, and of the one holding fr ^ 2
+  auto from1 = [&](float x) {
+    if constexpr (LPT == 8) return dpp<0xB1>(x);
+    else return dpp<0x141>(x);
+  };
+  auto from2 = [&](float x) {
+    if constexpr (LPT == 8) return dpp<0x141>(x);
+    else return dpp<0x140>(x);
+  };
   const int64_t row0 = (int64_t)(q_start + t) * a.hq + (int64_t)h * G;
   const int32_t* tbl = a.block_tables + (int64_t)seq * a.max_blocks;
 
@@ -202,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   } else {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const uint4* qp = (const uint4*)((const act_t*)a.q + (row0 + g) * D + sub * E);
+      const uint4* qp = (const uint4*)((const act_t*)a.q + (row0 + (RS ? (fr ^ g) : g)) * D + sub * E);
 #pragma unroll
       for (int c = 0; c < E / 8; ++c) {
         const uint4 w = qp[c];
@@ -364,42 +377,63 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     }
 
     if constexpr (RS) {
-      act2_t kh[NL][E2];
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-#pragma unroll
-        for (int c = 0; c < ND; ++c) {
-          kh[i][2 * c] = sdwa_pair<0, 1>(kr[i].v[c], kr[i].v[c]);
-          kh[i][2 * c + 1] = sdwa_pair<2, 3>(kr[i].v[c], kr[i].v[c]);
-        }
       float s[NL][G];   // token i, row slot j (row fr ^ j)
+      if constexpr (I8) {
+        act2_t kh[NL][E2];
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        act2_t qg[E2];
+        for (int i = 0; i < NL; ++i)
 #pragma unroll
-        for (int c = 0; c < E2 / 4; ++c) {
-          const uint4 w = ((const uint4*)(qs + (fr ^ j) * D + sub * E))[c];
-          qg[4 * c + 0] = __builtin_bit_cast(act2_t, w.x);
-          qg[4 * c + 1] = __builtin_bit_cast(act2_t, w.y);
-          qg[4 * c + 2] = __builtin_bit_cast(act2_t, w.z);
-          qg[4 * c + 3] = __builtin_bit_cast(act2_t, w.w);
+          for (int c = 0; c < ND; ++c) {
+            kh[i][2 * c] = sdwa_pair<0, 1>(kr[i].v[c], kr[i].v[c]);
+            kh[i][2 * c + 1] = sdwa_pair<2, 3>(kr[i].v[c], kr[i].v[c]);
+          }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          act2_t qg[E2];
+#pragma unroll
+          for (int c = 0; c < E2 / 4; ++c) {
+            const uint4 w = ((const uint4*)(qs + (fr ^ j) * D + sub * E))[c];
+            qg[4 * c + 0] = __builtin_bit_cast(act2_t, w.x);
+            qg[4 * c + 1] = __builtin_bit_cast(act2_t, w.y);
+            qg[4 * c + 2] = __builtin_bit_cast(act2_t, w.z);
+            qg[4 * c + 3] = __builtin_bit_cast(act2_t, w.w);
+          }
+#pragma unroll
+          for (int i = 0; i < NL; ++i) {
+            float d = dot2_first(qg[0], kh[i][0]);
+#pragma unroll
+            for (int c = 1; c < E2; ++c) d = dot2(qg[c], kh[i][c], d);
+            s[i][j] = d;
+          }
         }
+      } else {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-          float d = dot2_first(qg[0], kh[i][0]);
+          act2_t kh[E2];
 #pragma unroll
-          for (int c = 1; c < E2; ++c) d = dot2(qg[c], kh[i][c], d);
-          s[i][j] = d;
+          for (int c = 0; c < ND; ++c) kh[c] = __builtin_bit_cast(act2_t, kr[i].v[c]);
+#pragma unroll
+          for (int j = 0; j < G; ++j) {   // qh[j] holds row fr ^ j
+            float d = dot2_first(qh[j][0], kh[0]);
+#pragma unroll
+            for (int c = 1; c < E2; ++c) d = dot2(qh[j][c], kh[c], d);
+            s[i][j] = d;
+          }
         }
       }
+      // halving steps, then the rest of the row
 #pragma unroll
       for (int i = 0; i < NL; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) s[i][j] += dpp<0x141>(s[i][j ^ 2]);   // row half-mirror: lane ^ 7
+        for (int j = 0; j < 2; ++j) s[i][j] += from2(s[i][j ^ 2]);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) s[i][0] += dpp<0xB1>(s[i][1]);          // lane ^ 1
+      for (int i = 0; i < NL; ++i) s[i][0] += from1(s[i][1]);
+      if constexpr (LPT == 16) {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) s[i][0] += dpp<0x4E>(s[i][0]);          // lane ^ 2
+        for (int i = 0; i < NL; ++i) s[i][0] += dpp<0xB1>(s[i][0]);
+      }
+#pragma unroll
+      for (int i = 0; i < NL; ++i) s[i][0] += dpp<0x4E>(s[i][0]);
       if (edge) {
 #pragma unroll
         for (int i = 0; i < NL; ++i)
@@ -407,16 +441,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       }
       // lazy rescale as below, each lane testing its own row; the maxima of
       // the other slots' rows come from their owners
-      const float mb = fmaxf(s[0][0], s[1][0]) * ksc;
-      if (__builtin_amdgcn_ballot_w64(mb > m[0] + kRescaleI8)) {
+      constexpr float kRescale = I8 ? kRescaleI8 : kRescaleF16;
+      float mb = s[0][0];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) mb = fmaxf(mb, s[i][0]);
+      mb *= ksc;
+      if (__builtin_amdgcn_ballot_w64(mb > m[0] + kRescale)) {
         float mbs[G];
         mbs[0] = mb;
-        mbs[1] = dpp<0xB1>(mb);
-        mbs[2] = dpp<0x141>(mb);
-        mbs[3] = dpp<0x141>(mbs[1]);
+        mbs[1] = from1(mb);
+        mbs[2] = from2(mb);
+        mbs[3] = from2(mbs[1]);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-          if (mbs[j] > m[j] + kRescaleI8) {
+          if (mbs[j] > m[j] + kRescale) {
             const float al = fast_exp2(m[j] - mbs[j]);
             m[j] = mbs[j];
             l[j] *= al;
@@ -425,21 +463,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
           }
         }
       }
-      const float p0 = fast_exp2(fmaf(s[0][0], ksc, -m[0]));
-      const float p1 = fast_exp2(fmaf(s[1][0], ksc, -m[0]));
-      l[0] += p0 + p1;   // only the own row's sum is kept (slot 0)
-      float pp[G];       // fp16 weight pairs (token 0, token 1) of each slot's row, as raw bits
-      pp[0] = __builtin_bit_cast(float, (act2_t){(act_t)(p0 * vsc), (act_t)(p1 * vsc)});
-      pp[1] = dpp<0xB1>(pp[0]);
-      pp[2] = dpp<0x141>(pp[0]);
-      pp[3] = dpp<0x141>(pp[1]);
-      act2_t vp[E];
-      v_token_pairs<I8, ND>(vr[0], vr[1], vp);
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const act2_t pj = __builtin_bit_cast(act2_t, pp[j]);
+      for (int jp = 0; jp < NL / 2; ++jp) {
+        const float p0 = fast_exp2(fmaf(s[2 * jp][0], ksc, -m[0]));
+        const float p1 = fast_exp2(fmaf(s[2 * jp + 1][0], ksc, -m[0]));
+        act2_t pw;
+        if constexpr (I8) {
+          l[0] += p0 + p1;   // only the own row's sum is kept (slot 0)
+          pw = (act2_t){(act_t)(p0 * vsc), (act_t)(p1 * vsc)};
+        } else {
+          pw = (act2_t){(act_t)p0, (act_t)p1};
+          // sum the rounded weights the product uses, so the output stays a convex combination
+          l[0] = dot2(pw, (act2_t){(act_t)1.f, (act_t)1.f}, l[0]);
+        }
+        float pp[G];   // the weight pair of each slot's row, as raw bits
+        pp[0] = __builtin_bit_cast(float, pw);
+        pp[1] = from1(pp[0]);
+        pp[2] = from2(pp[0]);
+        pp[3] = from2(pp[1]);
+        act2_t vp[E];
+        v_token_pairs<I8, ND>(vr[2 * jp], vr[2 * jp + 1], vp);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[j][e] = dot2(pj, vp[e], acc[j][e]);
+        for (int j = 0; j < G; ++j) {
+          const act2_t pj = __builtin_bit_cast(act2_t, pp[j]);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[j][e] = dot2(pj, vp[e], acc[j][e]);
+        }
       }
       return;
     }
@@ -659,9 +708,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     // lane's rows back in order
     float ls[G];
     ls[0] = l[0];
-    ls[1] = dpp<0xB1>(l[0]);
-    ls[2] = dpp<0x141>(l[0]);
-    ls[3] = dpp<0x141>(ls[1]);
+    ls[1] = from1(l[0]);
+    ls[2] = from2(l[0]);
+    ls[3] = from2(ls[1]);
     auto pick = [&](int k, float x0, float x1, float x2, float x3) {
       return k == 0 ? x0 : k == 1 ? x1 : k == 2 ? x2 : x3;
     };
