@@ -376,6 +376,15 @@ def summarize_counters(csv_path: str, out: str, cmd: str, title: str, prefixes) 
             if "SQ_INSTS_VALU" in avg and "SQ_WAVES" in avg and avg["SQ_WAVES"]:
                 lines.append(f"VALU instructions per wave: {avg['SQ_INSTS_VALU'] / avg['SQ_WAVES']:,.0f}; "
                              f"MFMA per wave: {avg.get('SQ_INSTS_MFMA', 0) / avg['SQ_WAVES']:,.0f}.")
+        if avg.get("SQ_WAVE_CYCLES"):
+            wc = avg["SQ_WAVE_CYCLES"]
+            lines.append("")
+            for name, what in (("SQ_ACTIVE_INST_ANY", "issuing an instruction"),
+                               ("SQ_WAIT_ANY", "waiting on a counter or the barrier"),
+                               ("SQ_WAIT_INST_ANY", "waiting for an issue slot"),
+                               ("SQ_WAIT_INST_LDS", "with an LDS instruction waiting for issue")):
+                if name in avg:
+                    lines.append(f"Waves {what}: {avg[name] / wc:.1%} of wave cycles ({name} / SQ_WAVE_CYCLES).")
         lines.append("")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -575,6 +584,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the HBM read ceilings (stream read, random 4 KiB tile gather) in the JSON line")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--mfma-split-steps", type=int, default=0,
+                    help="split row tiles walking more 64-key steps than this (0: the library's choice, -1: never)")
     ap.add_argument("--cold", type=int, default=-1, choices=(-1, 0, 1),
                     help="also time steps after a 1 GiB scratch write that evicts the 256 MB MALL "
                          "(default: for working sets under 512 MB, workloads 1, 2 and 4)")
@@ -600,6 +611,10 @@ def main(argv=None) -> int:
     ap.add_argument("--w5-q-heads", type=int, default=32, choices=(32, 64, 128),
                     help="workload 5: query heads over the 8 KV heads (64: groups of eight; 128: groups of 16, "
                          "the decode rows on the matrix cores)")
+    ap.add_argument("--w5-chunks", type=int, default=8,
+                    help="workload 5: number of 512-query prefill chunks")
+    ap.add_argument("--w5-chunk-ctx", type=int, default=-1,
+                    help="workload 5: cached context of every chunk (-1: drawn from U[0,8192])")
     ap.add_argument("--w5-chunks-only", action="store_true",
                     help="workload 5: the 8 prefill chunks alone (no decode sequences): the MFMA kernel by itself")
     ap.add_argument("--no-share", action="store_true",
@@ -633,7 +648,8 @@ def main(argv=None) -> int:
         import synthetic
         if args.workload == 5:
             w = synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192,
-                                  num_q_heads=args.w5_q_heads)
+                                  num_q_heads=args.w5_q_heads, num_chunks=args.w5_chunks,
+                                  chunk_ctx=None if args.w5_chunk_ctx < 0 else args.w5_chunk_ctx)
         elif args.workload == 3:
             w = synthetic.config3(kv_dtype=args.kv_dtype, num_q_heads=args.w3_q_heads)
         else:
@@ -671,14 +687,17 @@ def main(argv=None) -> int:
     if args.kv_dtype == "i8" and args.workload != 6:
         print("--kv-dtype i8 applies to workload 6 (workload 5 is the int8 kernel workload)", file=sys.stderr)
         return 2
-    if (args.w5_pool != "i8" or args.w5_chunks_only or args.w5_q_heads != 32) and args.workload != 5:
-        print("--w5-pool, --w5-q-heads and --w5-chunks-only apply to workload 5 only", file=sys.stderr)
+    if (args.w5_pool != "i8" or args.w5_chunks_only or args.w5_q_heads != 32 or args.w5_chunks != 8
+            or args.w5_chunk_ctx >= 0) and args.workload != 5:
+        print("--w5-pool, --w5-q-heads, --w5-chunks, --w5-chunk-ctx and --w5-chunks-only apply to workload 5 only",
+              file=sys.stderr)
         return 2
     if args.workload == 4 and args.no_share:
         w = synthetic.config4(share=False)
     elif args.workload == 5:
         w = synthetic.config5(kv_dtype=args.w5_pool, num_decode=0 if args.w5_chunks_only else 192,
-                              num_q_heads=args.w5_q_heads)
+                              num_q_heads=args.w5_q_heads, num_chunks=args.w5_chunks,
+                              chunk_ctx=None if args.w5_chunk_ctx < 0 else args.w5_chunk_ctx)
     elif args.workload == 2:
         w = synthetic.config2(num_layers=args.layers, kv_dtype=args.kv_dtype)
     elif args.workload == 3:
@@ -699,7 +718,8 @@ def main(argv=None) -> int:
     vec_bytes, mfma_flops, kv_bytes = work_split(w, L, Q)
     kv_bytes *= w.num_layers                     # the step attends every layer
     need = pa.pa_attend_workspace_bytes(run.k_cache, w.num_q_heads, x.batch.seq_lens, x.batch.q_lens,
-                                        partition_tokens=args.partition_tokens, window=w.window)
+                                        partition_tokens=args.partition_tokens, window=w.window,
+                                        mfma_split_steps=args.mfma_split_steps)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     n = args.warmup + args.steps
     evs = TimingEvents(4 * n)
@@ -722,7 +742,8 @@ def main(argv=None) -> int:
             calls.append(pa.prepare_attend(q, kc, vc, x.block_tables, x.seq_lens, x.q_lens, x.batch.seq_lens,
                                            x.batch.q_lens, w.scale, out=outs[layer], workspace=ws, k_scale=ks,
                                            v_scale=vs, partition_tokens=args.partition_tokens, events=ev,
-                                           window=w.window, layer=layer, reuse_plan=layer > 0, side=side))
+                                           window=w.window, layer=layer, reuse_plan=layer > 0, side=side,
+                                           mfma_split_steps=args.mfma_split_steps))
         return calls
 
     prepared = {(i, tk): step_calls(i, tk) for i in range(n) for tk in (True, False)}
@@ -852,10 +873,13 @@ def main(argv=None) -> int:
                    + (f" [{args.w5_q_heads} query heads]" if args.w5_q_heads != 32 else "")
                    + (" [row tiles on a side stream]" if args.side_stream else "")
                    + (f" [{args.w5_pool} pool with N(0,1) contents]" if args.w5_pool != "i8" else "")
-                   + (" [the 8 prefill chunks only]" if args.w5_chunks_only else ""),
+                   + (f" [{args.w5_chunks} chunks]" if args.w5_chunks != 8 else "")
+                   + (f" [every chunk over {args.w5_chunk_ctx} cached keys]" if args.w5_chunk_ctx >= 0 else "")
+                   + (" [the prefill chunks only]" if args.w5_chunks_only else ""),
                    "num_seqs": S, "kv_tokens": int(L.sum()),
                    "query_rows": int(Q.sum()), "num_blocks": w.num_blocks,
-                   "partition_tokens": args.partition_tokens, "window": args.window, "layers": w.num_layers},
+                   "partition_tokens": args.partition_tokens, "mfma_split_steps": args.mfma_split_steps,
+                   "window": args.window, "layers": w.num_layers},
         "pct_of_peak": round(100 * kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "seq_steps_per_s": round(S / (ms * 1e-3), 1),
         "ms_per_step_with_kernel_events": round(ms_events, 5),

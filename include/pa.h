@@ -180,6 +180,19 @@ pa_status pa_write_kv(const pa_cache_desc* desc, const void* k, const void* v,
  *                     GPU.  All three NULL: everything on `stream`.  Either
  *                     way the call's work is complete when `stream` reaches
  *                     the point after the call.
+ *   mfma_split_steps  longest key range, in 64-key steps, that one
+ *                     workgroup of the row-tile kernel walks: a row tile
+ *                     (256 query rows of a sequence) whose keys span more
+ *                     steps is split into ceil(steps / s) parts of equal
+ *                     step counts, each run by its own workgroup, and the
+ *                     parts' (max, sum, output) are merged in log-sum-exp
+ *                     form into the tile's rows (the split-K of the decode
+ *                     path, applied to long chunked-prefill contexts).
+ *                     0 = chosen from the batch: a batch with fewer than
+ *                     512 row-tile workgroups (two per compute unit) is
+ *                     split at about one workgroup's share of its row-tile
+ *                     work per compute unit (at least 16 steps), a larger
+ *                     one is not; > 0 = s, < 0 = never split.
  */
 typedef struct {
   int32_t partition_tokens;
@@ -193,6 +206,7 @@ typedef struct {
   hipStream_t side_stream;
   hipEvent_t side_fork;
   hipEvent_t side_join;
+  int32_t mfma_split_steps;
 } pa_attend_opts;
 
 /*
@@ -228,6 +242,11 @@ size_t pa_attend_workspace_bytes(const pa_cache_desc* desc, int32_t num_q_heads,
  *                     (largest units first) from the device lengths and
  *                     takes its own unit
  *   workspace_bytes   what pa_attend_workspace_bytes returns
+ *   mfma_units        row-tile workgroups per KV head (a split tile counts
+ *                     once per part)
+ *   mfma_split_steps  the split of long row tiles (0: none is split); with
+ *                     mfma_split_steps fixed to this value as well, the
+ *                     workspace never grows when the lengths shrink
  * Returns the status pa_attend would return for these host arguments.
  */
 typedef struct {
@@ -238,6 +257,8 @@ typedef struct {
   int32_t mfma_tiles;
   int32_t plan_free;
   size_t workspace_bytes;
+  int32_t mfma_units;
+  int32_t mfma_split_steps;
 } pa_attend_info;
 
 pa_status pa_attend_plan_info(const pa_cache_desc* desc, int32_t num_q_heads, int32_t num_seqs,

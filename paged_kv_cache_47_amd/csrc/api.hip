@@ -61,29 +61,24 @@ __device__ int4 block_exclusive_scan4(int4 v, int4* lds, int4& total) {
   return make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
 }
 
-// First key the MFMA row tile starting at query position `qfirst` stages:
-// the step-aligned start of that row's window.
-__host__ __device__ __forceinline__ int tile_key0(int qfirst, int window) {
-  return window_lo(qfirst, window) & ~(kMfmaBN - 1);
-}
-
-// Row tiles of the MFMA path go out longest first.  A tile's cost is the
-// number of keys it steps over (causal: up to the last row's position; with a
-// window, from the first row's window start), and tiles that attend over
-// long contexts would otherwise start late and finish after the rest of the
-// grid; with 64-key cost buckets in descending order (a counting sort over
-// the workgroup) the dispatcher fills the machine greedily, longest job first.
-// The order within a bucket is whatever the atomics give: every tile writes
-// its own rows, so the results do not depend on it.
+// Row-tile units of the MFMA path go out longest first.  A unit's cost is
+// the number of 64-key steps it walks (a whole tile: up to its last row's
+// position, from its first row's window start; a part of a split tile: its
+// share), and units that attend over long contexts would otherwise start
+// late and finish after the rest of the grid; with 64-key cost buckets in
+// descending order (a counting sort over the workgroup) the dispatcher fills
+// the machine greedily, longest job first.  The order within a bucket is
+// whatever the atomics give: every unit writes its own rows (or its own
+// partial slot), so the results do not depend on it.
 constexpr int kCostBuckets = kPlanThreads;
 
-__device__ int tile_cost_bucket(const PlanArgs& a, int2 mu) {
+__device__ int tile_cost_bucket(const PlanArgs& a, int4 mu) {
+  if (mu.x < 0) return 0;   // the parts of a split tile dropped for lack of room: nothing to run
   const SeqInfo si = a.seqs[mu.x];
-  const int rows = si.q_len * a.group;
-  const int last_row = min(rows, (mu.y + 1) * kMfmaRows) - 1;
-  const int kmax = min(si.kv_len, si.kv_len - si.q_len + last_row / a.group + 1);
-  const int k0 = tile_key0(si.kv_len - si.q_len + mu.y * kMfmaRows / a.group, a.window);
-  return min((kmax - k0) / kMfmaBN, kCostBuckets - 1);
+  const int steps = tile_span(si.kv_len, si.q_len, a.group, mu.y, a.window).steps;
+  const int part = mu.z & 0xFFFF, parts = mu.z >> 16;
+  const int ps = part_steps(steps, parts);
+  return min(min(ps, steps - part * ps), kCostBuckets - 1);
 }
 
 // Vector-path units go out longest first too (a unit's cost: its keys, in
@@ -118,14 +113,14 @@ __device__ void order_row_tiles(const PlanArgs& a, int n) {
   slot[threadIdx.x] = first;
   __syncthreads();
   for (int u = threadIdx.x; u < n; u += kPlanThreads) {
-    const int2 mu = a.munit_tmp[u];
+    const int4 mu = a.munit_tmp[u];
     a.munit[atomicAdd(&slot[kCostBuckets - 1 - tile_cost_bucket(a, mu)], 1)] = mu;
   }
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int4 lds[kPlanWaves];
-  int base_q = 0, base_vt = 0, base_vu = 0, base_mu = 0;
+  int base_q = 0, base_vt = 0, base_vu = 0, base_mu = 0, base_ms = 0, base_sl = 0;
   for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
     const int i = c0 + threadIdx.x;
     int L = 0, Q = 0;
@@ -137,18 +132,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int4 tot;
     const int qs = base_q + block_exclusive_scan4(make_int4(Q, 0, 0, 0), lds, tot).x;
     const int qsum = tot.x;
-    int nvt = 0, nvu = 0, nmu = 0;
+    int nvt = 0, nvu = 0, nmu = 0, ntile = 0, nms = 0, nsl = 0;
     if (i < a.num_seqs) {
       Q = max(0, min(Q, a.total_q - qs));   // rows beyond the batch the host sized are dropped
       if (Q > 0 && Q * a.group >= a.min_rows) {
-        nmu = (Q * a.group + kMfmaRows - 1) / kMfmaRows;
+        ntile = (Q * a.group + kMfmaRows - 1) / kMfmaRows;
+        for (int r = 0; r < ntile; ++r) {
+          const int parts = tile_parts(tile_span(L, Q, a.group, r, a.window).steps, a.split_steps);
+          nmu += parts;
+          if (parts > 1) {
+            nms += 1;
+            nsl += parts;
+          }
+        }
       } else {
         nvt = Q;
         for (int t = 0; t < Q; ++t) nvu += parts_for(vector_keys(L - Q + t, a.window), a.part);
       }
     }
-    const int4 ex = block_exclusive_scan4(make_int4(nvt, nvu, nmu, 0), lds, tot);
-    const int vt0 = base_vt + ex.x, vu0 = base_vu + ex.y, mu0 = base_mu + ex.z;
+    const int4 ex = block_exclusive_scan4(make_int4(nvt, nvu, nmu, nms), lds, tot);
+    const int vt0 = base_vt + ex.x, vu0 = base_vu + ex.y, mu0 = base_mu + ex.z, ms0 = base_ms + ex.w;
+    int4 tot2;
+    const int sl0 = base_sl + block_exclusive_scan4(make_int4(nsl, 0, 0, 0), lds, tot2).x;
     if (i < a.num_seqs) {
       SeqInfo si;
       si.kv_len = L;
@@ -156,8 +161,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       si.q_start = qs;
       si.pad = 0;
       a.seqs[i] = si;
-      for (int r = 0; r < nmu; ++r)
-        if (mu0 + r < a.cap_munit) a.munit_tmp[mu0 + r] = make_int2(i, r);
+      // the row tiles' units; a split tile's parts take consecutive partial
+      // slots, and the tile is listed for the merge (dropped with its units
+      // when the device lengths need more than the host sized)
+      int mu = mu0, ms = ms0, sl = sl0;
+      for (int r = 0; r < ntile; ++r) {
+        const int parts = tile_parts(tile_span(L, Q, a.group, r, a.window).steps, a.split_steps);
+        if (parts == 1) {
+          if (mu < a.cap_munit) a.munit_tmp[mu] = make_int4(i, r, 1 << 16, -1);
+        } else {
+          const bool fits = ms < a.cap_msplit && sl + parts <= a.cap_mslot && mu + parts <= a.cap_munit;
+          if (ms < a.cap_msplit) a.msplit[ms] = make_int4(fits ? i : -1, r, parts, sl);
+          for (int p = 0; p < parts; ++p)
+            if (mu + p < a.cap_munit) a.munit_tmp[mu + p] = make_int4(fits ? i : -1, r, p | parts << 16, sl + p);
+          ms += 1;
+          sl += parts;
+        }
+        mu += parts;
+      }
       int u = vu0;
       for (int t = 0; t < nvt; ++t) {
         const int parts = parts_for(vector_keys(L - Q + t, a.window), a.part);
@@ -187,6 +208,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     base_vt += tot.x;
     base_vu += tot.y;
     base_mu += tot.z;
+    base_ms += tot.w;
+    base_sl += tot2.x;
   }
   for (int k = base_vt + threadIdx.x; k < a.cap_vtok; k += kPlanThreads) {
     VTok vt;
@@ -198,7 +221,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.vunit[u] = make_int2(-1, 0);
     a.vcost[u] = 0;
   }
-  for (int u = base_mu + threadIdx.x; u < a.cap_munit; u += kPlanThreads) a.munit[u] = make_int2(-1, 0);
+  for (int u = base_mu + threadIdx.x; u < a.cap_munit; u += kPlanThreads) a.munit[u] = make_int4(-1, 0, 1 << 16, -1);
+  for (int k = base_ms + threadIdx.x; k < a.cap_msplit; k += kPlanThreads) a.msplit[k] = make_int4(-1, 0, 1, 0);
   order_row_tiles(a, min(base_mu, a.cap_munit));
   __syncthreads();   // the two orderings share nothing but reuse the scan's LDS pattern
   order_vector_units(a, a.cap_vunit);
@@ -212,12 +236,13 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 // ------------------------------------------------------------ host plan ----
 struct HostPlan {
   int32_t part = 0, min_rows = 16, total_q = 0, window = 0;
-  int64_t n_vtok = 0, n_vunit = 0, n_munit = 0;
+  int64_t n_vtok = 0, n_vunit = 0, n_munit = 0, n_mtile = 0, n_msplit = 0, n_mslot = 0;
   int32_t max_parts = 0;
+  int32_t split_steps = 0;   // row tiles spanning more 64-key steps are split (0: never)
   bool direct = false;     // one decode workgroup per sequence, no plan kernel (see make_plan)
   bool selfplan = false;   // decode workgroups find their own units, no plan kernel (see make_plan)
   size_t off_seqs = 0, off_vtok = 0, off_vunit = 0, off_vorder = 0, off_vcost = 0, off_munit = 0, off_munit_tmp = 0,
-         off_lse = 0, off_po = 0, off_row_u0 = 0;
+         off_lse = 0, off_po = 0, off_row_u0 = 0, off_msplit = 0, off_mlse = 0, off_mpo = 0;
   size_t bytes = 0;
 };
 
@@ -267,6 +292,26 @@ static int32_t auto_part(int64_t total_keys, int32_t hkv, int32_t head_dim, int3
   return (int32_t)std::min<int64_t>(4096, p);
 }
 
+// Longest row-tile walk (in 64-key steps) when the caller leaves it to the
+// library.  One row-tile workgroup fills a compute unit, so a batch with
+// fewer row-tile workgroups than two rounds of the 256 compute units leaves
+// part of the machine idle while its long tiles run: such a batch is split
+// at about one workgroup's share of its row-tile work per compute unit, but
+// at least 16 steps (1024 keys), which amortise a part's start and its share
+// of the merge.  Measured with 512-query chunks over 8192 cached keys (fp16,
+// 32/8 heads, d128): one chunk 0.272 -> 0.115 ms, two 0.288 -> 0.228 ms,
+// four 0.359 -> 0.336 ms; one chunk over 32768 keys 0.948 -> 0.342 ms; finer
+// splits (8 or 16 steps) were slower.  Larger grids are not split: the packed
+// batch of eight chunks and 192 decode rows (512 row-tile workgroups) ran
+// 0.289 -> 0.300 ms with its longest tiles split.
+constexpr int64_t kComputeUnits = 256;
+constexpr int32_t kMinSplitSteps = 16;
+static int32_t auto_split_steps(int64_t tiles, int64_t tile_steps_total, int32_t hkv) {
+  if (tiles * hkv >= 2 * kComputeUnits) return 0;
+  const int64_t share = (tile_steps_total * hkv + kComputeUnits - 1) / kComputeUnits;
+  return (int32_t)std::min<int64_t>(INT32_MAX / 2, std::max<int64_t>(share, kMinSplitSteps));
+}
+
 static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs, const int32_t* hL,
                            const int32_t* hQ, int32_t max_blocks, const pa_attend_opts* opts, HostPlan& P) {
   pa_status st = check_desc(d);
@@ -297,10 +342,30 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   P.part = req_part > 0 ? req_part
                        : (req_part < 0 ? 0 : auto_part(vec_keys, d->num_kv_heads, d->head_dim,
                                                        d->kv_dtype == PA_KV_I8 ? 1 : 2, g));
+  // row tiles: their total walk picks the split (unless the caller fixed it), then units and parts are counted
+  const int32_t req_split = opts ? opts->mfma_split_steps : 0;
+  int64_t tile_steps = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int L = hL[i], Q = hQ[i];
+    if (!(Q > 0 && (int64_t)Q * g >= P.min_rows)) continue;
+    const int64_t nt = ((int64_t)Q * g + kMfmaRows - 1) / kMfmaRows;
+    P.n_mtile += nt;
+    for (int64_t r = 0; r < nt; ++r) tile_steps += tile_span(L, Q, g, (int)r, P.window).steps;
+  }
+  P.split_steps = req_split > 0 ? req_split
+                  : (req_split < 0 || P.n_mtile == 0 ? 0 : auto_split_steps(P.n_mtile, tile_steps, d->num_kv_heads));
   for (int i = 0; i < num_seqs; ++i) {
     const int L = hL[i], Q = hQ[i];
     if (Q > 0 && (int64_t)Q * g >= P.min_rows) {
-      P.n_munit += ((int64_t)Q * g + kMfmaRows - 1) / kMfmaRows;
+      const int64_t nt = ((int64_t)Q * g + kMfmaRows - 1) / kMfmaRows;
+      for (int64_t r = 0; r < nt; ++r) {
+        const int parts = tile_parts(tile_span(L, Q, g, (int)r, P.window).steps, P.split_steps);
+        P.n_munit += parts;
+        if (parts > 1) {
+          P.n_msplit += 1;
+          P.n_mslot += parts;
+        }
+      }
     } else {
       P.n_vtok += Q;
       for (int t = 0; t < Q; ++t) {
@@ -311,6 +376,8 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
     }
   }
   if (P.n_vunit >= INT32_MAX / 2 || P.n_munit >= INT32_MAX / 2) return PA_ERR_SHAPE;
+  // partial outputs of split row tiles: one float per (slot, KV head, tile row, dim)
+  if (P.n_mslot * d->num_kv_heads * kMfmaRows >= INT32_MAX / 2) return PA_ERR_SHAPE;
   // A batch of one query row per sequence that no row splits and that fits in
   // about one round of workgroups needs no plan: the decode kernel reads each
   // sequence's length itself (longest-first ordering matters only when the
@@ -335,9 +402,16 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   P.off_vcost = off;
   off = align_up(off + sizeof(int32_t) * (size_t)std::max<int64_t>(P.n_vunit, 1), 256);
   P.off_munit = off;
-  off = align_up(off + sizeof(int2) * (size_t)std::max<int64_t>(P.n_munit, 1), 256);
+  off = align_up(off + sizeof(int4) * (size_t)std::max<int64_t>(P.n_munit, 1), 256);
   P.off_munit_tmp = off;
-  off = align_up(off + sizeof(int2) * (size_t)std::max<int64_t>(P.n_munit, 1), 256);
+  off = align_up(off + sizeof(int4) * (size_t)std::max<int64_t>(P.n_munit, 1), 256);
+  P.off_msplit = off;
+  off = align_up(off + sizeof(int4) * (size_t)std::max<int64_t>(P.n_msplit, 1), 256);
+  const size_t mrows = (size_t)P.n_mslot * d->num_kv_heads * kMfmaRows;
+  P.off_mlse = off;
+  off = align_up(off + sizeof(float) * mrows, 256);
+  P.off_mpo = off;
+  off = align_up(off + sizeof(float) * mrows * d->head_dim, 256);
   const bool split = P.max_parts > 1;
   P.off_lse = off;
   if (split) off = align_up(off + sizeof(float) * (size_t)P.n_vunit * hq, 256);
@@ -469,7 +543,9 @@ pa_status pa_attend_plan_info(const pa_cache_desc* desc, int32_t num_q_heads, in
   info->vector_rows = (int32_t)P.n_vtok;
   info->vector_units = (int32_t)P.n_vunit;
   info->max_parts = P.max_parts;
-  info->mfma_tiles = (int32_t)P.n_munit;
+  info->mfma_tiles = (int32_t)P.n_mtile;
+  info->mfma_units = (int32_t)P.n_munit;
+  info->mfma_split_steps = P.split_steps;
   info->plan_free = P.direct ? 1 : (P.selfplan ? 2 : 0);
   info->workspace_bytes = P.bytes;
   return PA_OK;
@@ -519,8 +595,10 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   pl.vunit = (int2*)(ws + P.off_vunit);
   pl.vorder = (int32_t*)(ws + P.off_vorder);
   pl.vcost = (int32_t*)(ws + P.off_vcost);
-  pl.munit = (int2*)(ws + P.off_munit);
-  pl.munit_tmp = (int2*)(ws + P.off_munit_tmp);
+  pl.munit = (int4*)(ws + P.off_munit);
+  pl.munit_tmp = (int4*)(ws + P.off_munit_tmp);
+  pl.msplit = (int4*)(ws + P.off_msplit);
+  pl.split_steps = P.split_steps;
   pl.num_seqs = num_seqs;
   pl.group = g;
   pl.part = P.part;
@@ -531,6 +609,8 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   pl.cap_vtok = (int32_t)P.n_vtok;
   pl.cap_vunit = (int32_t)P.n_vunit;
   pl.cap_munit = (int32_t)P.n_munit;
+  pl.cap_msplit = (int32_t)P.n_msplit;
+  pl.cap_mslot = (int32_t)P.n_mslot;
   const bool direct = P.direct;
   if (!direct && !P.selfplan && !(opts && opts->reuse_plan) && launch_plan(pl, stream) != hipSuccess)
     return PA_ERR_HIP;
@@ -550,6 +630,9 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.vunit = pl.vunit;
   a.vorder = pl.vorder;
   a.munit = pl.munit;
+  a.msplit = pl.msplit;
+  a.mlse = (float*)(ws + P.off_mlse);
+  a.mpo = (float*)(ws + P.off_mpo);
   a.plse = P.max_parts > 1 ? (float*)(ws + P.off_lse) : nullptr;
   a.po = P.max_parts > 1 ? (float*)(ws + P.off_po) : nullptr;
   a.out = out;
@@ -578,6 +661,10 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   auto row_tiles = [&]() {
     if (!mark(opts ? opts->mfma_begin : nullptr, rs)) return false;
     if (launch_prefill(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_munit, rs) != hipSuccess) return false;
+    // the parts of split row tiles, merged into their rows
+    if (P.n_msplit > 0 &&
+        launch_prefill_merge(a, desc->head_dim, g, desc->kv_dtype, (int)P.n_msplit, rs) != hipSuccess)
+      return false;
     return mark(opts ? opts->mfma_end : nullptr, rs);
   };
   if (side && (hipEventRecord(opts->side_fork, stream) != hipSuccess ||

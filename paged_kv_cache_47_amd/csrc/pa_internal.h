@@ -69,7 +69,10 @@ struct AttnArgs {
   const VTok* vtok;
   const int2* vunit;   // {vtok index, partition}
   const int32_t* vorder;  // dispatch order of the vector units: workgroup x takes unit vorder[x]
-  const int2* munit;   // {sequence, row tile}
+  const int4* munit;   // {sequence, row tile, part | parts << 16, partial slot (-1: unsplit)}
+  const int4* msplit;  // split row tiles: {sequence, row tile, parts, first partial slot}
+  float* mpo;          // [slot][hkv][kMfmaRows][D] normalised partial outputs of split row tiles
+  float* mlse;         // [slot][hkv][kMfmaRows] base-2 log-sum-exp of each (-inf: no visible key)
   float* po;           // [n_vunit][Hq][D] normalised partial outputs
   float* plse;         // [n_vunit][Hq] base-2 log-sum-exp of each partial
   void* out;           // the type of q
@@ -134,8 +137,10 @@ struct PlanArgs {
   int2* vunit;
   int32_t* vorder;     // vector units, longest first (a permutation of 0 .. cap_vunit-1)
   int32_t* vcost;      // cost bucket of each vector unit (scratch for the ordering)
-  int2* munit;
-  int2* munit_tmp;     // row tiles in sequence order, before the longest-first ordering
+  int4* munit;         // row-tile units (a tile, or one part of a split tile), longest first
+  int4* munit_tmp;     // the same units in sequence order, before the ordering
+  int4* msplit;        // split row tiles, for the merge
+  int32_t split_steps; // a row tile spanning more 64-key steps is split into equal parts (<= 0: never)
   int32_t num_seqs;
   int32_t group;
   int32_t part;        // <= 0: one partition per row
@@ -143,7 +148,7 @@ struct PlanArgs {
   int32_t min_rows;
   int32_t max_kv;      // max_blocks_per_seq * block_size
   int32_t total_q;
-  int32_t cap_vtok, cap_vunit, cap_munit;
+  int32_t cap_vtok, cap_vunit, cap_munit, cap_msplit, cap_mslot;
 };
 
 // Launchers (one translation unit each); all return hipGetLastError() after launch.
@@ -152,6 +157,7 @@ hipError_t launch_decode(const AttnArgs& a, int head_dim, int group, int kv, int
 hipError_t launch_decode_mfma(const AttnArgs& a, int head_dim, int group, int kv, int n_vunit, hipStream_t s);
 hipError_t launch_reduce(const AttnArgs& a, int head_dim, int group, int kv, int n_vtok, hipStream_t s);
 hipError_t launch_prefill(const AttnArgs& a, int head_dim, int group, int kv, int n_munit, hipStream_t s);
+hipError_t launch_prefill_merge(const AttnArgs& a, int head_dim, int group, int kv, int n_msplit, hipStream_t s);
 hipError_t launch_write_f16(const pa_cache_desc& d, const void* k, const void* v, const int32_t* slots,
                             int32_t T, void* kc, void* vc, hipStream_t s);
 hipError_t launch_write_i8(const pa_cache_desc& d, const void* k, const void* v, const int32_t* slots,

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
 
   const int id = blockIdx.x;
   const int h = id % a.hkv;         // consecutive workgroups = consecutive KV heads (one XCD each when hkv = 8)
-  const int2 mu = a.munit[id / a.hkv];
+  const int4 mu = a.munit[id / a.hkv];   // {sequence, row tile, part | parts << 16, partial slot}
   if (mu.x < 0) return;
   const SeqInfo si = a.seqs[mu.x];
   const int L = si.kv_len, Q = si.q_len, rows = Q * G;
@@ -74,8 +74,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps block indices scalar
   const int l16 = lane & 15, grp = lane >> 4;
   const int r0 = mu.y * kMfmaRows;
-  const int last_row = min(rows, r0 + kMfmaRows) - 1;
-  const int kmax = min(L, L - Q + last_row / G + 1);
+  const TileSpan span = tile_span(L, Q, G, mu.y, a.window);
+  const int kmax = span.kmax;
   const int32_t* tbl = a.block_tables + (int64_t)mu.x * a.max_blocks;
   const int qmin = L - Q + (r0 + wave * 32) / G;  // query position of this wave's first row
   // With a window the tile starts at the 64-key step holding its first row's
@@ -83,7 +83,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   // blocks the window has left behind are never addressed.  A step needs the
   // window mask while it starts before the wave's last row's window does.
   const int klo = window_lo(L - Q + r0 / G, a.window);
-  const int kt0 = klo & ~(kMfmaBN - 1);
+  const int kt0 = span.k0;   // klo, step-aligned
+  // a part of a split tile walks its share of the tile's steps: keys [kbeg, kend)
+  const int part = mu.z & 0xFFFF, parts = mu.z >> 16;
+  const int psteps = part_steps(span.steps, parts);
+  const int kbeg = kt0 + part * psteps * BN;
+  const int kend = min(kmax, kbeg + psteps * BN);
   const int wlo_last = window_lo(L - Q + (min(rows, r0 + wave * 32 + 32) - 1) / G, a.window);
 
   int qpos[RB], qlo[RB];
@@ -213,10 +218,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   };
 
   Blocks tn, tn2;
-  table(kt0, tn);
-  gload(kt0, tn);
+  table(kbeg, tn);
+  gload(kbeg, tn);
   lstore(0);
-  table(kt0 + BN, tn);
+  table(kbeg + BN, tn);
   __syncthreads();
   typedef __attribute__((address_space(3))) short4_t lds_short4;
   int buf = 0;
@@ -235,8 +240,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   // are positive), and the scale rides in the exponent's FMA.  The running max
   // moves only when a score exceeds it by more than kRescalePf (log2 units),
   // so the accumulators are rescaled rarely.
-  for (int kt = kt0; kt < kmax; kt += BN, buf ^= 1) {
-    const bool more = kt + BN < kmax;
+  for (int kt = kbeg; kt < kend; kt += BN, buf ^= 1) {
+    const bool more = kt + BN < kend;
     // score scale per 16-key block (base 2; int8 folds in the block's K scale).  A zero K scale
     // (an all-zero block) becomes the least normal float: its scores stay 0, and -inf stays -inf.
     float cks[KB];
@@ -344,6 +349,23 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
     __syncthreads();
   }
 
+  if (mu.w >= 0) {
+    // a part of a split tile: its rows' normalised outputs and base-2
+    // log-sum-exps go to its partial slot (a row that saw no key of this
+    // part: output 0, log-sum-exp -inf), for the merge kernel
+    const int64_t prow = ((int64_t)mu.w * a.hkv + h) * kMfmaRows + wave * 32;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (!rvalid[rb]) continue;
+      const float l = lsum[rb][0];
+      const float inv = l > 0.f ? (I8 ? 2.f : 1.f) / l : 0.f;
+      const int64_t pr = prow + rb * 16 + l16;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) *(float4_t*)(a.mpo + pr * D + nt * 16 + 4 * grp) = o[rb][nt] * inv;
+      if (grp == 0) a.mlse[pr] = l > 0.f ? m[rb] + __builtin_log2f(l) : -__builtin_inff();
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     if (!rvalid[rb]) continue;
@@ -358,6 +380,82 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
       *(act4_t*)((act_t*)a.out + orow[rb] + nt * 16 + 4 * grp) = r;
     }
   }
+}
+
+// Merge of split row tiles: for each of the tile's rows, the parts' outputs
+// weighted by 2^(lse_p - max lse) over the sum of those weights (the
+// log-sum-exp merge of split-K partitions).  One wave per row: lane p holds
+// part p's log-sum-exp (64 parts at a time), each lane D / 64 dims of the
+// output; a workgroup of four waves takes four rows of one (split tile, KV
+// head), so the grid has 64 workgroups per split tile and head and the
+// rows' loads are spread over the machine instead of queued in one wave.
+constexpr int kMergeRowsPerGroup = 4;
+
+template <int D, int G, int KV>
+__global__ __launch_bounds__(64 * kMergeRowsPerGroup) void prefill_merge_kernel(AttnArgs a) {
+  using act_t = typename Act<KV>::t;
+  constexpr int E = D / 64;
+  constexpr int GROUPS = kMfmaRows / kMergeRowsPerGroup;   // workgroups per (split tile, head)
+  const int gid = blockIdx.x % GROUPS;
+  const int h = (blockIdx.x / GROUPS) % a.hkv;
+  const int4 ms = a.msplit[blockIdx.x / GROUPS / a.hkv];   // {sequence, row tile, parts, first slot}
+  if (ms.x < 0) return;
+  const SeqInfo si = a.seqs[ms.x];
+  const int lane = threadIdx.x & 63;
+  const int tr = gid * kMergeRowsPerGroup + (threadIdx.x >> 6);   // row within the tile
+  const int row = ms.y * kMfmaRows + tr;
+  if (row >= si.q_len * G) return;
+  const int64_t base = (int64_t)ms.w * a.hkv + h;   // partial record of part p: (base + p * hkv) * kMfmaRows + tr
+  auto rec = [&](int p) { return (base + (int64_t)p * a.hkv) * kMfmaRows + tr; };
+  float mx = -__builtin_inff();
+  for (int c = 0; c < ms.z; c += 64)
+    mx = fmaxf(mx, c + lane < ms.z ? a.mlse[rec(c + lane)] : -__builtin_inff());
+  mx = wave_max(mx);
+  float acc[E] = {}, wsum = 0.f;
+  for (int c = 0; c < ms.z; c += 64) {
+    const float lse = c + lane < ms.z ? a.mlse[rec(c + lane)] : -__builtin_inff();
+    const float wl = lse == -__builtin_inff() ? 0.f : fast_exp2(lse - mx);   // lane's part weight
+    const int n = min(64, ms.z - c);
+#pragma unroll 4
+    for (int j = 0; j < n; ++j) {
+      const float wt = __shfl(wl, j, 64);
+      wsum += wt;
+      const float* src = a.mpo + rec(c + j) * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(wt, src[e], acc[e]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  act_t* dst = (act_t*)a.out + ((int64_t)(si.q_start + row / G) * a.hq + (int64_t)h * G + row % G) * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) dst[e] = (act_t)(acc[e] * inv);
+}
+
+template <int D, int KV>
+static hipError_t prefill_merge_g(const AttnArgs& a, int g, int n, hipStream_t s) {
+  // workgroup x: split tile x / (hkv * GROUPS), head (x / GROUPS) % hkv, rows of group x % GROUPS
+  const dim3 grid(n * a.hkv * (kMfmaRows / kMergeRowsPerGroup));
+  constexpr int NT = 64 * kMergeRowsPerGroup;
+  switch (g) {
+    case 1: prefill_merge_kernel<D, 1, KV><<<grid, NT, 0, s>>>(a); break;
+    case 2: prefill_merge_kernel<D, 2, KV><<<grid, NT, 0, s>>>(a); break;
+    case 4: prefill_merge_kernel<D, 4, KV><<<grid, NT, 0, s>>>(a); break;
+    case 8: prefill_merge_kernel<D, 8, KV><<<grid, NT, 0, s>>>(a); break;
+    case 16: prefill_merge_kernel<D, 16, KV><<<grid, NT, 0, s>>>(a); break;
+    case 32: prefill_merge_kernel<D, 32, KV><<<grid, NT, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t prefill_merge_d(const AttnArgs& a, int g, int kv, int n, hipStream_t s) {
+  // the merged outputs take the type of q: bf16 for bf16 pools, fp16 otherwise
+  return kv == kKvBF16 ? prefill_merge_g<D, kKvBF16>(a, g, n, s) : prefill_merge_g<D, kKvF16>(a, g, n, s);
+}
+
+hipError_t launch_prefill_merge(const AttnArgs& a, int head_dim, int group, int kv, int n, hipStream_t s) {
+  return head_dim == 128 ? prefill_merge_d<128>(a, group, kv, n, s) : prefill_merge_d<64>(a, group, kv, n, s);
 }
 
 template <int D, int KV>

@@ -41,14 +41,16 @@ class AttendOpts(ctypes.Structure):
                 ("vector_begin", ctypes.c_void_p), ("vector_end", ctypes.c_void_p),
                 ("mfma_begin", ctypes.c_void_p), ("mfma_end", ctypes.c_void_p),
                 ("window", ctypes.c_int32), ("reuse_plan", ctypes.c_int32),
-                ("side_stream", ctypes.c_void_p), ("side_fork", ctypes.c_void_p), ("side_join", ctypes.c_void_p)]
+                ("side_stream", ctypes.c_void_p), ("side_fork", ctypes.c_void_p), ("side_join", ctypes.c_void_p),
+                ("mfma_split_steps", ctypes.c_int32)]
 
 
 class AttendInfo(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("vector_rows", ctypes.c_int32),
                 ("vector_units", ctypes.c_int32), ("max_parts", ctypes.c_int32),
                 ("mfma_tiles", ctypes.c_int32), ("plan_free", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("mfma_units", ctypes.c_int32),
+                ("mfma_split_steps", ctypes.c_int32)]
 
 
 _lib = None
@@ -231,11 +233,12 @@ def _hp(a: np.ndarray):
 
 
 def _opts(partition_tokens: int = 0, mfma_min_rows: int = 0, events=None, window: int = 0,
-          reuse_plan: bool = False, side=None) -> AttendOpts:
+          reuse_plan: bool = False, side=None, mfma_split_steps: int = 0) -> AttendOpts:
     ev = list(events) if events is not None else [None] * 4
     sd = list(side) if side is not None else [None] * 3
     return AttendOpts(int(partition_tokens), int(mfma_min_rows), *[None if e is None else int(e) for e in ev],
-                      int(window), int(bool(reuse_plan)), *[None if x is None else int(x) for x in sd])
+                      int(window), int(bool(reuse_plan)), *[None if x is None else int(x) for x in sd],
+                      int(mfma_split_steps))
 
 
 class PreparedCall:
@@ -290,12 +293,13 @@ def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None
 
 
 def pa_attend_workspace_bytes(k_cache, num_q_heads: int, h_seq_lens, h_q_lens,
-                              partition_tokens: int = 0, mfma_min_rows: int = 0, window: int = 0) -> int:
+                              partition_tokens: int = 0, mfma_min_rows: int = 0, window: int = 0,
+                              mfma_split_steps: int = 0) -> int:
     """Workspace bytes pa_attend needs for this batch (the same for every layer)."""
     lib = load_library()
     desc = cache_desc(k_cache)
     hl, hq = _host_i32(h_seq_lens), _host_i32(h_q_lens)
-    opts = _opts(partition_tokens, mfma_min_rows, window=window)
+    opts = _opts(partition_tokens, mfma_min_rows, window=window, mfma_split_steps=mfma_split_steps)
     n = lib.pa_attend_workspace_bytes(ctypes.byref(desc), int(num_q_heads), len(hl), _host_addr(hl),
                                       _host_addr(hq), ctypes.byref(opts))
     if n == 0:
@@ -304,14 +308,15 @@ def pa_attend_workspace_bytes(k_cache, num_q_heads: int, h_seq_lens, h_q_lens,
 
 
 def pa_attend_plan_info(k_cache, num_q_heads: int, h_seq_lens, h_q_lens, partition_tokens: int = 0,
-                        mfma_min_rows: int = 0, window: int = 0, layer: int = 0) -> dict:
+                        mfma_min_rows: int = 0, window: int = 0, layer: int = 0, mfma_split_steps: int = 0) -> dict:
     """How ``pa_attend`` would run this batch (decided from the host lengths;
     no device work): partition, vector rows and units, largest split, MFMA
-    row tiles, whether the plan kernel is skipped, workspace bytes."""
+    row tiles, whether the plan kernel is skipped, workspace bytes, MFMA
+    workgroups per KV head and the split of long row tiles."""
     lib = load_library()
     desc = cache_desc(k_cache, layer)
     hl, hq = _host_i32(h_seq_lens), _host_i32(h_q_lens)
-    opts = _opts(partition_tokens, mfma_min_rows, window=window)
+    opts = _opts(partition_tokens, mfma_min_rows, window=window, mfma_split_steps=mfma_split_steps)
     info = AttendInfo()
     _check(lib.pa_attend_plan_info(ctypes.byref(desc), int(num_q_heads), len(hl), _host_addr(hl), _host_addr(hq),
                                    ctypes.byref(opts), ctypes.byref(info)), "pa_attend_plan_info")
@@ -321,7 +326,8 @@ def pa_attend_plan_info(k_cache, num_q_heads: int, h_seq_lens, h_q_lens, partiti
 def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
                    out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
                    mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
-                   reuse_plan: bool = False, noalloc: bool = False, side=None) -> PreparedCall:
+                   reuse_plan: bool = False, noalloc: bool = False, side=None,
+                   mfma_split_steps: int = 0) -> PreparedCall:
     """``pa_attend`` as a prepared call (arguments as for ``pa_attend``; the
     output tensor is the call's ``keep[0]``).  ``h_seq_lens`` and ``h_q_lens``
     are passed by address: when they are int32 numpy arrays they are used in
@@ -352,7 +358,7 @@ def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_le
         _need(out, "out", _act_dtype(desc), 3)
         if out.shape != q.shape:
             raise ValueError("out must match q")
-    opts = _opts(partition_tokens, mfma_min_rows, events, window, reuse_plan, side)
+    opts = _opts(partition_tokens, mfma_min_rows, events, window, reuse_plan, side, mfma_split_steps)
     if noalloc:
         if workspace is not None:
             raise ValueError("pa_attend_noalloc takes no workspace")
@@ -377,7 +383,7 @@ def prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_le
 def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
               out=None, workspace=None, k_scale=None, v_scale=None, partition_tokens: int = 0,
               mfma_min_rows: int = 0, events=None, stream=None, window: int = 0, layer: int = 0,
-              reuse_plan: bool = False, side=None) -> torch.Tensor:
+              reuse_plan: bool = False, side=None, mfma_split_steps: int = 0) -> torch.Tensor:
     """Paged attention of the packed batch ``q [T, Hq, D]``; returns ``out [T, Hq, D]``
     (fp16; bf16 for bf16 pools).
 
@@ -388,10 +394,12 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
     step) left in ``workspace`` instead of planning again.
 
     ``events``: optional (vector_begin, vector_end, mfma_begin, mfma_end) raw
-    hipEvent_t handles (ints or None) recorded around the two attention kernels."""
+    hipEvent_t handles (ints or None) recorded around the two attention kernels.
+    ``mfma_split_steps``: split row tiles that walk more 64-key steps than
+    this (0: the library's choice, < 0: never)."""
     call = prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale, out,
                           workspace, k_scale, v_scale, partition_tokens, mfma_min_rows, events, stream, window,
-                          layer, reuse_plan, side=side)
+                          layer, reuse_plan, side=side, mfma_split_steps=mfma_split_steps)
     call()
     return call.keep[0]
 
@@ -399,13 +407,13 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
 def pa_attend_noalloc(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale: float,
                       out=None, k_scale=None, v_scale=None, partition_tokens: int = 0, mfma_min_rows: int = 0,
                       events=None, stream=None, window: int = 0, layer: int = 0,
-                      reuse_plan: bool = False) -> torch.Tensor:
+                      reuse_plan: bool = False, mfma_split_steps: int = 0) -> torch.Tensor:
     """``pa_attend`` on the library's fixed per-GPU scratch instead of a
     caller workspace (``pa_attend_noalloc``: the call allocates nothing; batches
     needing more than its size are refused; calls on one GPU must not overlap)."""
     call = prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale, out,
                           None, k_scale, v_scale, partition_tokens, mfma_min_rows, events, stream, window, layer,
-                          reuse_plan, noalloc=True)
+                          reuse_plan, noalloc=True, mfma_split_steps=mfma_split_steps)
     call()
     return call.keep[0]
 

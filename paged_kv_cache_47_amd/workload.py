@@ -181,7 +181,8 @@ class DeviceRun:
         if workspace is None:
             need = pa.pa_attend_workspace_bytes(self.k_cache, self.w.num_q_heads, x.batch.seq_lens,
                                                 x.batch.q_lens, opts.get("partition_tokens", 0),
-                                                opts.get("mfma_min_rows", 0), self.w.window)
+                                                opts.get("mfma_min_rows", 0), self.w.window,
+                                                opts.get("mfma_split_steps", 0))
             if self._ws is None or self._ws.numel() < need:
                 self._ws = torch.empty(2 * need, dtype=torch.uint8, device=self.device)
             workspace = self._ws
@@ -259,11 +260,15 @@ class StaticSteps:
         # The automatic split size depends on the batch's total keys, so steps with shorter true
         # lengths could pick a smaller partition and need more split units than the bound; fixing
         # the partition the bound gets keeps every step's units (and workspace) within it.
+        # The split of long row tiles is fixed the same way; with a window a tile's step count
+        # depends on the alignment of its window start, not only on the length, so there row
+        # tiles are never split.
+        info = pa.pa_attend_plan_info(run.k_cache, hq, self.h_len, self.h_ql, window=w.window)
         if self.partition_tokens == 0:
-            info = pa.pa_attend_plan_info(run.k_cache, hq, self.h_len, self.h_ql, window=w.window)
             self.partition_tokens = info["partition_tokens"] or -1
+        self.split_steps = -1 if w.window > 0 else (info["mfma_split_steps"] or -1)
         need = pa.pa_attend_workspace_bytes(run.k_cache, hq, self.h_len, self.h_ql, self.partition_tokens, 0,
-                                            w.window)
+                                            w.window, self.split_steps)
         self.ws = torch.empty(need, dtype=torch.uint8, device=run.device)
         self._lib = host._native()
         self._ok = host._ok
@@ -288,7 +293,8 @@ class StaticSteps:
             calls.append(pa.prepare_attend(self.q[layer], kc, vc, self.tables, self.seq_lens, self.q_lens,
                                            self.h_len, self.h_ql, w.scale, out=self.out[layer], workspace=self.ws,
                                            k_scale=ks, v_scale=vs, partition_tokens=self.partition_tokens,
-                                           window=w.window, layer=layer, reuse_plan=layer > 0))
+                                           window=w.window, layer=layer, reuse_plan=layer > 0,
+                                           mfma_split_steps=self.split_steps))
         return calls
 
     def set_activations(self, s: int = None, acts=None) -> None:

@@ -356,7 +356,7 @@ def config4(seed: int = 47004, num_requests: int = 64, prefix: int = 1024, min_s
 
 def config5(seed: int = 47005, num_chunks: int = 8, chunk_q: int = 512, max_chunk_ctx: int = 8192,
             num_decode: int = 192, max_decode_len: int = 32768, kv_dtype: str = "i8",
-            num_q_heads: int = 32) -> Workload:
+            num_q_heads: int = 32, chunk_ctx: Optional[int] = None) -> Workload:
     """Packed chunked prefill + decode over an int8 pool: ``num_chunks``
     segments of ``chunk_q`` query tokens with cached context U[0,8192], then
     ``num_decode`` decode sequences with post-write length U[1,32768].  The
@@ -367,10 +367,14 @@ def config5(seed: int = 47005, num_chunks: int = 8, chunk_q: int = 512, max_chun
     contents are N(0,1) (the context already in place, as in workload 3);
     with ``num_decode=0`` that is the chunks alone (the same contexts: they
     are drawn first).  ``num_q_heads`` 64 gives groups of eight query
-    heads per KV head (the same draws otherwise)."""
+    heads per KV head (the same draws otherwise).  ``chunk_ctx`` gives every
+    chunk that cached context instead of the draw (which is still made, so
+    the other draws stay the same)."""
     hq, hkv, d = num_q_heads, 8, 128
     rng = np.random.default_rng([seed, S_META])
     cctx = rng.integers(0, max_chunk_ctx + 1, num_chunks).astype(np.int64)
+    if chunk_ctx is not None:
+        cctx[:] = int(chunk_ctx)
     dpost = rng.integers(1, max_decode_len + 1, num_decode).astype(np.int64)
     ctx = np.concatenate([cctx, dpost - 1])
     q_lens = np.concatenate([np.full(num_chunks, chunk_q, np.int64), np.ones(num_decode, np.int64)])

@@ -300,3 +300,89 @@ def test_ceiling_calls_refuse_bad_arguments_on_the_host():
     assert lib.pa_ceiling_gather(fake, fake, 4, ids, 4, 16, 3, sink, None) == 2
     assert lib.pa_ceiling_gather(ctypes.c_void_p(4100), fake, 4, ids, 4, 16, 2, sink, None) == 2
     assert lib.pa_ceiling_gather(fake, fake, 4, ids, 1 << 40, 1, 2, sink, None) == 2   # grid beyond 2^31
+
+
+def _tile_steps(L, Q, g, r, window=0):
+    """64-key steps row tile r (256 rows) of a sequence walks: from the
+    64-aligned window start of its first row to its last row's position."""
+    rows = Q * g
+    last = min(rows, (r + 1) * 256) - 1
+    kmax = min(L, L - Q + last // g + 1)
+    first = L - Q + (r * 256) // g
+    lo = max(0, first - window + 1) if window > 0 else 0
+    k0 = lo & ~63
+    return -(-(kmax - k0) // 64)
+
+
+def _expected_units(lens, qls, g, split, window=0):
+    units = tiles = splits = slots = 0
+    for L, Q in zip(lens, qls):
+        if not (Q > 0 and Q * g >= 16):
+            continue
+        for r in range(-(-Q * g // 256)):
+            tiles += 1
+            st = _tile_steps(L, Q, g, r, window)
+            parts = -(-st // split) if split > 0 and st > split else 1
+            units += parts
+            if parts > 1:
+                splits += 1
+                slots += parts
+    return units, tiles, splits, slots
+
+
+def test_plan_info_splits_long_row_tiles():
+    """Row tiles walking more 64-key steps than the split are cut into equal
+    parts.  Automatic: a batch with fewer than 512 row-tile workgroups is split
+    at one workgroup's share of the row-tile work per compute unit (at least
+    16 steps), a larger one is not.  Also a fixed split, and never (-1); the
+    workspace grows by the parts' partial outputs (fp32 rows and log-sum-exps)."""
+    pool = _meta_pool(64, 8, 128)
+    g, hkv, d = 4, 8, 128
+    # three 512-query chunks with long contexts and one decode row: 24 tiles x 8 heads
+    ctx = [1715, 5354, 6645]
+    lens, qls = [c + 512 for c in ctx] + [3000], [512] * 3 + [1]
+    total = sum(_tile_steps(L, Q, g, r) for L, Q in zip(lens, qls) if Q * g >= 16 for r in range(-(-Q * g // 256)))
+    auto = max(16, -(-total * hkv // 256))
+    info = pa.pa_attend_plan_info(pool, 32, lens, qls)
+    units, tiles, splits, slots = _expected_units(lens, qls, g, auto)
+    assert info["mfma_split_steps"] == auto and info["mfma_tiles"] == tiles == 24
+    assert info["mfma_units"] == units > tiles and splits > 0
+    never = pa.pa_attend_plan_info(pool, 32, lens, qls, mfma_split_steps=-1)
+    assert never["mfma_split_steps"] == 0 and never["mfma_units"] == 24
+    extra = info["workspace_bytes"] - never["workspace_bytes"]
+    # int4 per unit twice (ordered and unordered lists), int4 per split tile, and per slot and KV head
+    # 256 rows of one log-sum-exp and d floats, each region 256-byte aligned
+    partials = slots * hkv * 256 * (d + 1) * 4
+    assert partials <= extra <= partials + 32 * (units - 24) + 16 * splits + 6 * 256
+    for split in (1, 2, 3, 7, 50):
+        fixed = pa.pa_attend_plan_info(pool, 32, lens, qls, mfma_split_steps=split)
+        assert fixed["mfma_units"] == _expected_units(lens, qls, g, split)[0]
+        assert fixed["mfma_split_steps"] == split
+    # with a window the walk starts at the step holding the first row's window start
+    win = pa.pa_attend_plan_info(pool, 32, lens, qls, window=700, mfma_split_steps=5)
+    assert win["mfma_units"] == _expected_units(lens, qls, g, 5, window=700)[0]
+    # short prompts stay whole: no tile walks more than the 16-step floor
+    short = pa.pa_attend_plan_info(pool, 32, [300] * 4, [300] * 4)
+    assert short["mfma_units"] == short["mfma_tiles"] == 4 * 5 and short["mfma_split_steps"] == 16
+    # a single long chunk spreads over more workgroups than its 8 tiles x 8 heads
+    one = pa.pa_attend_plan_info(pool, 32, [8192 + 512], [512])
+    assert one["mfma_tiles"] == 8 and one["mfma_units"] == _expected_units([8704], [512], g, one["mfma_split_steps"])[0]
+    assert one["mfma_units"] >= 4 * 8
+    # the packed batch of eight chunks (64 tiles x 8 heads = 512 workgroups) is not split
+    ctx8 = [254, 765, 1000, 1715, 1826, 5136, 5354, 6645]
+    packed = pa.pa_attend_plan_info(pool, 32, [c + 512 for c in ctx8] + [3000], [512] * 8 + [1])
+    assert packed["mfma_split_steps"] == 0 and packed["mfma_units"] == packed["mfma_tiles"] == 64
+
+
+def test_fixed_split_keeps_the_workspace_within_the_bound():
+    """With the row-tile split fixed to the bound's, shorter lengths never need
+    more workspace (without a window a tile's walk only shrinks with its length)."""
+    pool = _meta_pool(64, 8, 128)
+    S, W, q = 8, 700, 8
+    bound = pa.pa_attend_plan_info(pool, 32, [W * 16] * S, [q] * S)
+    split, part = bound["mfma_split_steps"], bound["partition_tokens"]
+    rng = np.random.default_rng(11)
+    for _ in range(50):
+        lens = rng.integers(q, W * 16 + 1, S)
+        need = pa.pa_attend_workspace_bytes(pool, 32, lens, [q] * S, part or -1, 0, 0, split or -1)
+        assert need <= bound["workspace_bytes"]

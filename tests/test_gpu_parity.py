@@ -47,8 +47,10 @@ def _check_step(run, ora, s, opts_list=({},), check_pool=True):
     return x
 
 
+# split-K of the decode rows at several partition sizes, and of the MFMA row
+# tiles into parts of one and two 64-key steps
 SPLITS = ({}, {"partition_tokens": 16}, {"partition_tokens": 64}, {"partition_tokens": 512},
-          {"partition_tokens": -1})
+          {"partition_tokens": -1}, {"mfma_split_steps": 1}, {"mfma_split_steps": 2, "partition_tokens": 64})
 
 
 def test_workload1_full():
