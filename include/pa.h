@@ -319,7 +319,11 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
  * address is looked up on the first call on each device, with that device
  * current).  The call itself allocates nothing.
  *   - A batch whose pa_attend_workspace_bytes exceeds PA_ATTEND_SCRATCH_BYTES
- *     returns PA_ERR_WORKSPACE, checked on the host before the GPU is used.
+ *     returns PA_ERR_WORKSPACE, checked on the host before the GPU is used;
+ *     except that when the excess comes from the automatic split of long
+ *     row tiles (opts NULL or mfma_split_steps 0), the call runs with row
+ *     tiles unsplit if that fits (the same results up to the merge's
+ *     rounding).
  *   - Every call on one GPU shares that GPU's array.  Calls that may overlap
  *     on the device (other streams, other threads) race on it and give wrong
  *     results; order them on one stream.  opts->reuse_plan = 1 takes the plan

@@ -732,9 +732,20 @@ extern "C" pa_status pa_attend_noalloc(const pa_cache_desc* desc, const void* q,
                                        const pa_attend_opts* opts, hipStream_t stream) {
   // the size check needs only the host arguments: an oversized batch is refused before the GPU is touched
   HostPlan P;
-  pa_status st = make_plan(desc, num_q_heads, num_seqs, h_seq_lens, h_q_lens,
-                           max_blocks_per_seq >= 0 ? max_blocks_per_seq : 0, opts, P);
+  const int32_t width = max_blocks_per_seq >= 0 ? max_blocks_per_seq : 0;
+  pa_status st = make_plan(desc, num_q_heads, num_seqs, h_seq_lens, h_q_lens, width, opts, P);
   if (st != PA_OK) return st;
+  // the automatic split of long row tiles adds partial outputs; without room for them the tiles stay whole
+  pa_attend_opts whole;
+  if (P.bytes > (size_t)PA_ATTEND_SCRATCH_BYTES && P.n_msplit > 0 && (opts == nullptr || opts->mfma_split_steps == 0)) {
+    if (opts) whole = *opts;
+    else std::memset(&whole, 0, sizeof(whole));
+    whole.mfma_split_steps = -1;
+    HostPlan unsplit;
+    if ((st = make_plan(desc, num_q_heads, num_seqs, h_seq_lens, h_q_lens, width, &whole, unsplit)) != PA_OK) return st;
+    P = unsplit;
+    opts = &whole;
+  }
   if (P.bytes > (size_t)PA_ATTEND_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
   if (P.total_q == 0) return PA_OK;
   void* ws = nullptr;

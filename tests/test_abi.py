@@ -386,3 +386,37 @@ def test_fixed_split_keeps_the_workspace_within_the_bound():
         lens = rng.integers(q, W * 16 + 1, S)
         need = pa.pa_attend_workspace_bytes(pool, 32, lens, [q] * S, part or -1, 0, 0, split or -1)
         assert need <= bound["workspace_bytes"]
+
+
+def test_noalloc_keeps_row_tiles_whole_when_their_split_does_not_fit():
+    """When only the automatic split of long row tiles takes a batch past
+    pa_attend_noalloc's 64 MiB scratch, the call keeps the tiles whole
+    instead of refusing: the call gets past the size check to the device
+    scratch lookup (PA_ERR_HIP without a GPU) or, with one, to the NULL
+    output (PA_ERR_NULL), never launching anything; a split the caller asked
+    for is refused as before (PA_ERR_WORKSPACE)."""
+    lib = pa.load_library()
+    d = _desc(num_blocks=1 << 16, num_kv_heads=8)
+    # 38 decode rows of 4096 keys in 64-key partitions (~40 MB of partials) and one
+    # 512-query chunk over 8192 cached keys, whose automatic split adds ~34 MB
+    hl = np.asarray([4096] * 38 + [8192 + 512], np.int32)
+    hq = np.asarray([1] * 38 + [512], np.int32)
+    auto, whole = pa.AttendOpts(), pa.AttendOpts()
+    auto.partition_tokens = whole.partition_tokens = 64
+    whole.mfma_split_steps = -1
+    info = pa.AttendInfo()
+    assert lib.pa_attend_plan_info(ctypes.byref(d), 32, len(hl), pa._hp(hl), pa._hp(hq), ctypes.byref(auto),
+                                   ctypes.byref(info)) == 0
+    assert info.mfma_units > info.mfma_tiles and info.workspace_bytes > (64 << 20)
+    assert lib.pa_attend_workspace_bytes(ctypes.byref(d), 32, len(hl), pa._hp(hl), pa._hp(hq),
+                                         ctypes.byref(whole)) <= (64 << 20)
+    fake = ctypes.c_void_p(256)
+
+    def call(o):   # out is NULL: no call can reach a kernel launch
+        return lib.pa_attend_noalloc(ctypes.byref(d), fake, 32, fake, fake, None, None, fake, 1024, fake, fake,
+                                     len(hl), pa._hp(hl), pa._hp(hq), ctypes.c_float(0.1), None, ctypes.byref(o),
+                                     None)
+    assert call(auto) in (1, 6)                   # PA_ERR_NULL (with a GPU) or PA_ERR_HIP (without)
+    forced = pa.AttendOpts()
+    forced.partition_tokens, forced.mfma_split_steps = 64, info.mfma_split_steps
+    assert call(forced) == 5                      # PA_ERR_WORKSPACE

@@ -40,7 +40,7 @@ def test_side_stream_equals_one_stream(dt):
     ora.write(0, slots, copies)
     ref = ora.attend(0)
     keep, side = _side()
-    for opts in ({}, {"partition_tokens": 128}):
+    for opts in ({}, {"partition_tokens": 128}, {"mfma_split_steps": 2}):   # the merge of split tiles runs there too
         want = run.attend(x, **opts).clone()
         got = run.attend(x, side=side, **opts)
         # the caller's stream alone orders what follows: read on it without a device-wide sync
