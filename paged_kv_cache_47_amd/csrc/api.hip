@@ -418,7 +418,7 @@ static pa_status make_plan(const pa_cache_desc* d, int32_t hq, int32_t num_seqs,
   P.off_po = off;
   if (split) off = align_up(off + sizeof(float) * (size_t)P.n_vunit * hq * d->head_dim, 256);
   P.off_row_u0 = off;
-  if (P.selfplan) off = align_up(off + sizeof(int32_t) * (size_t)num_seqs, 256);
+  if (P.selfplan) off = align_up(off + sizeof(int2) * (size_t)num_seqs, 256);
   P.bytes = off;
   return PA_OK;
 }
@@ -652,7 +652,7 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.selfplan = P.selfplan ? 1 : 0;
   a.num_seqs = num_seqs;
   a.n_units = (int32_t)P.n_vunit;
-  a.row_u0 = P.selfplan ? (int32_t*)(ws + P.off_row_u0) : nullptr;
+  a.row_u0 = P.selfplan ? (int2*)(ws + P.off_row_u0) : nullptr;
 
   auto mark = [&](hipEvent_t ev, hipStream_t s) { return ev == nullptr || hipEventRecord(ev, s) == hipSuccess; };
   // With a side stream the row tiles run there, beside the decode units on `stream`.

@@ -791,18 +791,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
 
 // Merge the split-K partials of one (query row, KV head): its G query heads,
 // base-2 log-sum-exp: out = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M).
+// The kernel is a short chain of dependent loads (where the row's units are,
+// then their log-sum-exps and partials), so the partials of the first
+// kPrefetch units are loaded before the weights are formed.
 template <int D, int G, typename OUT>
 __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const int h = blockIdx.y;
   int u0, parts;
   int64_t row0;
   if (a.selfplan) {
-    // grid x = sequence; its units start where its first unit recorded
-    const SPRow r = sp_row(a, blockIdx.x);
-    if (r.parts <= 1) return;
-    u0 = a.row_u0[blockIdx.x];
-    parts = r.parts;
-    if (u0 < 0 || u0 + parts > a.n_units) return;   // only if device and host lengths disagree
+    // grid x = sequence; its first unit recorded where the row's units are
+    // (written every call by that unit: one query row per sequence, each with units)
+    const int2 ru = a.row_u0[blockIdx.x];
+    u0 = ru.x;
+    parts = ru.y;
+    if (parts <= 1) return;
+    if (u0 < 0 || (int64_t)u0 + parts > a.n_units) return;   // only if device and host lengths disagree
     row0 = (int64_t)blockIdx.x * a.hq + (int64_t)h * G;
   } else {
     const VTok vt = a.vtok[blockIdx.x];
@@ -817,8 +821,20 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   // plain weighted sum of its partials (the element loop below otherwise
   // re-reads the log-sum-exps of every partial for each of the G * D elements).
   constexpr int kMaxParts = 64;
+  constexpr int kPer = (G * D + 255) / 256;   // output elements per thread
+  constexpr int kPrefetch = 4;
   __shared__ float wsh[G][kMaxParts];
   if (parts <= kMaxParts) {
+    float pre[kPer][kPrefetch];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int idx = threadIdx.x + 256 * k;
+      const int g = idx / D, d = idx % D;
+#pragma unroll
+      for (int p = 0; p < kPrefetch; ++p)
+        pre[k][p] = (idx < G * D && p < parts)
+                        ? a.po[((int64_t)(u0 + p) * a.hq + (int64_t)h * G + g) * D + d] : 0.f;
+    }
     for (int i = threadIdx.x; i < G * parts; i += 256)
       wsh[i / parts][i % parts] = a.plse[(int64_t)(u0 + i % parts) * a.hq + (int64_t)h * G + i / parts];
     __syncthreads();
@@ -835,11 +851,17 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
       for (int p = 0; p < parts; ++p) w[p] *= inv;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int idx = threadIdx.x + 256 * k;
+      if (idx >= G * D) break;
       const int g = idx / D, d = idx % D;
       const float* po = a.po + ((int64_t)u0 * a.hq + (int64_t)h * G + g) * D + d;
       float O = 0.f;
-      for (int p = 0; p < parts; ++p) O = fmaf(wsh[g][p], po[(int64_t)p * a.hq * D], O);
+#pragma unroll
+      for (int p = 0; p < kPrefetch; ++p)
+        if (p < parts) O = fmaf(wsh[g][p], pre[k][p], O);
+      for (int p = kPrefetch; p < parts; ++p) O = fmaf(wsh[g][p], po[(int64_t)p * a.hq * D], O);
       ((OUT*)a.out)[(row0 + g) * D + d] = (OUT)O;
     }
     return;

@@ -94,12 +94,12 @@ struct AttnArgs {
   int32_t direct;
   // selfplan != 0: a self-planned decode batch (see kSelfPlanMaxSeqs): decode
   // workgroup x takes the x-th unit of the bucketed order it derives from
-  // seq_lens / q_lens; the first unit of each row records its index in
-  // row_u0[row] for the merge kernel
+  // seq_lens / q_lens; the first unit of each row records its index and the
+  // row's unit count in row_u0[row] for the merge kernel
   int32_t selfplan;
   int32_t num_seqs;
   int32_t n_units;     // units of the launch (the decode grid's x extent)
-  int32_t* row_u0;     // [num_seqs]
+  int2* row_u0;        // [num_seqs] {first unit, units}
 };
 
 // First key a query at position `pos` sees (0 without a window).

@@ -138,7 +138,7 @@ __device__ __forceinline__ bool resolve_unit(const AttnArgs& a, int h, Unit& w) 
     w.kv_len = min(max(a.seq_lens[w.seq], 0), a.max_kv);
     w.q_len = 1;
     w.q_start = w.seq;   // one query row per sequence: packed row = sequence
-    if (w.part_idx == 0 && h == 0 && threadIdx.x == 0) a.row_u0[w.seq] = w.u;
+    if (w.part_idx == 0 && h == 0 && threadIdx.x == 0) a.row_u0[w.seq] = make_int2(w.u, w.parts);
   } else {
     w.u = a.vorder[blockIdx.x];   // units go out longest first
     const int2 un = a.vunit[w.u];
