@@ -22,43 +22,38 @@ constexpr int64_t kDirectMaxGroups = 1024;   // decode workgroups of a batch tha
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 // Exclusive scan of four counters over the workgroup (one sequence per
-// thread): wave-level shuffles, then the 16 wave totals through LDS.
+// thread): wave-level shuffles, then one wave scans the 16 wave totals and
+// every thread reads its wave's prefix back (one LDS read, instead of a loop
+// over the waves that kept 16 partial sums live and spilled registers).
+__device__ __forceinline__ int4 add4(int4 a, int4 b) { return make_int4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+__device__ __forceinline__ int4 shfl_up4(int4 v, int off) {
+  return make_int4(__shfl_up(v.x, off, 64), __shfl_up(v.y, off, 64), __shfl_up(v.z, off, 64), __shfl_up(v.w, off, 64));
+}
+
 __device__ int4 block_exclusive_scan4(int4 v, int4* lds, int4& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int4 inc = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    int4 t;
-    t.x = __shfl_up(inc.x, off, 64);
-    t.y = __shfl_up(inc.y, off, 64);
-    t.z = __shfl_up(inc.z, off, 64);
-    t.w = __shfl_up(inc.w, off, 64);
-    if (lane >= off) {
-      inc.x += t.x;
-      inc.y += t.y;
-      inc.z += t.z;
-      inc.w += t.w;
-    }
+    const int4 t = shfl_up4(inc, off);
+    if (lane >= off) inc = add4(inc, t);
   }
   if (lane == 63) lds[wave] = inc;
   __syncthreads();
-  int4 base = make_int4(0, 0, 0, 0);
-  total = make_int4(0, 0, 0, 0);
-  for (int w = 0; w < kPlanWaves; ++w) {
-    const int4 t = lds[w];
-    if (w < wave) {
-      base.x += t.x;
-      base.y += t.y;
-      base.z += t.z;
-      base.w += t.w;
+  if (wave == 0) {
+    int4 w = lane < kPlanWaves ? lds[lane] : make_int4(0, 0, 0, 0);
+#pragma unroll
+    for (int off = 1; off < kPlanWaves; off <<= 1) {
+      const int4 t = shfl_up4(w, off);
+      if (lane >= off) w = add4(w, t);
     }
-    total.x += t.x;
-    total.y += t.y;
-    total.z += t.z;
-    total.w += t.w;
+    if (lane < kPlanWaves) lds[lane] = w;   // inclusive prefixes of the wave totals
   }
   __syncthreads();
-  return make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
+  const int4 before = wave > 0 ? lds[wave - 1] : make_int4(0, 0, 0, 0);
+  total = lds[kPlanWaves - 1];
+  __syncthreads();   // the next scan reuses lds
+  return make_int4(before.x + inc.x - v.x, before.y + inc.y - v.y, before.z + inc.z - v.z, before.w + inc.w - v.w);
 }
 
 // Row-tile units of the MFMA path go out longest first.  A unit's cost is
