@@ -28,23 +28,10 @@ namespace pa {
 // operand read from LDS feeds two MFMAs.  Keys advance 64 at a time (four
 // 16-key blocks): the next 64-key K and V tiles are loaded from HBM into
 // registers while the current tiles in LDS are used, then written to the
-// other LDS buffers; one barrier per one (16-bit pools) or two (int8) steps.
-// The more waves share a tile, the less staging (loads, int8 conversion, LDS
-// stores) each wave does per step.
+// other LDS buffer; one barrier per step.  The more waves share a tile, the
+// less staging (loads, int8 conversion, LDS stores) each wave does per step.
 #ifndef PA_PF_PRIO
 #define PA_PF_PRIO 0   // 1: raise the wave's issue priority over the S = K Q^T products
-#endif
-// 64-key steps between barriers (1 or 2; 2 holds four K and four V tiles in
-// LDS, 147 KB at head dim 128).  Two halve the barriers and keep two tiles'
-// loads in flight, at 16-38 more registers: measured on the eight 512-query
-// chunks of the packed batch, int8 pools 0.270 -> 0.258 ms alone and 0.314
-// -> 0.300 ms inside the packed step (three runs each on one box), fp16
-// pools 0.238 -> 0.246 ms (and one fp16 chunk over 8192 keys 0.093 -> 0.096 ms).
-#ifndef PA_PF_SUB_I8
-#define PA_PF_SUB_I8 2
-#endif
-#ifndef PA_PF_SUB_16
-#define PA_PF_SUB_16 1
 #endif
 #ifndef PA_PF_PADK
 #define PA_PF_PADK 16  // K tile row padding (halves)
@@ -74,9 +61,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   constexpr int NCH = BN * CPR;                    // 16-byte chunks per tile
   constexpr int PT = NCH >= NTH ? NCH / NTH : 1;   // chunks per thread per tile
   static_assert(NCH % NTH == 0 || NTH % NCH == 0, "chunks must tile the workgroup");
-  constexpr int SUB = I8 ? PA_PF_SUB_I8 : PA_PF_SUB_16;   // 64-key steps between barriers
-  __shared__ __attribute__((aligned(16))) half_t ldk[2 * SUB][BN * LDK];  // [buffer]
-  __shared__ __attribute__((aligned(16))) half_t ldv[2 * SUB][BN * LDV];
+  __shared__ __attribute__((aligned(16))) half_t ldk[2][BN * LDK];  // [buffer]
+  __shared__ __attribute__((aligned(16))) half_t ldv[2][BN * LDV];
 
   const int id = blockIdx.x;
   const int h = id % a.hkv;         // consecutive workgroups = consecutive KV heads (one XCD each when hkv = 8)
@@ -136,14 +122,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
 
   // native vectors: an array of HIP's uint4 class type was kept in private memory (80 B per lane
   // of scratch traffic each step on 16-bit pools); these stay in registers
-  // The staging of one tile in flight: this thread's 16-byte chunks of K and
-  // V and, for int8 pools, the K scales of the tile's four 16-key blocks and
-  // the V scale of each chunk's block.
-  struct Stage {
-    u32x4_t k[PT], v[PT];
-    float nks[KB];
-    float nvc[PT];
-  };
+  u32x4_t stk[PT], stv[PT];
+  float nks[KB];  // int8: K scales of the four 16-key blocks of the tiles in flight
+  float nvc[PT];  // int8: V scale of the 16-key block of each of this thread's staging chunks
   // Physical blocks, read one step before the tiles they address: per 16-key
   // block of the step (int8: for its scales), and per staging chunk of this
   // wave (its 64 lanes cover 64 / CPR <= 16 aligned keys, one 16-key block).
@@ -175,13 +156,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   // needed.  Per lane only a 32-bit
   // offset inside the (block, head) tile varies; the tile base is scalar.
   constexpr int64_t kTileBytes = (int64_t)kBlockSize * D * EB;
-  auto gload = [&](int kt, const Blocks& t, Stage& sg) {
+  auto gload = [&](int kt, const Blocks& t) {
     if constexpr (I8) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int64_t sidx =
             (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.kb[kb]), a.num_blocks) * a.blk_tiles + h;
-        sg.nks[kb] = (float)(a.ks + sidx)[vz];
+        nks[kb] = (float)(a.ks + sidx)[vz];
       }
     }
 #pragma unroll
@@ -191,10 +172,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
       const int kg = min(max(kt + key, klo), L - 1);
       const int64_t tile =
           (int64_t)clamp_block(__builtin_amdgcn_readfirstlane(t.chunk[i]), a.num_blocks) * a.blk_tiles + h;
-      if constexpr (I8) sg.nvc[i] = (float)(a.vs + tile)[vz];
+      if constexpr (I8) nvc[i] = (float)(a.vs + tile)[vz];
       const uint32_t off = (uint32_t)((kg % kBlockSize) * D * EB + ch * 16);
-      sg.k[i] = *(const u32x4_t*)((const char*)a.kc + tile * kTileBytes + off);
-      sg.v[i] = *(const u32x4_t*)((const char*)a.vc + tile * kTileBytes + off);
+      stk[i] = *(const u32x4_t*)((const char*)a.kc + tile * kTileBytes + off);
+      stv[i] = *(const u32x4_t*)((const char*)a.vc + tile * kTileBytes + off);
     }
   };
   // int8 tiles become fp16: K as exact codes (its scale multiplies the
@@ -202,18 +183,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   // the weights that multiply V are the plain softmax weights.  The half keeps
   // 127 * scale finite (scale <= 65504 / 127 rounds up to 516); the output
   // takes the factor 2 back.
-  auto lstore = [&](int buf, const Stage& sg) {
+  auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int c = (threadIdx.x + NTH * i) % NCH;   // threads past the chunks repeat the first ones
       const int key = c / CPR, ch = c % CPR;
       if constexpr (I8) {
-        const half_t vh = (half_t)(0.5f * sg.nvc[i]);
+        const half_t vh = (half_t)(0.5f * nvc[i]);
         const half2_t vs2 = {vh, vh};
         half_t* kd = &ldk[buf][key * LDK + ch * 16];
         half_t* vd = &ldv[buf][key * LDV + ch * 16];
-        const uint32_t kw[4] = {sg.k[i][0], sg.k[i][1], sg.k[i][2], sg.k[i][3]};
-        const uint32_t vw[4] = {sg.v[i][0], sg.v[i][1], sg.v[i][2], sg.v[i][3]};
+        const uint32_t kw[4] = {stk[i][0], stk[i][1], stk[i][2], stk[i][3]};
+        const uint32_t vw[4] = {stv[i][0], stv[i][1], stv[i][2], stv[i][3]};
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           const half2_t a0 = sdwa_pair<0, 1>(kw[2 * c2], kw[2 * c2]), a1 = sdwa_pair<2, 3>(kw[2 * c2], kw[2 * c2]);
@@ -230,20 +211,27 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
           *(half8_t*)(vd + 8 * c2) = (half8_t){b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
         }
       } else {
-        *(u32x4_t*)&ldk[buf][key * LDK + ch * 8] = sg.k[i];
-        *(u32x4_t*)&ldv[buf][key * LDV + ch * 8] = sg.v[i];
+        *(u32x4_t*)&ldk[buf][key * LDK + ch * 8] = stk[i];
+        *(u32x4_t*)&ldv[buf][key * LDV + ch * 8] = stv[i];
       }
     }
   };
 
+  Blocks tn, tn2;
+  table(kbeg, tn);
+  gload(kbeg, tn);
+  lstore(0);
+  table(kbeg + BN, tn);
+  __syncthreads();
   typedef __attribute__((address_space(3))) short4_t lds_short4;
+  int buf = 0;
   const act8_t kOnes8 = (act8_t)(act_t)1.0f;
 
-  // One 64-key step at key kt, tiles in LDS buffer buf, score scales cks:
-  // S = K Q^T for the four 16-key blocks (this lane: query row l16 of each
-  // row block, keys 16*kb + 4*grp + e), the online-softmax max, then the fp16
-  // weights and O^T += V^T P^T per 32-key half, so that the second half's
-  // vector work sits beside the first half's matrix products.
+  // One 64-key step: S = K Q^T for the four 16-key blocks (this lane: query
+  // row l16 of each row block, keys 16*kb + 4*grp + e), the online-softmax
+  // max, then the fp16 weights and O^T += V^T P^T per 32-key half, so that the
+  // second half's vector work sits beside the first half's matrix products,
+  // and the next tiles' staging beside the second half's.
   //
   // Only steps that reach past this wave's first query position, or start
   // before its last row's window does, need the mask (a wave-uniform test);
@@ -252,140 +240,112 @@ __global__ __launch_bounds__(64 * kMfmaWaves, 8 / kMfmaWaves) void prefill_kerne
   // are positive), and the scale rides in the exponent's FMA.  The running max
   // moves only when a score exceeds it by more than kRescalePf (log2 units),
   // so the accumulators are rescaled rarely.
-  auto step = [&](const int kt, const int buf, const float (&cks)[KB]) {
-      // S^T = K Q^T, k-step outer so the eight accumulators interleave, with the
-      // next k-step's four K operands read from LDS while this one's products run
-      float4_t s[RB][KB];
-      act8_t kq[2][KB];
+  for (int kt = kbeg; kt < kend; kt += BN, buf ^= 1) {
+    const bool more = kt + BN < kend;
+    // score scale per 16-key block (base 2; int8 folds in the block's K scale).  A zero K scale
+    // (an all-zero block) becomes the least normal float: its scores stay 0, and -inf stays -inf.
+    float cks[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) cks[kb] = I8 ? fmaxf(a.scale_log2 * nks[kb], 1.17549435e-38f) : a.scale_log2;
+    // the staging at the end of the step is unconditional, so it can share a block with the
+    // matrix work; after the last step it rewrites the idle buffer with tiles nothing reads
+    if (more) {
+      gload(kt + BN, tn);
+      table(kt + 2 * BN, tn2);
+    }
+
+    // S^T = K Q^T, k-step outer so the eight accumulators interleave, with the
+    // next k-step's four K operands read from LDS while this one's products run
+    float4_t s[RB][KB];
+    act8_t kq[2][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      kq[0][kb] = __builtin_bit_cast(act8_t, *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + 8 * grp]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          kq[(ks + 1) & 1][kb] = __builtin_bit_cast(
+              act8_t, *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + (ks + 1) * 32 + 8 * grp]);
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        kq[0][kb] = __builtin_bit_cast(act8_t, *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + 8 * grp]);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
+        for (int rb = 0; rb < RB; ++rb)
+          s[rb][kb] = mfma16x16x32(kq[ks & 1][kb], qop[rb][ks], ks == 0 ? (float4_t)0.f : s[rb][kb]);
+    }
+    if (kt + BN - 1 > qmin || kt < wlo_last) {
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-            kq[(ks + 1) & 1][kb] = __builtin_bit_cast(
-                act8_t, *(const half8_t*)&ldk[buf][(kb * 16 + l16) * LDK + (ks + 1) * 32 + 8 * grp]);
-        }
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            s[rb][kb] = mfma16x16x32(kq[ks & 1][kb], qop[rb][ks], ks == 0 ? (float4_t)0.f : s[rb][kb]);
+          for (int e = 0; e < 4; ++e) {
+            const int key = kt + kb * 16 + 4 * grp + e;
+            if (key > qpos[rb] || key < qlo[rb]) s[rb][kb][e] = -__builtin_inff();
+          }
+    }
+    // Each lane tests its own 16 scores against its row's running max; only
+    // when some score of the wave exceeds it by more than kRescalePf are the
+    // row maxima formed across the row's four lanes and the rows rescaled.
+    float mloc[RB];
+    bool grow = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float mb = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const float r = fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3]));
+        mb = fmaxf(mb, r * cks[kb]);
       }
-      if (kt + BN - 1 > qmin || kt < wlo_last) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int key = kt + kb * 16 + 4 * grp + e;
-              if (key > qpos[rb] || key < qlo[rb]) s[rb][kb][e] = -__builtin_inff();
-            }
-      }
-      // Each lane tests its own 16 scores against its row's running max; only
-      // when some score of the wave exceeds it by more than kRescalePf are the
-      // row maxima formed across the row's four lanes and the rows rescaled.
-      float mloc[RB];
-      bool grow = false;
+      mloc[rb] = mb;
+      grow |= mb > m[rb] + kRescalePf;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float mb = -__builtin_inff();
+        float mb = fmaxf(mloc[rb], __shfl_xor(mloc[rb], 16, 64));
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const bool g = mb > m[rb] + kRescalePf;   // the same for the row's four lanes
+        const float al = g ? fast_exp2(m[rb] - mb) : 1.f;
+        m[rb] = g ? mb : m[rb];
+        lsum[rb] *= al;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const float r = fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3]));
-          mb = fmaxf(mb, r * cks[kb]);
-        }
-        mloc[rb] = mb;
-        grow |= mb > m[rb] + kRescalePf;
-      }
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          float mb = fmaxf(mloc[rb], __shfl_xor(mloc[rb], 16, 64));
-          mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-          const bool g = mb > m[rb] + kRescalePf;   // the same for the row's four lanes
-          const float al = g ? fast_exp2(m[rb] - mb) : 1.f;
-          m[rb] = g ? mb : m[rb];
-          lsum[rb] *= al;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) o[rb][nt] *= al;
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < KB / 2; ++hh) {
-        // this half's V operands (transposing LDS reads) are requested before its weights are formed
-        act8_t vq[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const half_t* p1 = &ldv[buf][(hh * 32 + 4 * grp + (l16 >> 2)) * LDV + nt * 16 + 4 * (l16 & 3)];
-          const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
-          const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1 + 16 * LDV));
-          const half4_t h1 = __builtin_bit_cast(half4_t, v1), h2 = __builtin_bit_cast(half4_t, v2);
-          vq[nt] = __builtin_bit_cast(act8_t, (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w});
-        }
-        act8_t p[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            // slot j of the k-step: keys 4*grp + [0..3] of the half's first and second 16-key block
-            const int kb = 2 * hh + j / 4;
-            p[rb][j] = (act_t)fast_exp2(fmaf(s[rb][kb][j % 4], cks[kb], -m[rb]));
-          }
-          // row sums of exactly the weights the product uses: ones^T P^T on the matrix cores
-          lsum[rb] = mfma16x16x32(kOnes8, p[rb], lsum[rb]);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) o[rb][nt] = mfma16x16x32(vq[nt], p[rb], o[rb][nt]);
-      }
-  };
-  // score scale per 16-key block (base 2; int8 folds in the block's K scale).  A zero K scale
-  // (an all-zero block) becomes the least normal float: its scores stay 0, and -inf stays -inf.
-  auto step_scales = [&](const Stage& sg, float (&cks)[KB]) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) cks[kb] = I8 ? fmaxf(a.scale_log2 * sg.nks[kb], 1.17549435e-38f) : a.scale_log2;
-  };
-
-  // SUB 64-key steps between barriers: their tiles sit in buffers
-  // SUB * pair + sub, and the next SUB tiles are loaded into registers at the
-  // start and stored into the other pair at the end, then one barrier.  The
-  // stores are unconditional, so they can share a block with the matrix work;
-  // a tile past the range rewrites a buffer nothing reads.
-  Stage sg[SUB] = {};
-  Blocks tn[SUB], tn2[SUB];
-#pragma unroll
-  for (int j = 0; j < SUB; ++j) {
-    table(kbeg + j * BN, tn[j]);
-    if (j == 0 || kbeg + j * BN < kend) gload(kbeg + j * BN, tn[j], sg[j]);
-    lstore(j, sg[j]);
-    table(kbeg + (SUB + j) * BN, tn[j]);
-  }
-  __syncthreads();
-  int pair = 0;
-  for (int kt = kbeg; kt < kend; kt += SUB * BN, pair ^= 1) {
-    float cks[SUB][KB];
-#pragma unroll
-    for (int j = 0; j < SUB; ++j) step_scales(sg[j], cks[j]);
-#pragma unroll
-    for (int j = 0; j < SUB; ++j) {
-      if (kt + (SUB + j) * BN < kend) {
-        gload(kt + (SUB + j) * BN, tn[j], sg[j]);
-        table(kt + (2 * SUB + j) * BN, tn2[j]);
+        for (int nt = 0; nt < NT; ++nt) o[rb][nt] *= al;
       }
     }
 #pragma unroll
-    for (int j = 0; j < SUB; ++j)
-      if (j == 0 || kt + j * BN < kend) step(kt + j * BN, SUB * pair + j, cks[j]);
+    for (int hh = 0; hh < KB / 2; ++hh) {
+      // this half's V operands (transposing LDS reads) are requested before its weights are formed
+      act8_t vq[NT];
 #pragma unroll
-    for (int j = 0; j < SUB; ++j) {
-      lstore(SUB * (pair ^ 1) + j, sg[j]);
-      if (kt + (SUB + j) * BN < kend) tn[j] = tn2[j];
+      for (int nt = 0; nt < NT; ++nt) {
+        const half_t* p1 = &ldv[buf][(hh * 32 + 4 * grp + (l16 >> 2)) * LDV + nt * 16 + 4 * (l16 & 3)];
+        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
+        const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1 + 16 * LDV));
+        const half4_t h1 = __builtin_bit_cast(half4_t, v1), h2 = __builtin_bit_cast(half4_t, v2);
+        vq[nt] = __builtin_bit_cast(act8_t, (half8_t){h1.x, h1.y, h1.z, h1.w, h2.x, h2.y, h2.z, h2.w});
+      }
+      act8_t p[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // slot j of the k-step: keys 4*grp + [0..3] of the half's first and second 16-key block
+          const int kb = 2 * hh + j / 4;
+          p[rb][j] = (act_t)fast_exp2(fmaf(s[rb][kb][j % 4], cks[kb], -m[rb]));
+        }
+        // row sums of exactly the weights the product uses: ones^T P^T on the matrix cores
+        lsum[rb] = mfma16x16x32(kOnes8, p[rb], lsum[rb]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][nt] = mfma16x16x32(vq[nt], p[rb], o[rb][nt]);
     }
+    lstore(buf ^ 1);
+    if (more) tn = tn2;
     __syncthreads();
   }
 
