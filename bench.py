@@ -584,6 +584,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the HBM read ceilings (stream read, random 4 KiB tile gather) in the JSON line")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--fused-write", action="store_true",
+                    help="issue each layer's write and attention as one pa_write_attend call")
     ap.add_argument("--mfma-split-steps", type=int, default=0,
                     help="split row tiles walking more 64-key steps than this (0: the library's choice, -1: never)")
     ap.add_argument("--cold", type=int, default=-1, choices=(-1, 0, 1),
@@ -738,12 +740,16 @@ def main(argv=None) -> int:
         for layer in range(w.num_layers):
             nk, nv, q = run.layer_acts(x, layer)
             ev = tuple(evs.handle(4 * i + j) for j in range(4)) if (timed_kernel and layer == 0) else None
+            att = dict(out=outs[layer], workspace=ws, k_scale=ks, v_scale=vs, partition_tokens=args.partition_tokens,
+                       events=ev, window=w.window, layer=layer, reuse_plan=layer > 0, side=side,
+                       mfma_split_steps=args.mfma_split_steps)
+            if args.fused_write:
+                calls.append(pa.prepare_write_attend(nk, nv, x.slot_mapping, q, kc, vc, x.block_tables, x.seq_lens,
+                                                     x.q_lens, x.batch.seq_lens, x.batch.q_lens, w.scale, **att))
+                continue
             calls.append(pa.prepare_write_kv(nk, nv, x.slot_mapping, kc, vc, ks, vs, layer=layer))
             calls.append(pa.prepare_attend(q, kc, vc, x.block_tables, x.seq_lens, x.q_lens, x.batch.seq_lens,
-                                           x.batch.q_lens, w.scale, out=outs[layer], workspace=ws, k_scale=ks,
-                                           v_scale=vs, partition_tokens=args.partition_tokens, events=ev,
-                                           window=w.window, layer=layer, reuse_plan=layer > 0, side=side,
-                                           mfma_split_steps=args.mfma_split_steps))
+                                           x.batch.q_lens, w.scale, **att))
         return calls
 
     prepared = {(i, tk): step_calls(i, tk) for i in range(n) for tk in (True, False)}
@@ -872,6 +878,7 @@ def main(argv=None) -> int:
                    + (f" [{args.w3_q_heads} query heads]" if args.w3_q_heads != 32 else "")
                    + (f" [{args.w5_q_heads} query heads]" if args.w5_q_heads != 32 else "")
                    + (" [row tiles on a side stream]" if args.side_stream else "")
+                   + (" [write and attention as one call]" if args.fused_write else "")
                    + (f" [{args.w5_pool} pool with N(0,1) contents]" if args.w5_pool != "i8" else "")
                    + (f" [{args.w5_chunks} chunks]" if args.w5_chunks != 8 else "")
                    + (f" [every chunk over {args.w5_chunk_ctx} cached keys]" if args.w5_chunk_ctx >= 0 else "")

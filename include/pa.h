@@ -310,6 +310,34 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
                     const pa_attend_opts* opts, hipStream_t stream);
 
 /*
+ * pa_write_attend - pa_write_kv followed by pa_attend on the same stream, as
+ * one call (the arguments of both; the write's k, v, slot_mapping, num_tokens
+ * first).  Results are those of the two calls.  For a decode step ([pytorch]
+ * "How to implement paged attention: the minimal data flow": write the new
+ * token's K/V, then attend over the sequence including it) the write runs
+ * inside the attention kernel: when the pool is fp16 or bf16, every sequence
+ * has exactly one query row (h_q_lens all 1), num_tokens == num_seqs and the
+ * rows take the decode units (no row tiles, group below 16), the workgroup
+ * that walks a row's last key writes the row's new K and V for its KV head
+ * before it loads any tile, which saves the write kernel's launch.  That form
+ * requires token i to be the new token of sequence i: slot_mapping[i] is the
+ * slot of position seq_lens[i] - 1 of sequence i (the slot its table
+ * names); otherwise results are undefined (no access outside the pools).
+ * Any other batch (int8 pools, several query rows, row tiles) runs the two
+ * calls.  Debug builds always run the two calls, each with its metadata
+ * check.  Errors: those of pa_write_kv and pa_attend; a refused fused call
+ * enqueues nothing.
+ */
+pa_status pa_write_attend(const pa_cache_desc* desc, const void* k, const void* v,
+                          const int32_t* slot_mapping, int32_t num_tokens,
+                          const void* q, int32_t num_q_heads, void* k_cache, void* v_cache,
+                          void* k_scale, void* v_scale, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens, const int32_t* q_lens,
+                          int32_t num_seqs, const int32_t* h_seq_lens, const int32_t* h_q_lens,
+                          float scale, void* out, void* workspace, size_t workspace_bytes,
+                          const pa_attend_opts* opts, hipStream_t stream);
+
+/*
  * pa_attend_noalloc - pa_attend without a workspace argument, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Arguments, results and errors are

@@ -546,11 +546,26 @@ pa_status pa_attend_plan_info(const pa_cache_desc* desc, int32_t num_q_heads, in
   return PA_OK;
 }
 
-pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_heads, const void* k_cache,
-                    const void* v_cache, const void* k_scale, const void* v_scale, const int32_t* block_tables,
-                    int32_t max_blocks_per_seq, const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
-                    const int32_t* h_seq_lens, const int32_t* h_q_lens, float scale, void* out, void* workspace,
-                    size_t workspace_bytes, const pa_attend_opts* opts, hipStream_t stream) {
+}  // extern "C"
+
+namespace pa {
+
+// The new rows of a fused write (pa_write_attend): token i is the new token of
+// sequence i.  NULL k: no fused write.
+struct FusedWrite {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* slots = nullptr;
+};
+
+// pa_attend, with the KV write of a fused call folded into the decode units
+// when the batch takes them alone (otherwise the write kernel runs first).
+static pa_status attend_impl(const pa_cache_desc* desc, const void* q, int32_t num_q_heads, const void* k_cache,
+                             const void* v_cache, const void* k_scale, const void* v_scale,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                             const int32_t* q_lens, int32_t num_seqs, const int32_t* h_seq_lens,
+                             const int32_t* h_q_lens, float scale, void* out, void* workspace, size_t workspace_bytes,
+                             const pa_attend_opts* opts, hipStream_t stream, FusedWrite fw) {
   pa_status st = check_desc(desc);
   if (st != PA_OK) return st;
   if (max_blocks_per_seq < 0) return PA_ERR_SHAPE;
@@ -648,6 +663,18 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
   a.num_seqs = num_seqs;
   a.n_units = (int32_t)P.n_vunit;
   a.row_u0 = P.selfplan ? (int2*)(ws + P.off_row_u0) : nullptr;
+  a.new_k = a.new_v = nullptr;
+  a.new_slots = nullptr;
+  if (fw.k != nullptr) {
+    if (P.n_munit == 0 && g < 16) {
+      a.new_k = fw.k;
+      a.new_v = fw.v;
+      a.new_slots = fw.slots;
+    } else if (launch_write_f16(*desc, fw.k, fw.v, fw.slots, num_seqs, const_cast<void*>(k_cache),
+                                const_cast<void*>(v_cache), stream) != hipSuccess) {
+      return PA_ERR_HIP;   // rows on the matrix cores: the write kernel first, as pa_write_kv
+    }
+  }
 
   auto mark = [&](hipEvent_t ev, hipStream_t s) { return ev == nullptr || hipEventRecord(ev, s) == hipSuccess; };
   // With a side stream the row tiles run there, beside the decode units on `stream`.
@@ -681,6 +708,51 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
     return PA_ERR_HIP;
   }
   return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_heads, const void* k_cache,
+                    const void* v_cache, const void* k_scale, const void* v_scale, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
+                    const int32_t* h_seq_lens, const int32_t* h_q_lens, float scale, void* out, void* workspace,
+                    size_t workspace_bytes, const pa_attend_opts* opts, hipStream_t stream) {
+  return attend_impl(desc, q, num_q_heads, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                     seq_lens, q_lens, num_seqs, h_seq_lens, h_q_lens, scale, out, workspace, workspace_bytes, opts,
+                     stream, FusedWrite{});
+}
+
+pa_status pa_write_attend(const pa_cache_desc* desc, const void* k, const void* v, const int32_t* slot_mapping,
+                          int32_t num_tokens, const void* q, int32_t num_q_heads, void* k_cache, void* v_cache,
+                          void* k_scale, void* v_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, const int32_t* q_lens, int32_t num_seqs,
+                          const int32_t* h_seq_lens, const int32_t* h_q_lens, float scale, void* out,
+                          void* workspace, size_t workspace_bytes, const pa_attend_opts* opts, hipStream_t stream) {
+  // The fused form: a 16-bit pool, one new token and one query row per
+  // sequence, the token of sequence i at index i, the write's own arguments
+  // valid.  Debug builds always take the two calls, so that each one's
+  // metadata check runs.
+  bool fused = !PA_DEBUG && check_desc(desc) == PA_OK && desc->kv_dtype != PA_KV_I8 && num_seqs > 0 &&
+               num_tokens == num_seqs && h_q_lens != nullptr && k && v && slot_mapping && k_cache && v_cache &&
+               aligned(k, 16) && aligned(v, 16) && aligned(slot_mapping, 4) && aligned(k_cache, 16) &&
+               aligned(v_cache, 16);
+  for (int32_t i = 0; fused && i < num_seqs; ++i) fused = h_q_lens[i] == 1;
+  if (!fused) {
+    const pa_status st = pa_write_kv(desc, k, v, slot_mapping, num_tokens, k_cache, v_cache, k_scale, v_scale, stream);
+    if (st != PA_OK) return st;
+    return pa_attend(desc, q, num_q_heads, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                     seq_lens, q_lens, num_seqs, h_seq_lens, h_q_lens, scale, out, workspace, workspace_bytes, opts,
+                     stream);
+  }
+  FusedWrite fw;
+  fw.k = k;
+  fw.v = v;
+  fw.slots = slot_mapping;
+  return attend_impl(desc, q, num_q_heads, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                     seq_lens, q_lens, num_seqs, h_seq_lens, h_q_lens, scale, out, workspace, workspace_bytes, opts,
+                     stream, fw);
 }
 
 }  // extern "C"

@@ -206,6 +206,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   const int64_t row0 = (int64_t)(q_start + t) * a.hq + (int64_t)h * G;
   const int32_t* tbl = a.block_tables + (int64_t)seq * a.max_blocks;
 
+  // Fused KV write: the unit that walks the row's last key (the new token's
+  // position) writes the token's K and V rows of this KV head into its slot
+  // before any tile is loaded, and the barrier orders every wave's loads of
+  // that block after the store.  No other unit reads the slot: it lies past
+  // the row's other units and belongs to this sequence alone.
+  if constexpr (!I8) {
+    if (a.new_k != nullptr && kend == un.kv_len) {
+      constexpr int CH = D * EB / 16;   // 16-byte chunks of one row
+      const int64_t tok = (int64_t)q_start + t;
+      const int32_t slot = a.new_slots[tok];
+      if (threadIdx.x < 2 * CH && slot >= 0 && (int64_t)slot < (int64_t)a.num_blocks * kBlockSize) {
+        const bool isv = threadIdx.x >= CH;
+        const int c = threadIdx.x % CH;
+        const uint4* src = (const uint4*)((const act_t*)(isv ? a.new_v : a.new_k) + (tok * a.hkv + h) * D) + c;
+        const int64_t tile = (int64_t)(slot / kBlockSize) * a.blk_tiles + h;
+        // the pools are the caller's writable memory; the attention reads them through const pointers
+        uint4* dst = (uint4*)((char*)const_cast<void*>(isv ? a.vc : a.kc) + tile * TILE +
+                              (int64_t)(slot % kBlockSize) * D * EB) + c;
+        *dst = *src;
+      }
+      __syncthreads();
+    }
+  }
+
   act2_t qh[QLDS ? 1 : G][E2];
   if constexpr (QLDS) {
     // the workgroup's G rows are contiguous: G * D / 8 chunks of 16 bytes

@@ -100,6 +100,14 @@ struct AttnArgs {
   int32_t num_seqs;
   int32_t n_units;     // units of the launch (the decode grid's x extent)
   int2* row_u0;        // [num_seqs] {first unit, units}
+  // Fused KV write (pa_write_attend; NULL otherwise): a batch of one query row
+  // per sequence over a 16-bit pool, token i the new token of sequence i.  The
+  // unit that walks a row's last key first writes the token's K and V rows of
+  // its KV head into slot new_slots[i] of the pools (kc / vc, the same memory
+  // the attention reads).
+  const void* new_k;   // [num_seqs][hkv][D], the type of q
+  const void* new_v;
+  const int32_t* new_slots;
 };
 
 // First key a query at position `pos` sees (0 without a window).

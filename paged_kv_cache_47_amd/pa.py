@@ -99,6 +99,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.pa_attend_noalloc.argtypes = [pdesc, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp,
                                       ctypes.c_float, vp, popts, vp]
     lib.pa_attend_noalloc.restype = ctypes.c_int
+    lib.pa_write_attend.argtypes = [pdesc, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp,
+                                    ctypes.c_float, vp, vp, sz, popts, vp]
+    lib.pa_write_attend.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [pdesc, vp, vp, vp, vp, vp, i32, vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_status_str.argtypes = [ctypes.c_int]
@@ -400,6 +403,36 @@ def pa_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h
     call = prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale, out,
                           workspace, k_scale, v_scale, partition_tokens, mfma_min_rows, events, stream, window,
                           layer, reuse_plan, side=side, mfma_split_steps=mfma_split_steps)
+    call()
+    return call.keep[0]
+
+
+def prepare_write_attend(k, v, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens,
+                         h_q_lens, scale: float, out=None, workspace=None, k_scale=None, v_scale=None,
+                         partition_tokens: int = 0, mfma_min_rows: int = 0, events=None, stream=None, window: int = 0,
+                         layer: int = 0, reuse_plan: bool = False, side=None,
+                         mfma_split_steps: int = 0) -> PreparedCall:
+    """``pa_write_attend``: ``pa_write_kv`` of ``k, v [T, Hkv, D]`` through
+    ``slot_mapping`` followed by ``pa_attend``, as one prepared call (for a
+    decode step over a 16-bit pool, token i the new token of sequence i, the
+    write runs inside the attention kernel).  The output tensor is the call's
+    ``keep[0]``."""
+    att = prepare_attend(q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens, scale, out,
+                         workspace, k_scale, v_scale, partition_tokens, mfma_min_rows, events, stream, window, layer,
+                         reuse_plan, side=side, mfma_split_steps=mfma_split_steps)
+    wr = prepare_write_kv(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream, layer)
+    lib = load_library()
+    # pa_write_kv's (desc, k, v, slots, T) then pa_attend's arguments after its descriptor
+    args = wr.args[:5] + att.args[1:]
+    return PreparedCall(lib.pa_write_attend, args, "pa_write_attend", att.keep + wr.keep)
+
+
+def pa_write_attend(k, v, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens, h_q_lens,
+                    scale: float, **kw) -> torch.Tensor:
+    """``pa_write_kv`` then ``pa_attend`` as one call (keyword arguments as
+    for ``pa_attend``); returns ``out``."""
+    call = prepare_write_attend(k, v, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, q_lens, h_seq_lens,
+                                h_q_lens, scale, **kw)
     call()
     return call.keep[0]
 

@@ -420,3 +420,24 @@ def test_noalloc_keeps_row_tiles_whole_when_their_split_does_not_fit():
     forced = pa.AttendOpts()
     forced.partition_tokens, forced.mfma_split_steps = 64, info.mfma_split_steps
     assert call(forced) == 5                      # PA_ERR_WORKSPACE
+
+
+def test_write_attend_refuses_before_enqueueing():
+    """pa_write_attend's host checks: a fused decode step with too small a
+    workspace is PA_ERR_WORKSPACE and nothing runs (the write would have run
+    inside the attention kernel); a batch that takes the two calls reports
+    the write's own errors first (int8 without scales: PA_ERR_NULL).  The
+    addresses here are never dereferenced."""
+    lib = pa.load_library()
+    d = _desc(num_kv_heads=2)
+    L, Q = np.asarray([5, 9], np.int32), np.asarray([1, 1], np.int32)
+    f = ctypes.c_void_p(4096)
+    o = pa.AttendOpts()
+
+    def call(desc, ws_bytes, scales=None):
+        return lib.pa_write_attend(ctypes.byref(desc), f, f, f, 2, f, 4, f, f, scales, scales, f, 4, f, f, 2,
+                                   pa._hp(L), pa._hp(Q), ctypes.c_float(0.1), f, f, ws_bytes, ctypes.byref(o), None)
+    assert call(d, 8) == 5
+    assert call(_desc(num_kv_heads=2, kv_dtype=1), 1 << 20) == 1
+    assert lib.pa_write_attend(None, f, f, f, 2, f, 4, f, f, None, None, f, 4, f, f, 2, pa._hp(L), pa._hp(Q),
+                               ctypes.c_float(0.1), f, f, 1 << 20, ctypes.byref(o), None) == 1
