@@ -94,3 +94,14 @@ def test_split_tiles_without_a_workspace():
     assert torch.equal(out, ref)
     from tests.oracle_side import assert_attn_close, dev_np
     assert_attn_close(dev_np(out), ora.attend(0), "f16", "noalloc split")
+
+
+def test_more_parts_than_one_wave_of_lanes():
+    # a 64-query chunk over ~5000 cached keys cut into one-step parts: ~80 parts per tile, more
+    # than the 64 log-sum-exps the merge takes per pass
+    from paged_kv_cache_47_amd import pa
+    w = synthetic.custom(730, [5100, 300], [64, 1], 16, 4, 128)
+    run = _run(w)
+    info = pa.pa_attend_plan_info(run.k_cache, 16, [5100, 300], [64, 1], mfma_split_steps=1)
+    assert info["mfma_units"] >= 65 * info["mfma_tiles"]
+    _check_step(run, OracleSide(w), 0, ({"mfma_split_steps": 1}, {"mfma_split_steps": 2}))
