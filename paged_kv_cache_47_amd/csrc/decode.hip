@@ -207,26 +207,33 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
   const int32_t* tbl = a.block_tables + (int64_t)seq * a.max_blocks;
 
   // Fused KV write: the unit that walks the row's last key (the new token's
-  // position) writes the token's K and V rows of this KV head into its slot
-  // before any tile is loaded, and the barrier orders every wave's loads of
-  // that block after the store.  No other unit reads the slot: it lies past
-  // the row's other units and belongs to this sequence alone.
+  // position) loads the token's K and V rows of this KV head and uses them
+  // from registers in place of the pool's copy of that slot when it
+  // processes the last block, so nothing in this kernel reads the slot; it
+  // stores them into the slot after its walk (a store issued at the start
+  // would hold up the wave's first tile loads until its data arrived).  Only the lanes that hold that
+  // token in the last block's loads (in the wave that loads the block) take
+  // part: each loads and stores its 16-byte chunk of the two rows.  No other
+  // unit reads the slot: it lies past the row's other units and belongs to
+  // this sequence alone.
+  bool fused_last = false;   // wave-uniform: this wave processes the block holding the new token
+  int new_i = 0, new_g = 0;  // the load (of NL) and the lane group holding the new token in that block
+  int32_t new_slot = -1;     // where the rows are stored (after the walk: the store waits for its data)
+  Dw<ND> new_kr{}, new_vr{};
   if constexpr (!I8) {
-    if (a.new_k != nullptr && kend == un.kv_len) {
-      constexpr int CH = D * EB / 16;   // 16-byte chunks of one row
-      const int64_t tok = (int64_t)q_start + t;
-      const int32_t slot = a.new_slots[tok];
-      if (threadIdx.x < 2 * CH && slot >= 0 && (int64_t)slot < (int64_t)a.num_blocks * kBlockSize) {
-        const bool isv = threadIdx.x >= CH;
-        const int c = threadIdx.x % CH;
-        const uint4* src = (const uint4*)((const act_t*)(isv ? a.new_v : a.new_k) + (tok * a.hkv + h) * D) + c;
-        const int64_t tile = (int64_t)(slot / kBlockSize) * a.blk_tiles + h;
-        // the pools are the caller's writable memory; the attention reads them through const pointers
-        uint4* dst = (uint4*)((char*)const_cast<void*>(isv ? a.vc : a.kc) + tile * TILE +
-                              (int64_t)(slot % kBlockSize) * D * EB) + c;
-        *dst = *src;
+    const int last_blk = (kend + kBlockSize - 1) / kBlockSize - 1;
+    if (a.new_k != nullptr && kend == un.kv_len && wave == (last_blk - kbeg / kBlockSize) % NW) {
+      fused_last = true;
+      const int o = (kend - 1) % kBlockSize;
+      new_i = o / TPL;
+      new_g = o % TPL;
+      if (grp == new_g) {
+        const int64_t tok = (int64_t)q_start + t;
+        const int64_t row = (tok * a.hkv + h) * D;
+        new_kr = load_dw<ND, false>((const uint32_t*)((const act_t*)a.new_k + row) + sub * ND);
+        new_vr = load_dw<ND, false>((const uint32_t*)((const act_t*)a.new_v + row) + sub * ND);
+        new_slot = a.new_slots[tok];
       }
-      __syncthreads();
     }
   }
 
@@ -312,6 +319,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
     const int tok0 = blk * kBlockSize + grp;
     // wave-uniform: the last block of the range, or the block the window starts in
     const bool edge = blk * kBlockSize + kBlockSize > kend || blk * kBlockSize < klo;
+    if constexpr (!I8) {
+      // fused write: the new token's rows come from registers, not from the slot being stored
+      if (fused_last && blk * kBlockSize + kBlockSize >= kend) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+          if (i == new_i && grp == new_g) {
+            kr[i] = new_kr;
+            vr[i] = new_vr;
+          }
+      }
+    }
     // keys outside [klo, kend) (the slots past the range may hold anything)
     auto hidden = [&](int tok) { return (unsigned)(tok - klo) >= (unsigned)(kend - klo); };
     if (edge) {  // drop their V
@@ -724,6 +742,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
       kqc = kqn;
       vqc = vqn;
       b += NW;
+    }
+  }
+
+  // the fused write's store, once the walk no longer waits on this wave's loads
+  if constexpr (!I8) {
+    if (fused_last && grp == new_g && new_slot >= 0 && (int64_t)new_slot < (int64_t)a.num_blocks * kBlockSize) {
+      const int64_t off =
+          ((int64_t)(new_slot / kBlockSize) * a.blk_tiles + h) * TILE + (int64_t)(new_slot % kBlockSize) * D * EB;
+      // the pools are the caller's writable memory; the attention reads them through const pointers
+      uint32_t* dk = (uint32_t*)((char*)const_cast<void*>(a.kc) + off) + sub * ND;
+      uint32_t* dv = (uint32_t*)((char*)const_cast<void*>(a.vc) + off) + sub * ND;
+#pragma unroll
+      for (int c = 0; c < ND; ++c) {
+        dk[c] = new_kr.v[c];
+        dv[c] = new_vr.v[c];
+      }
     }
   }
 
