@@ -318,8 +318,9 @@ pa_status pa_attend(const pa_cache_desc* desc, const void* q, int32_t num_q_head
  * inside the attention kernel: when the pool is fp16 or bf16, every sequence
  * has exactly one query row (h_q_lens all 1), num_tokens == num_seqs and the
  * rows take the decode units (no row tiles, group below 16), the workgroup
- * that walks a row's last key writes the row's new K and V for its KV head
- * before it loads any tile, which saves the write kernel's launch.  That form
+ * that walks a row's last key takes that key's K and V rows of its KV head
+ * from k and v (not from the pool) and stores them into the slot after its
+ * walk, which saves the write kernel's launch.  That form
  * requires token i to be the new token of sequence i: slot_mapping[i] is the
  * slot of position seq_lens[i] - 1 of sequence i (the slot its table
  * names); otherwise results are undefined (no access outside the pools).
