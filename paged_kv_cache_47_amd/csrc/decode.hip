@@ -106,6 +106,9 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)
 #ifndef PA_DECODE_KQ
 #define PA_DECODE_KQ 1      // int8 d128, G = 8: K read four lanes per token row (see the kernel)
 #endif
+#ifndef PA_DECODE_G8_OCC
+#define PA_DECODE_G8_OCC 1  // d128, G = 8, 16-bit pools: registers bounded for two waves per SIMD
+#endif
 #ifndef PA_DECODE_RS
 #define PA_DECODE_RS 1      // d128, G = 4: scores summed by reduce-scatter (see the kernel)
 #endif
@@ -122,8 +125,17 @@ __device__ __forceinline__ Dw<N> load_dw(const uint32_t* p) {
   return r;
 }
 
+// Waves per SIMD the compiler must leave room for.  16-bit pools at head dim
+// 128 with eight rows otherwise take all 256 vector registers plus one
+// accumulator register as spill room, which leaves one wave per SIMD.
+template <int D, int G, int KV>
+constexpr int decode_min_waves() {
+  return (PA_DECODE_G8_OCC && D == 128 && G == 8 && KV != kKvI8) ? 2 : 1;
+}
+
 template <int D, int G, int KV, int NW, int VB>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(decode_min_waves<D, G, KV>())))
+void decode_kernel(AttnArgs a) {
   constexpr bool I8 = KV == kKvI8;
   using act_t = typename Act<KV>::t;   // 16-bit type of queries, weights and outputs
   using act2_t = typename Act<KV>::t2;
